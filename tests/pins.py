@@ -1,0 +1,295 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes an oracle namespace ``O`` (the real ``oracle`` module, or
+a deliberately broken copy in the mutation tests) and raises AssertionError when the
+oracle disagrees with what the pages or the mathematics fix.  The brute-force
+references here are written independently of the oracle's code.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+from weight_activation_quantized_amd import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+G = 128
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _group_vec(ex):
+    v = list(ex["head"]) + [ex["fill"]] * (G - len(ex["head"]))
+    return np.array(v, dtype=np.float64)
+
+
+def _codes(ex):
+    return np.array(list(ex["codes_head"]) + [ex["codes_fill"]] * (G - len(ex["codes_head"])))
+
+
+# ------------------------------------------------------------------ hand-derived examples
+
+def pin_golden_quant_examples(O):
+    gold = load_golden("quant_examples.json")
+    for ex in gold["activation"]:
+        x = _group_vec(ex).astype(np.float16)[None, :]
+        assert np.array_equal(x.astype(np.float64), _group_vec(ex)[None, :]), ex["name"]
+        q, s, ssum = O.quant_act(x)
+        assert float(s[0, 0]) == ex["scale"], (ex["name"], s)
+        assert np.array_equal(q[0].astype(np.int64), _codes(ex)), ex["name"]
+        assert int(ssum[0, 0]) == ex["code_sum"], ex["name"]
+    for ex in gold["weight8"]:
+        x = _group_vec(ex).astype(np.float16)[None, :]
+        assert np.array_equal(x.astype(np.float64), _group_vec(ex)[None, :]), ex["name"]
+        q, s = O.quant_w8_sym(x)
+        assert float(s[0, 0]) == ex["scale"], (ex["name"], s)
+        assert np.array_equal(q[0].astype(np.int64), _codes(ex)), ex["name"]
+    for ex in gold["weight4"]:
+        x = _group_vec(ex).astype(np.float16)[None, :]
+        assert np.array_equal(x.astype(np.float64), _group_vec(ex)[None, :]), ex["name"]
+        q, z, s = O.quant_w4_asym(x)
+        assert float(s[0, 0]) == ex["scale"], (ex["name"], s)
+        assert int(z[0, 0]) == ex["zero"], (ex["name"], z)
+        assert np.array_equal(q[0].astype(np.int64), _codes(ex)), ex["name"]
+
+
+def pin_tiny_gemm_golden(O):
+    gold = load_golden("quant_examples.json")
+    t = gold["tiny_gemm"]
+    a = np.zeros((1, G), dtype=np.float16)
+    a[0, 0] = 127.0
+    w8 = next(e for e in gold["weight8"] if e["name"] == "ties_scale_2^-8")
+    w4 = next(e for e in gold["weight4"] if e["name"] == "mixed_sign_ties")
+    w = np.stack([_group_vec(w8), _group_vec(w4)]).astype(np.float16)
+    out = O.layer_forward(a, w, np.array(t["idx8"]))
+    p = O.partials(out["aq"], out["q"], out["z"])
+    assert [int(v) for v in p[0, :, 0]] == t["partials"], p
+    assert [float(v) for v in out["y64"][0]] == t["y64"], out["y64"]
+    assert [float(v) for v in out["y16"][0]] == t["y16"], out["y16"]
+
+
+# ------------------------------------------------------------------ quantizer bounds
+
+def _rand_cases():
+    rng = np.random.default_rng(1234)
+    cases = []
+    cases.append(rng.normal(0, 0.02, size=(24, 3 * G)))
+    x = rng.normal(0, 1, size=(24, 3 * G))
+    x[:, rng.permutation(3 * G)[:8]] *= 20
+    cases.append(x)
+    cases.append(rng.standard_t(3, size=(24, 3 * G)))
+    cases.append(np.abs(rng.normal(0, 1, size=(8, 2 * G))))        # one-signed +
+    cases.append(-np.abs(rng.normal(0, 1, size=(8, 2 * G))))       # one-signed -
+    y = rng.normal(0, 1e-6, size=(8, 2 * G))                         # fp16 subnormal range
+    cases.append(y)
+    z = rng.normal(0, 1, size=(4, 2 * G))
+    z[1] = 0.0
+    z[2, :G] = 0.0
+    cases.append(z)
+    return [c.astype(np.float16) for c in cases]
+
+
+def pin_quant_error_bounds(O):
+    """|x - dequant(x)| <= s/2 + (what the stored scale's rounding adds), per element.
+
+    fp32 activation scale: amax/s <= 127 (1 + 2^-24) < 127.5, no clamp fires, and the
+    only slack is the fp32 rounding of x/s: |x/s| < 128, so half an fp32 ulp there is
+    at most 2^-18 (the test allows 2^-16).
+    fp16 weight scales: with s_ideal the exact scale of the definition (amax/127, or
+    (max - min)/15 with the range widened to 0), a clamped code adds at most
+    127 |s_ideal - s| (symmetric) or 15 |s_ideal - s| (asymmetric: the zero point
+    shifts the representable range by at most s/2).  For a normal fp16 scale this is
+    below 2^-4 s resp. 2^-7 s; for a subnormal scale it can exceed s/2.
+    """
+    for x in _rand_cases():
+        xf = x.astype(np.float64)
+        xg = xf.reshape(x.shape[0], -1, G)
+        q, s, ssum = O.quant_act(x)
+        s64 = s.astype(np.float64)
+        deq = q.astype(np.float64).reshape(xg.shape) * s64[:, :, None]
+        assert np.all(np.abs(xg - deq) <= s64[:, :, None] * (0.5 + 2.0 ** -16)), "act bound"
+        assert np.all(np.abs(q.astype(np.int64)) <= 127)
+        assert np.array_equal(q.astype(np.int64).reshape(xg.shape).sum(axis=2), ssum.astype(np.int64))
+        amax = np.abs(xg).max(axis=2)
+        hit = np.abs(q.astype(np.int64).reshape(xg.shape)).max(axis=2)
+        assert np.all(hit[amax > 0] == 127), "the group maximum must map to +-127"
+        assert np.all(s64[amax == 0] == 0)
+
+        q8, s8 = O.quant_w8_sym(x)
+        s8 = s8.astype(np.float64)
+        deq8 = q8.astype(np.float64).reshape(xg.shape) * s8[:, :, None]
+        ideal8 = np.abs(xg).max(axis=2) / 127.0
+        slack8 = s8 * (0.5 + 2.0 ** -16) + 127 * np.abs(ideal8 - s8) + 1e-12 * ideal8
+        assert np.all(np.abs(xg - deq8) <= slack8[:, :, None]), "w8 bound"
+        assert np.all(np.abs(q8.astype(np.int64)) <= 127)
+        ok = np.abs(xg).max(axis=2) > 0
+        assert np.all(s8[ok] > 0) and np.all(s8[~ok] == 0)
+
+        q4, z4, s4 = O.quant_w4_asym(x)
+        s4 = s4.astype(np.float64)
+        zz = z4.astype(np.float64)[:, :, None]
+        deq4 = (q4.astype(np.float64).reshape(xg.shape) - zz) * s4[:, :, None]
+        ideal4 = (np.maximum(xg.max(axis=2), 0) - np.minimum(xg.min(axis=2), 0)) / 15.0
+        slack4 = s4 * (0.5 + 2.0 ** -16) + 15 * np.abs(ideal4 - s4) + 1e-12 * ideal4
+        assert np.all(np.abs(xg - deq4) <= slack4[:, :, None]), "w4 bound"
+        normal = s4 >= 2.0 ** -14
+        assert np.all(np.abs(xg - deq4)[normal] <= (s4 * (0.5 + 2.0 ** -7))[normal][:, None])
+        assert q4.min() >= 0 and q4.max() <= 15 and z4.min() >= 0 and z4.max() <= 15
+        # the group minimum, when negative, maps to code 0 (round(-x) = -round(x))
+        lo = xg.min(axis=2)
+        argmin = xg.argmin(axis=2)
+        qg = q4.reshape(xg.shape)
+        neg = (lo < 0) & (s4 > 0)
+        mins = np.take_along_axis(qg, argmin[:, :, None], axis=2)[:, :, 0]
+        assert np.all(mins[neg] == 0), "group minimum must map to 0"
+
+
+# ------------------------------------------------------------------ contraction and fold
+
+def _bruteforce_partials_python(aq, q, z):
+    m, k = aq.shape
+    n = q.shape[0]
+    out = np.zeros((m, n, k // G), dtype=object)
+    aql = aq.tolist()
+    ql = q.tolist()
+    zl = z.tolist()
+    for i in range(m):
+        for j in range(n):
+            for g in range(k // G):
+                acc = 0
+                for kk in range(g * G, (g + 1) * G):
+                    acc += (int(ql[j][kk]) - int(zl[j][g])) * int(aql[i][kk])
+                out[i, j, g] = acc
+    return out
+
+
+def _tiny_layers():
+    out = []
+    for seed, (m, n, k, n8) in enumerate([(3, 5, 256, 2), (4, 6, 256, 0), (2, 7, 256, 7),
+                                           (5, 4, 384, 1)]):
+        s = (99, seed, m)
+        a = WL.make_acts(m, k, s)
+        w = WL.make_weights(n, k, s)
+        idx8 = WL.make_idx8(n, n8, s)
+        out.append((a, w, idx8))
+    return out
+
+
+def pin_partials_bruteforce(O):
+    for a, w, idx8 in _tiny_layers():
+        aq, _, _ = O.quant_act(a)
+        q, z, _, _ = O.quant_weights_mixed(w, idx8)
+        p = O.partials(aq, q, z)
+        ref = _bruteforce_partials_python(aq, q, z)
+        assert np.array_equal(p.astype(object), ref), "partials differ from integer loops"
+        assert np.abs(p).max() <= 127 * 127 * G
+
+
+def _dequant_dense(aq, sa, q, z, s16):
+    a = aq.astype(np.float64) * np.repeat(sa.astype(np.float64), G, axis=1)
+    w = (q.astype(np.float64) - np.repeat(z.astype(np.float64), G, axis=1)) \
+        * np.repeat(s16.astype(np.float64), G, axis=1)
+    return a @ w.T
+
+
+def pin_y_vs_dequant(O):
+    shapes = [WL.config_shapes(0)[0]] + [WL.Shape(0, "edge", m, n, k, n8)
+                                         for m, n, k, n8 in [(1, 64, 256, 5), (7, 33, 384, 33),
+                                                             (9, 40, 512, 0)]]
+    for sh in shapes:
+        a, w, idx8 = WL.make_layer_inputs(sh)
+        out = O.layer_forward(a, w, idx8)
+        ref = _dequant_dense(out["aq"], out["sa"], out["q"], out["z"], out["s16"])
+        scale = max(np.abs(ref).max(), 1e-30)
+        assert np.abs(out["y64"] - ref).max() <= 1e-12 * scale, "fold differs from dense dequant"
+        # the quantized layer approximates the unquantized one within the quantization bound
+        af = a.astype(np.float64)
+        wf = w.astype(np.float64)
+        da = np.abs(af - out["aq"].astype(np.float64) * np.repeat(out["sa"].astype(np.float64), G, 1))
+        dw = np.abs(wf - (out["q"].astype(np.float64) - np.repeat(out["z"].astype(np.float64), G, 1))
+                    * np.repeat(out["s16"].astype(np.float64), G, 1))
+        bound = np.abs(af) @ dw.T + da @ np.abs(wf).T + da @ dw.T
+        assert np.all(np.abs(out["y64"] - af @ wf.T) <= bound * (1 + 1e-9) + 1e-12)
+
+
+def pin_p0_p100_and_disjoint(O):
+    sh = WL.Shape(0, "edge", 6, 48, 384, 0)
+    a, w, _ = WL.make_layer_inputs(sh)
+    n = w.shape[0]
+    y0 = O.layer_forward(a, w, np.array([], dtype=np.int32))["y64"]
+    assert np.array_equal(y0, O.gemm_w4a8_pure(a, w)), "p0 must equal pure W4A8"
+    y100 = O.layer_forward(a, w, np.arange(n))["y64"]
+    assert np.array_equal(y100, O.gemm_w8a8_pure(a, w)), "p100 must equal pure W8A8"
+    idx8 = WL.make_idx8(n, 11, (5, 5, 5))
+    ym = O.layer_forward(a, w, idx8)["y64"]
+    is8 = np.zeros(n, bool)
+    is8[idx8] = True
+    assert np.array_equal(ym[:, is8], y100[:, is8]), "8-bit columns must equal W8A8"
+    assert np.array_equal(ym[:, ~is8], y0[:, ~is8]), "4-bit columns must equal W4A8"
+
+
+# ------------------------------------------------------------------ fast I2F and byte model
+
+def pin_i2f(O):
+    gold = load_golden("paper_numbers.json")["fast_i2f"]
+    assert O.I2F_BIAS_BITS == int(gold["bias_bits"], 16)
+    i = np.arange(-2 ** 22, 2 ** 22, dtype=np.int64)
+    assert np.array_equal(O.i2f_bias(i), i.astype(np.float32)), "bias trick must be exact on the window"
+    # the window is exactly 2^16 * k wide for k = 128 int8 products (2^23)
+    assert 2 ** 16 * gold["k"] == 2 ** 23
+    assert O.i2f_bias(np.array([-2 ** 22 - 1]))[0] != np.float32(-2 ** 22 - 1)
+    # every group partial of the layer fits the window
+    assert 127 * 127 * G < 2 ** 22
+
+
+def pin_byte_model(O):
+    gold = load_golden("paper_numbers.json")
+    for _, p, bits in gold["effective_bits"]["rows"]:
+        assert abs(O.effective_bits(p) - bits) < 1e-12
+    r = gold["roofline_a100"]
+    assert O.weight_footprint(8, r["group"]) == 1 + 2 / 128 == 1.015625
+    assert O.weight_footprint(4, r["group"]) == 0.5 + 2.5 / 128 == 0.51953125
+    assert round(r["int8_tops"] * 1e12 / (r["hbm_gb_per_s"] * 1e9)) == r["ridge_ops_per_byte_approx"]
+    assert round(r["int8_tops"] / r["fp32_tflops"]) == r["int8_to_fp32_ratio_approx"]
+    d = gold["intensity_deltas"]
+    m, n, k = d["M"], d["N"], d["K"]
+    base = O.operand_intensity(m, n, k, 8, 8)
+    assert round(O.operand_intensity(m, n, k, 8, 4) / base - 1, 4) == d["act_8_to_4_gain"]
+    assert abs(O.operand_intensity(m, n, k, 4, 8) / base - 1 - d["weight_8_to_4_gain_approx"]) < 1e-12
+    # per-element footprint model vs the layer byte model at M = 0 (weights only)
+    n8 = 410
+    wb = O.algorithmic_bytes(0, 4096, 4096, n8) - 4 * 4096
+    assert abs(wb - ((4096 - n8) * O.weight_footprint(4) + n8 * O.weight_footprint(8)) * 4096) < 1e-6
+
+
+def pin_layer_fractions(O):
+    """The per-layer 8-bit counts used for the Llama-3.1-8B-shaped workload follow the
+    reported fractions and the global 10% budget."""
+    f = load_golden("paper_numbers.json")["layer_fractions_llama31_8b"]
+    n8 = WL.llama8b_n8()
+    sizes = {name: n for name, n, _ in WL.LLAMA8B}
+    assert abs(n8["v"] / sizes["v"] - f["v_proj"]) < 0.5 / sizes["v"]
+    assert abs(n8["down"] / sizes["down"] - f["down_proj"]) < 0.5 / sizes["down"]
+    assert abs(n8["gate"] / sizes["gate"] - f["gate_proj"]) < 0.5 / sizes["gate"]
+    total = sum(sizes.values())
+    assert sum(n8.values()) == int(np.ceil(f["global_share"] * total))
+
+
+def pin_fp16_rounding(O):
+    """The output is rounded once to fp16, to nearest with ties to even (IEEE 754):
+    hand-checked values around 1 (fp16 spacing 2^-10) and 63 (spacing 2^-5)."""
+    cases = [(1 + 2.0 ** -11, 1.0), (1 + 3 * 2.0 ** -11, 1 + 2.0 ** -9),
+             (1 + 2.0 ** -11 + 2.0 ** -20, 1 + 2.0 ** -10), (-(1 + 2.0 ** -11 + 2.0 ** -20), -(1 + 2.0 ** -10)),
+             (63.02, 63.03125), (63.00390625, 63.0), (65519.0, 65504.0)]
+    for x, want in cases:
+        assert float(O.to_fp16(np.array([x]))[0]) == want, (x, want)
+
+
+ALL_PINS = [pin_golden_quant_examples, pin_tiny_gemm_golden, pin_fp16_rounding, pin_quant_error_bounds,
+            pin_partials_bruteforce, pin_y_vs_dequant, pin_p0_p100_and_disjoint, pin_i2f,
+            pin_byte_model, pin_layer_fractions]
