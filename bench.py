@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4.4A8 mixed-precision linear layer on one MI355X.
+
+One step = the whole hot path over one batch: mixllm_quant_act (fp16 activations ->
+int8 + group scales) then mixllm_gemm_w4w8a8 (mixed 4/8-bit GEMM with scatter
+epilogue), with inputs and packed weights already resident in HBM.  Packing is offline
+(once per layer) and not part of a step.
+
+Workload: M=512 tokens, N=K=4096, group 128, 410 of 4096 output channels (10%) 8-bit,
+synthetic seeded inputs (weights N(0, 0.02) with 4 outlier channels x8, activations
+N(0, 1) with 2% of input columns x20).  The step cycles through enough independent
+(weights, activations, output) sets that the working set exceeds the 256 MB last-level
+cache, so every step reads its weights from HBM.
+
+Prints one JSON line.  value = 2 M N K / step time, in TOPS (int8 ops; each
+multiply-add counts 2).  roofline: the GEMM kernel's own duration, measured with HIP
+events on its launch stream inside the timed region, against the dense int8 MFMA peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemm_w4w8a8_M512_N4096_K4096_p10_traffic.json")
+GEMM_SRC = os.path.join(HERE, "weight_activation_quantized_amd", "csrc", "mixllm_gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough for >512 MB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--m", type=int, default=512)
+    ap.add_argument("--n", type=int, default=4096)
+    ap.add_argument("--k", type=int, default=4096)
+    ap.add_argument("--p8", type=float, default=0.10)
+    return ap.parse_args()
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(gemm_hash):
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != gemm_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(m, n, k, n8):
+    """Bytes the layer must move: 4-bit codes + 4-bit zero points + fp16 scales of the
+    4-bit channels, int8 codes + fp16 scales of the 8-bit channels, a 4-byte channel
+    index per output channel, int8 activations + fp32 activation scales, fp16 output."""
+    g, n4 = k // 128, n - n8
+    return (n4 * k / 2 + n4 * g * 2.5 + n8 * k + n8 * g * 2 + 4 * n
+            + m * k + 4 * m * g + 2 * m * n)
+
+
+def cpu_baseline(m, n, k, n8):
+    """The CPU oracle as it stands, on the same workload (the full layer: quantize
+    activations and weights, two-step dequantized GEMM)."""
+    import numpy as np
+    import oracle as O
+    from weight_activation_quantized_amd import workloads as WL
+    sh = WL.Shape(1, "p10", m, n, k, n8)
+    a16, w16, idx8 = WL.make_layer_inputs(sh)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    # bounded sample: whole-layer passes until about 10 s of CPU work (at least one)
+    reps, dt = 0, 0.0
+    while reps == 0 or (dt < 10.0 and reps < 20):
+        t0 = time.perf_counter()
+        O.layer_forward(a16, w16, idx8)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(2.0 * m * n * k * reps / dt / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{reps} pass(es) of the oracle layer (quantize activations and weights + fp64 "
+                      f"two-step GEMM), M={m} N={n} K={k} n8={n8}, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(the sharding design is described in DESIGN.md)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from weight_activation_quantized_amd import mixllm as L
+    from weight_activation_quantized_amd import workloads as WL
+
+    m, n, k = args.m, args.n, args.k
+    n8 = WL.n8_fraction(n, args.p8)
+    g = k // 128
+    sh = WL.Shape(1, "p10", m, n, k, n8)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # one packed layer + activations on the host, replicated into rotating device sets
+    a16, w16, idx8 = WL.make_layer_inputs(sh)
+    blob_host = L.mixllm_pack_weights(w16, idx8)
+    set_bytes = blob_host.size + m * k * 2 + m * k + 4 * g * m + 2 * m * n
+    sets = args.sets or max(4, int(np.ceil(512e6 / set_bytes)))
+    base_blob = torch.from_numpy(blob_host).to(dev)
+    base_a = torch.from_numpy(a16).to(dev)
+    S = []
+    for _ in range(sets):
+        S.append(dict(blob=base_blob.clone(), a=base_a.clone(),
+                      aq=torch.empty((m, k), dtype=torch.int8, device=dev),
+                      sa=torch.empty((g, m), dtype=torch.float32, device=dev),
+                      y=torch.empty((m, n), dtype=torch.float16, device=dev)))
+    ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, n8)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s = S[i % sets]
+        if ev is not None:
+            ev[0].record(stream)
+        L.mixllm_quant_act(s["a"], s["aq"], s["sa"], None, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        L.mixllm_gemm_w4w8a8(s["aq"], s["sa"], m, n, k, n8, s["blob"], s["y"], ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, HIP events on the launch stream before, between
+    # and after the two kernels of every step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    step_ms = evs[0][0].elapsed_time(evs[-1][2]) / args.steps
+    q_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    g_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    gemm_us = 1e3 * float(np.mean(g_ms))
+    quant_us = 1e3 * float(np.mean(q_ms))
+
+    ops = 2.0 * m * n * k
+    value = ops / (step_ms * 1e-3) / 1e12
+    gemm_tops = ops / (gemm_us * 1e-6) / 1e12
+    alg_bytes = algorithmic_bytes(m, n, k, n8)
+    gemm_hash = src_hash(GEMM_SRC)
+    traffic = traffic_for(gemm_hash)
+    out = {
+        "metric": "W4.4A8 GEMM TOPS at M=512,N=K=4096; % of int8 MFMA peak / HBM BW",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"W4.4A8 mixed linear layer M={m} N={n} K={k} group=128 n8={n8} "
+                               f"(p{round(100 * n8 / n)}); step = quant_act + mixed GEMM",
+                   "M": m, "N": n, "K": k, "n8": n8, "group": 128, "rotating_sets": sets},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic, "kernel": "mixllm_gemm_w4w8a8",
+                     "algorithmic_ops_per_launch": ops, "avg_launch_us": round(gemm_us, 3)},
+        "gemm_us": round(gemm_us, 3),
+        "quant_act_us": round(quant_us, 3),
+        "gemm_hbm_frac_algorithmic": round(alg_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "quant_act_gbps": round(m * k * (2 + 1 + 4 / 128) / (quant_us * 1e-6) / 1e9, 1),
+        "gemm_source_sha256_16": gemm_hash,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(m, n, k, n8)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * mixllm.h -- C ABI of the MI355X (gfx950) W4.4A8 output-channel mixed-precision
+ * linear layer (the MixLLM hot path).
+ *
+ * What the layer computes (sources: the MixLLM talk notes on notes.yuuk.io, MLSys 2026,
+ * sections 設計判断の概要 "design decisions", 二段階逆量子化 "two-step dequantization",
+ * 並列実行 "parallel execution"; and the awesome-system-papers summary page of the same
+ * paper, section 核心方法 "core method"):
+ *
+ *   * activations A (fp16 [M][K]) are quantized per token and per 128-wide group of
+ *     input features to int8 with a symmetric round-to-nearest scale;
+ *   * a set S8 of output channels (~10%) holds 8-bit symmetric group-128 weights,
+ *     the other channels hold 4-bit asymmetric group-128 weights (code, 4-bit zero
+ *     point, fp16 scale);
+ *   * Y[m][n] = sum_g s_w[n][g] * s_a[m][g] * sum_{k in g} (W_q[n][k] - z[n][g]) * A_q[m][k]
+ *     -- an exact int32 dot product per group, then one fp32 scale-and-accumulate per
+ *     group -- written as fp16 to the channel's original index n.
+ *
+ * Conventions shared by every entry point:
+ *   * Every function returns a mixllm_status: 0 on success, a negative code on error.
+ *     No function aborts, prints, or allocates device memory.
+ *   * All argument checks run on the host before any HIP call; on error nothing is
+ *     launched and no output is written.
+ *   * Device entry points are asynchronous on the given stream (NULL = the default
+ *     stream) and never synchronize.  A launch failure returns MIXLLM_E_HIP.
+ *   * The caller owns every buffer.  Device pointers must be 16-byte aligned.
+ *   * The quantization group size is fixed at 128 (MIXLLM_GROUP); K must be a
+ *     multiple of it.  M = 0 is a valid no-op.
+ *   * Inputs must be finite; non-finite activations or weights give unspecified codes.
+ *
+ * Calls that overlap on one device and share an output buffer race; calls on
+ * different streams with distinct outputs are independent.
+ */
+#ifndef MIXLLM_H_
+#define MIXLLM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIXLLM_GROUP 128
+#define MIXLLM_BLOB_MAGIC 0x344C584Du /* "MXL4" little-endian */
+#define MIXLLM_BLOB_VERSION 1u
+
+typedef enum mixllm_status {
+  MIXLLM_OK = 0,
+  MIXLLM_E_NULL = -1,   /* a required pointer is NULL */
+  MIXLLM_E_SHAPE = -2,  /* M < 0, N or K <= 0, K % 128 != 0, misaligned pointer, size overflow, bad stride */
+  MIXLLM_E_GROUP = -3,  /* group != 128 */
+  MIXLLM_E_INDEX = -4,  /* an 8-bit channel index is out of [0, N) or repeated, or n8 out of [0, N] */
+  MIXLLM_E_SPACE = -5,  /* a caller buffer (blob, workspace, output window) is too small */
+  MIXLLM_E_FORMAT = -6, /* a packed blob has a bad magic, version or shape */
+  MIXLLM_E_HIP = -7     /* the HIP runtime reported an error at launch */
+} mixllm_status;
+
+/* Host-side copy of the packed-blob header (the first 256 bytes of every blob). */
+typedef struct mixllm_blob_info {
+  uint32_t magic, version;
+  int32_t N, K, group, n8, n4;  /* n4 = N - n8 */
+  int32_t G;                    /* K / 128 groups per channel */
+  int32_t nb;                   /* 32-channel blocks: ceil(N / 32) */
+  int32_t nb4;                  /* blocks holding 4-bit data: ceil(n4 / 32) */
+  int32_t b8s;                  /* first block holding 8-bit data: floor(n4 / 32) (nb if n8 == 0) */
+  int32_t nb8;                  /* blocks holding 8-bit data: nb - b8s */
+  uint64_t off_w4, off_s4, off_z4, off_w8, off_s8, off_idx, total_bytes;
+} mixllm_blob_info;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *mixllm_status_str(int status);
+
+/* ------------------------------------------------------------------------------------
+ * Weight packing (host, offline, once per layer).
+ *
+ * Quantizes an fp16 weight matrix per output channel and group of 128 input features
+ * (talk notes, 二段階逆量子化 and ルーフラインモデル: 4-bit asymmetric channels store
+ * 0.5 + 2.5/G bytes per element, 8-bit symmetric channels 1 + 2/G) and lays the codes
+ * out in the order the GEMM kernels consume them, so no permutation happens at run
+ * time (talk notes, ソフトウェアパイプライン: pre-packed, interleaved weight layout).
+ *
+ *   8-bit channel n, group g:  amax = max |W|;  s = fp16(amax / 127)  (fp32 division,
+ *       round to nearest even; a non-zero group whose scale underflows gets 2^-24);
+ *       q = clamp(rne(W / s), -127, 127);  s = 0 and q = 0 for an all-zero group.
+ *   4-bit channel n, group g:  lo = min(min W, 0), hi = max(max W, 0);
+ *       s = fp16((hi - lo) / 15);  z = clamp(rne(-lo / s), 0, 15);
+ *       q = clamp(rne(W / s) + z, 0, 15);  dequantized value (q - z) * s.
+ *
+ * Channel order inside the blob: the 4-bit channels in ascending original index, then
+ * the 8-bit channels in ascending original index, padded with empty channels (index -1)
+ * to a multiple of 32.  The blob is position independent: a byte copy of it to device
+ * memory is what the GEMM reads.
+ * ------------------------------------------------------------------------------------ */
+
+/* Size in bytes of the blob for these parameters, or 0 if they are invalid. */
+size_t mixllm_packed_bytes(int32_t N, int32_t K, int32_t group, int32_t n8);
+
+/*
+ * w_fp16_host: [N][K] row-major IEEE fp16 bit patterns (nn.Linear layout [out][in]).
+ * idx8_host:   n8 distinct 8-bit channel indices in [0, N), any order (NULL if n8 == 0).
+ * blob_host:   output, blob_bytes >= mixllm_packed_bytes(N, K, group, n8).
+ * Host-only, synchronous, pure (no global state).  Errors: E_NULL, E_SHAPE, E_GROUP,
+ * E_INDEX, E_SPACE.
+ */
+int mixllm_pack_weights(const uint16_t *w_fp16_host, int32_t N, int32_t K, int32_t group,
+                        const int32_t *idx8_host, int32_t n8, void *blob_host, size_t blob_bytes);
+
+/* Reads and checks the header of a host blob.  Errors: E_NULL, E_SPACE, E_FORMAT. */
+int mixllm_blob_get_info(const void *blob_host, size_t blob_bytes, mixllm_blob_info *info);
+
+/*
+ * Inverse of the packing, for tests: codes in original channel order.
+ * q: [N][K] bytes (uint4 code for 4-bit channels, int8 code bits for 8-bit channels);
+ * z: [N][G] (zero point; 0 for 8-bit channels); s_fp16: [N][G] scale bits;
+ * is8: [N] (1 for 8-bit channels).  Host-only.  Errors: E_NULL, E_SPACE, E_FORMAT.
+ */
+int mixllm_unpack_weights(const void *blob_host, size_t blob_bytes, uint8_t *q, uint8_t *z,
+                          uint16_t *s_fp16, uint8_t *is8);
+
+/* ------------------------------------------------------------------------------------
+ * Activation quantization (device).
+ *
+ * Per token m and group g (talk notes, 設計判断の概要: 8-bit symmetric group-wise RTN
+ * activations): amax = max |A[m][g*128 .. +128)| in fp32; s = amax / 127 (fp32 IEEE
+ * division); A_q = clamp(rne(A / s), -127, 127) (IEEE division); s = 0, A_q = 0 for an
+ * all-zero group; S_A = sum of the group's codes.
+ *
+ * a_fp16_dev: [M][lda] fp16, lda >= K, lda % 8 == 0.
+ * aq_dev:     output int8 [M][K] row-major.
+ * sa_dev:     output fp32 [G][M] (group-major: the scales of one group for consecutive
+ *             tokens are contiguous).
+ * asum_dev:   output int32 [G][M] code sums, or NULL to skip.
+ * Errors: E_NULL, E_SHAPE, E_GROUP, E_HIP.
+ * ------------------------------------------------------------------------------------ */
+int mixllm_quant_act(const uint16_t *a_fp16_dev, int64_t lda, int32_t M, int32_t K, int32_t group,
+                     int8_t *aq_dev, float *sa_dev, int32_t *asum_dev, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Mixed W4/W8 x A8 GEMM with scatter epilogue (device).
+ *
+ * Two-step dequantization (talk notes, 二段階逆量子化): for each group, the exact
+ * int32 dot product of (W_q - z) with A_q on the int8 matrix cores, then one fp32
+ * multiply-add by s_w * s_a into a per-element fp32 accumulator (double accumulator:
+ * per group and global, summary page, 核心方法).  The 4-bit and 8-bit channel subsets
+ * are two disjoint sub-GEMMs run in one grid (talk notes, 並列実行); the epilogue
+ * writes each channel's fp16 result (round to nearest even) to its original index.
+ *
+ * aq_dev, sa_dev: as produced by mixllm_quant_act for the same M and K.
+ * blob_dev:       device copy of a blob packed for this N, K, n8 (blob_bytes long).
+ * y_fp16_dev:     output fp16 [M][ldy], ldy >= N; only columns 0..N-1 are written.
+ * workspace_dev:  scratch of at least mixllm_gemm_workspace_bytes(M, N, K, n8) bytes,
+ *                 or NULL when that is 0.  Its contents need no initialization.
+ * Errors: E_NULL, E_SHAPE, E_GROUP, E_INDEX, E_SPACE, E_HIP.
+ * ------------------------------------------------------------------------------------ */
+size_t mixllm_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n8);
+
+int mixllm_gemm_w4w8a8(const int8_t *aq_dev, const float *sa_dev, int32_t M, int32_t N, int32_t K,
+                       int32_t n8, const void *blob_dev, size_t blob_bytes, uint16_t *y_fp16_dev,
+                       int64_t ldy, void *workspace_dev, size_t workspace_bytes, void *stream);
+
+/*
+ * Test entry point: the same inner loop as mixllm_gemm_w4w8a8, but instead of folding,
+ * it writes the int32 group partials P[m][j][g] = sum_{k in g} (W_q - z) * A_q for the
+ * original channels n_begin + j, 0 <= j < n_count.
+ * p_dev: int32 [M][n_count][G].  Errors: as mixllm_gemm_w4w8a8, plus E_SHAPE when the
+ * window is outside [0, N).
+ */
+int mixllm_gemm_w4w8a8_partials(const int8_t *aq_dev, const float *sa_dev, int32_t M, int32_t N,
+                                int32_t K, int32_t n8, const void *blob_dev, size_t blob_bytes,
+                                int32_t n_begin, int32_t n_count, int32_t *p_dev, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIXLLM_H_ */

@@ -1,0 +1,206 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: int8 activation codes, fp32 activation scales, code sums, int32 group
+partials.  Within tolerance (2 fp16 ulp of the oracle value + 1e-3 max|Y|): the fp16
+layer output.  Small shapes compare every element; the five workloads at their full
+sizes compare sampled rows x columns (the oracle computes exactly those) and a window
+of group partials.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+from tests import gpu_util as U
+from weight_activation_quantized_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from weight_activation_quantized_amd import mixllm
+    return mixllm
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _quant(L, a16, lda_pad=0, with_sum=True):
+    m, k = a16.shape
+    if lda_pad:
+        big = np.zeros((m, k + lda_pad), np.float16)
+        big[:, :k] = a16
+        a = _dev(big)[:, :k]
+    else:
+        a = _dev(a16)
+    aq = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    sa = torch.empty((k // 128, m), dtype=torch.float32, device="cuda")
+    asum = torch.empty((k // 128, m), dtype=torch.int32, device="cuda") if with_sum else None
+    L.mixllm_quant_act(a, aq, sa, asum)
+    return aq, sa, asum
+
+
+# --------------------------------------------------------------------------- quant_act
+
+QA_SHAPES = [(16, 1024, "normal"), (1, 128, "normal"), (17, 384, "normal"), (512, 4096, "normal"),
+             (1, 4096, "normal"), (100, 14336, "normal"), (33, 28672, "t3"), (2048, 8192, "t3")]
+
+
+@pytest.mark.parametrize("m,k,dist", QA_SHAPES)
+def test_quant_act_bitexact(L, m, k, dist):
+    import oracle as O
+    a16 = WL.make_acts(m, k, (7, m, k), dist)
+    if m > 2:
+        a16[1, :128] = 0  # an all-zero group
+    U.say("quant_act", m, k, dist)
+    aq, sa, asum = _quant(L, a16, lda_pad=8 if m % 2 else 0)
+    torch.cuda.synchronize()
+    oq, osa, osum = O.quant_act(a16)
+    assert np.array_equal(aq.cpu().numpy(), oq)
+    assert np.array_equal(sa.cpu().numpy().T.view(np.uint32), osa.view(np.uint32))
+    assert np.array_equal(asum.cpu().numpy().T, osum)
+
+
+def test_quant_act_golden_ties(L):
+    """The hand-derived tie examples of tests/golden/quant_examples.json on the GPU."""
+    from tests import pins
+    gold = pins.load_golden("quant_examples.json")
+    rows = [pins._group_vec(ex) for ex in gold["activation"]]
+    a16 = np.stack(rows).astype(np.float16)
+    U.say("quant_act golden")
+    aq, sa, asum = _quant(L, a16)
+    torch.cuda.synchronize()
+    for i, ex in enumerate(gold["activation"]):
+        assert float(sa[0, i].item()) == ex["scale"]
+        assert np.array_equal(aq[i].cpu().numpy().astype(np.int64), pins._codes(ex))
+        assert int(asum[0, i].item()) == ex["code_sum"]
+
+
+# --------------------------------------------------------------------------- GEMM, full compare
+
+SMALL = [
+    # (M, N, K, n8) -- config 0 and edge shapes: ragged M and N, empty subsets, K = 128,
+    # n4 a multiple of 32 (no shared block), a single channel
+    (16, 512, 1024, 52), (1, 512, 1024, 52), (4, 100, 256, 7), (17, 96, 384, 0), (31, 96, 384, 96),
+    (33, 160, 256, 64), (64, 64, 128, 1), (65, 200, 512, 31), (100, 72, 256, 8), (130, 300, 384, 30),
+    (1, 1, 128, 0), (3, 1, 128, 1), (256, 520, 640, 52), (200, 33, 256, 32),
+]
+
+
+def _run_gemm(L, a16, w16, idx8, ldy_pad=0):
+    m, k = a16.shape
+    n = w16.shape[0]
+    blob = _dev(L.mixllm_pack_weights(w16, idx8))
+    aq, sa, _ = _quant(L, a16, with_sum=False)
+    y = torch.full((m, n + ldy_pad), float("nan"), dtype=torch.float16, device="cuda")
+    ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, len(idx8))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    L.mixllm_gemm_w4w8a8(aq, sa, m, n, k, len(idx8), blob, y, ws)
+    return blob, aq, sa, y
+
+
+@pytest.mark.parametrize("m,n,k,n8", SMALL)
+def test_gemm_full_compare(L, m, n, k, n8):
+    sh = WL.Shape(0, "edge", m, n, k, n8)
+    a16, w16, idx8 = WL.make_layer_inputs(sh)
+    U.say("gemm full", sh.name)
+    blob, aq, sa, y = _run_gemm(L, a16, w16, idx8, ldy_pad=5)
+    torch.cuda.synchronize()
+    ref = U.oracle_at(a16, w16, idx8)
+    yg = y.cpu().numpy()
+    assert np.all(np.isnan(yg[:, n:].astype(np.float32))), "wrote outside [0, N)"
+    U.assert_y_close(yg[:, :n], ref["y16"], sh.name)
+    # int32 group partials over every channel, bit-exact
+    g = k // 128
+    part = torch.zeros((m, n, g), dtype=torch.int32, device="cuda")
+    U.say("gemm partials", sh.name)
+    L.mixllm_gemm_w4w8a8_partials(aq, sa, m, n, k, n8, blob, 0, n, part)
+    torch.cuda.synchronize()
+    assert np.array_equal(part.cpu().numpy().astype(np.int64), U.partials_at(ref))
+
+
+def test_gemm_golden_tiny(L):
+    """The hand-derived M=1, N=2 example of tests/golden/quant_examples.json."""
+    from tests import pins
+    gold = pins.load_golden("quant_examples.json")
+    t = gold["tiny_gemm"]
+    a16 = np.zeros((1, 128), np.float16)
+    a16[0, 0] = 127.0
+    w8 = next(e for e in gold["weight8"] if e["name"] == "ties_scale_2^-8")
+    w4 = next(e for e in gold["weight4"] if e["name"] == "mixed_sign_ties")
+    w16 = np.stack([pins._group_vec(w8), pins._group_vec(w4)]).astype(np.float16)
+    U.say("gemm golden tiny")
+    blob, aq, sa, y = _run_gemm(L, a16, w16, np.array(t["idx8"], np.int32))
+    part = torch.zeros((1, 2, 1), dtype=torch.int32, device="cuda")
+    L.mixllm_gemm_w4w8a8_partials(aq, sa, 1, 2, 128, 1, blob, 0, 2, part)
+    torch.cuda.synchronize()
+    assert [float(v) for v in y[0].cpu().numpy()] == t["y16"]
+    assert [int(v) for v in part[0, :, 0].cpu().numpy()] == t["partials"]
+
+
+def test_gemm_m_zero_and_errors(L):
+    sh = WL.Shape(0, "edge", 4, 64, 256, 3)
+    a16, w16, idx8 = WL.make_layer_inputs(sh)
+    blob = _dev(L.mixllm_pack_weights(w16, idx8))
+    aq, sa, _ = _quant(L, a16)
+    y = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
+    L.mixllm_gemm_w4w8a8(aq, sa, 0, 64, 256, 3, blob, y)
+    with pytest.raises(L.MixLLMError) as e:
+        L.mixllm_gemm_w4w8a8(aq, sa, 4, 64, 256, 3, blob[:-1], y)
+    assert e.value.status == -5
+    torch.cuda.synchronize()
+    assert float(y.abs().max()) == 0.0
+
+
+# --------------------------------------------------------------------------- the five workloads at full size
+
+def _layers():
+    seen = {}
+    for cfg in range(5):
+        for sh in WL.config_shapes(cfg):
+            seen.setdefault((cfg, sh.layer, sh.n, sh.k, sh.n8, sh.dist), []).append(sh.m)
+    return sorted(seen.items())
+
+
+@pytest.mark.parametrize("key,ms", _layers(), ids=lambda v: "-".join(map(str, v)) if isinstance(v, tuple) else None)
+def test_gemm_workloads_sampled(L, key, ms):
+    cfg, layer, n, k, n8, dist = key
+    rng = np.random.default_rng(zlib.crc32(repr(key).encode()))
+    sh0 = WL.Shape(cfg, layer, ms[0], n, k, n8, dist)
+    w16, idx8 = WL.make_layer_weights(sh0)
+    U.say("pack", sh0.name)
+    blob_host = L.mixllm_pack_weights(w16, idx8)
+    blob = _dev(blob_host)
+    cols = U.sample_cols(n, idx8, rng)
+    # packed codes of the sampled channels against the oracle quantizers
+    q, z, s16, is8 = L.mixllm_unpack_weights(blob_host)
+    for m in ms:
+        sh = WL.Shape(cfg, layer, m, n, k, n8, dist)
+        a16 = WL.make_acts(m, k, sh.seed, dist)
+        rows = U.sample_rows(m, rng)
+        U.say("gemm sampled", sh.name)
+        aq, sa, _ = _quant(L, a16, with_sum=False)
+        y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, n8)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+        L.mixllm_gemm_w4w8a8(aq, sa, m, n, k, n8, blob, y, ws)
+        win = int(rng.integers(0, n - 48)) if n > 48 else 0
+        cnt = min(48, n - win)
+        part = torch.zeros((m, cnt, k // 128), dtype=torch.int32, device="cuda")
+        L.mixllm_gemm_w4w8a8_partials(aq, sa, m, n, k, n8, blob, win, cnt, part)
+        torch.cuda.synchronize()
+        ref = U.oracle_at(a16, w16, idx8, rows, cols)
+        if m == ms[0]:
+            assert np.array_equal(q[cols], (ref["q"].astype(np.int16) & 0xFF).astype(np.uint8))
+            assert np.array_equal(z[cols], ref["z"])
+            assert np.array_equal(s16[cols].view(np.uint16), ref["s16"].view(np.uint16))
+        assert np.array_equal(aq.cpu().numpy()[rows], ref["aq"])
+        U.assert_y_close(y.cpu().numpy()[np.ix_(rows, cols)], ref["y16"], sh.name)
+        wref = U.oracle_at(a16, w16, idx8, rows, np.arange(win, win + cnt))
+        assert np.array_equal(part.cpu().numpy()[rows].astype(np.int64), U.partials_at(wref)), sh.name

@@ -1,0 +1,113 @@
+// Activation quantization of the W4.4A8 layer: fp16 -> int8, one symmetric
+// round-to-nearest scale per token and per group of 128 inputs (MixLLM talk notes,
+// 設計判断の概要 "design decisions": 8-bit symmetric group-wise RTN activations;
+// アブレーション研究 "ablation": activation groups of 128).
+//
+// The pages do not describe this kernel.  It is a streaming pass (2 bytes in, 1 + 4/128
+// (+ 4/128) bytes out per element), so its roofline is HBM bandwidth.  Layout: one
+// 16-lane quarter of a wave owns one (token, group) pair; each lane loads 8 fp16 values
+// (16 bytes), the quarter reduces the group maximum and the code sum with lane shuffles,
+// and each lane stores its 8 codes (8 bytes).  Consecutive quarters own consecutive
+// groups of the same token, so a wave reads 1 KB of contiguous fp16 input.
+//
+// Arithmetic matches the definition bit for bit: the maximum of |x| is exact, the scale
+// is an IEEE fp32 division amax / 127, each code is rne(x / s) with an IEEE division
+// (hipcc's default correctly rounded division; no fast-math), clamped to [-127, 127].
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mixllm.h"
+
+namespace mixllm {
+bool is_aligned16(const void *p);
+}
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPairsPerBlock = kThreads / 16;
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+__device__ __forceinline__ float quarter_max(float v) {
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
+  return v;
+}
+
+__device__ __forceinline__ int quarter_sum(int v) {
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) v += __shfl_xor(v, m, 16);
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__restrict__ a, int64_t lda,
+                                                             int32_t M, int32_t K, int8_t *__restrict__ aq,
+                                                             float *__restrict__ sa, int32_t *__restrict__ asum) {
+  const int G = K / MIXLLM_GROUP;
+  const int64_t pair = (int64_t)blockIdx.x * kPairsPerBlock + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const int64_t npairs = (int64_t)M * G;
+  const bool live = pair < npairs;
+  const int64_t m = live ? pair / G : 0;
+  const int g = live ? (int)(pair - m * G) : 0;
+
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (live) raw = *reinterpret_cast<const uint4 *>(a + m * lda + (int64_t)g * MIXLLM_GROUP + sub * 8);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = h2f(w[i] & 0xFFFFu);
+    x[2 * i + 1] = h2f(w[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = quarter_max(amax);
+  const float s = amax / 127.0f;
+
+  int q[8];
+  int qsum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v = amax > 0.0f ? __builtin_rintf(x[i] / s) : 0.0f;
+    v = fminf(fmaxf(v, -127.0f), 127.0f);
+    q[i] = (int)v;
+    qsum += q[i];
+  }
+  qsum = quarter_sum(qsum);
+  if (!live) return;
+
+  uint2 packed;
+  packed.x = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
+             ((uint32_t)(q[3] & 0xFF) << 24);
+  packed.y = (uint32_t)(q[4] & 0xFF) | ((uint32_t)(q[5] & 0xFF) << 8) | ((uint32_t)(q[6] & 0xFF) << 16) |
+             ((uint32_t)(q[7] & 0xFF) << 24);
+  *reinterpret_cast<uint2 *>(aq + m * K + (int64_t)g * MIXLLM_GROUP + sub * 8) = packed;
+  if (sub == 0) {
+    sa[(int64_t)g * M + m] = s;
+    if (asum) asum[(int64_t)g * M + m] = qsum;
+  }
+}
+
+}  // namespace
+
+extern "C" int mixllm_quant_act(const uint16_t *a, int64_t lda, int32_t M, int32_t K, int32_t group,
+                                int8_t *aq, float *sa, int32_t *asum, void *stream) {
+  if (group != MIXLLM_GROUP) return MIXLLM_E_GROUP;
+  if (M < 0 || K <= 0 || K % MIXLLM_GROUP != 0 || lda < K || lda % 8 != 0) return MIXLLM_E_SHAPE;
+  if (M == 0) return MIXLLM_OK;
+  if (!a || !aq || !sa) return MIXLLM_E_NULL;
+  if (!mixllm::is_aligned16(a) || !mixllm::is_aligned16(aq) || !mixllm::is_aligned16(sa) ||
+      (asum && !mixllm::is_aligned16(asum)))
+    return MIXLLM_E_SHAPE;
+  const int64_t npairs = (int64_t)M * (K / MIXLLM_GROUP);
+  const int64_t blocks = (npairs + kPairsPerBlock - 1) / kPairsPerBlock;
+  if (blocks > 0x7FFFFFFF) return MIXLLM_E_SHAPE;
+  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a,
+                     lda, M, K, aq, sa, asum);
+  return hipGetLastError() == hipSuccess ? MIXLLM_OK : MIXLLM_E_HIP;
+}

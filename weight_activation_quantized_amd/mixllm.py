@@ -1,0 +1,231 @@
+"""Thin Python binding of libmixllm.so (C ABI in include/mixllm.h).
+
+Argument marshalling only: every step of the layer runs in the library (host packer in
+C++, activation quantization and the mixed GEMM in HIP kernels).  PyTorch supplies
+device memory and the HIP stream.  The functions carry the C names; a non-zero status
+raises ``MixLLMError``.  Importing this module fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+try:  # torch first: its HIP runtime must be the one the library binds to
+    import torch
+except ImportError:  # pragma: no cover - host-only use of the packer
+    torch = None
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmixllm.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mixllm.h")
+GROUP = 128
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m weight_activation_quantized_amd.build` "
+        "(there is no fallback implementation)")
+
+_lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+
+
+def hip_runtimes_loaded():
+    """Distinct libamdhip64 files mapped into this process."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 6 and "libamdhip64" in parts[-1]:
+                paths.add(os.path.realpath(parts[-1]))
+    return paths
+
+
+_runtimes = hip_runtimes_loaded()
+if len(_runtimes) > 1:
+    raise ImportError(f"two HIP runtimes are loaded into one process: {sorted(_runtimes)}")
+
+
+class BlobInfo(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+                ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("n8", ctypes.c_int32), ("n4", ctypes.c_int32), ("G", ctypes.c_int32),
+                ("nb", ctypes.c_int32), ("nb4", ctypes.c_int32), ("b8s", ctypes.c_int32),
+                ("nb8", ctypes.c_int32),
+                ("off_w4", ctypes.c_uint64), ("off_s4", ctypes.c_uint64), ("off_z4", ctypes.c_uint64),
+                ("off_w8", ctypes.c_uint64), ("off_s8", ctypes.c_uint64), ("off_idx", ctypes.c_uint64),
+                ("total_bytes", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "mixllm_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "mixllm_packed_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "mixllm_pack_weights": ([_vp, _i32, _i32, _i32, _vp, _i32, _vp, _sz], ctypes.c_int),
+    "mixllm_blob_get_info": ([_vp, _sz, ctypes.POINTER(BlobInfo)], ctypes.c_int),
+    "mixllm_unpack_weights": ([_vp, _sz, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mixllm_quant_act": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mixllm_gemm_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "mixllm_gemm_w4w8a8": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _i64, _vp, _sz, _vp],
+                           ctypes.c_int),
+    "mixllm_gemm_w4w8a8_partials": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp, _vp],
+                                    ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+STATUS = {0: "MIXLLM_OK", -1: "MIXLLM_E_NULL", -2: "MIXLLM_E_SHAPE", -3: "MIXLLM_E_GROUP",
+          -4: "MIXLLM_E_INDEX", -5: "MIXLLM_E_SPACE", -6: "MIXLLM_E_FORMAT", -7: "MIXLLM_E_HIP"}
+
+
+class MixLLMError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(mixllm_status_str(status))
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MixLLMError(status)
+
+
+def exported_symbols():
+    """Function names declared in include/mixllm.h."""
+    import re
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(mixllm_[a-z0-9_]+)\s*\(", text)))
+
+
+def library_handle():
+    return _lib
+
+
+# ---------------------------------------------------------------------------- host calls
+
+def mixllm_status_str(status: int) -> str:
+    return _lib.mixllm_status_str(int(status)).decode()
+
+
+def mixllm_packed_bytes(n: int, k: int, group: int = GROUP, n8: int = 0) -> int:
+    return int(_lib.mixllm_packed_bytes(n, k, group, n8))
+
+
+def mixllm_pack_weights(w_fp16: np.ndarray, idx8, group: int = GROUP) -> np.ndarray:
+    """Packs an fp16 [N, K] weight matrix; returns the blob as a uint8 numpy array."""
+    w = np.ascontiguousarray(w_fp16, dtype=np.float16)
+    n, k = w.shape
+    idx = np.ascontiguousarray(np.asarray(idx8, dtype=np.int32).reshape(-1))
+    size = mixllm_packed_bytes(n, k, group, int(idx.size))
+    blob = np.zeros(max(size, 1), dtype=np.uint8)
+    _check(_lib.mixllm_pack_weights(w.ctypes.data, n, k, group,
+                                    idx.ctypes.data if idx.size else None, int(idx.size),
+                                    blob.ctypes.data, blob.size if size else 0))
+    return blob
+
+
+def mixllm_blob_get_info(blob: np.ndarray) -> dict:
+    b = np.ascontiguousarray(blob, dtype=np.uint8)
+    info = BlobInfo()
+    _check(_lib.mixllm_blob_get_info(b.ctypes.data, b.size, ctypes.byref(info)))
+    return info.as_dict()
+
+
+def mixllm_unpack_weights(blob: np.ndarray):
+    """Returns (q uint8 [N, K], z uint8 [N, G], s fp16 [N, G], is8 bool [N])."""
+    info = mixllm_blob_get_info(blob)
+    n, k, g = info["N"], info["K"], info["G"]
+    b = np.ascontiguousarray(blob, dtype=np.uint8)
+    q = np.zeros((n, k), np.uint8)
+    z = np.zeros((n, g), np.uint8)
+    s = np.zeros((n, g), np.uint16)
+    is8 = np.zeros(n, np.uint8)
+    _check(_lib.mixllm_unpack_weights(b.ctypes.data, b.size, q.ctypes.data, z.ctypes.data,
+                                      s.ctypes.data, is8.ctypes.data))
+    return q, z, s.view(np.float16), is8.astype(bool)
+
+
+# ---------------------------------------------------------------------------- device calls
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def mixllm_quant_act(a, aq, sa, asum=None, stream=None):
+    """a: fp16 [M, K] CUDA tensor (rows may be strided); aq: int8 [M, K];
+    sa: fp32 [G, M]; asum: int32 [G, M] or None."""
+    m, k = a.shape
+    if a.dtype != torch.float16 or a.stride(1) != 1:
+        raise ValueError("a must be fp16 with unit column stride")
+    lda = a.stride(0) if m > 1 else k
+    _check(_lib.mixllm_quant_act(_ptr(a), lda, m, k, GROUP, _ptr(aq), _ptr(sa), _ptr(asum), _stream(stream)))
+
+
+def mixllm_gemm_workspace_bytes(m: int, n: int, k: int, n8: int) -> int:
+    return int(_lib.mixllm_gemm_workspace_bytes(m, n, k, n8))
+
+
+def mixllm_gemm_w4w8a8(aq, sa, m: int, n: int, k: int, n8: int, blob_dev, y, workspace=None, stream=None):
+    """y: fp16 [M, ldy] CUDA tensor; blob_dev: uint8 CUDA tensor holding the packed blob."""
+    ldy = y.stride(0) if y.dim() == 2 and m > 1 else n
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.mixllm_gemm_w4w8a8(_ptr(aq), _ptr(sa), m, n, k, n8, _ptr(blob_dev), blob_dev.numel(),
+                                   _ptr(y), ldy, _ptr(workspace), ws, _stream(stream)))
+
+
+def mixllm_gemm_w4w8a8_partials(aq, sa, m: int, n: int, k: int, n8: int, blob_dev, n_begin: int,
+                                n_count: int, part, stream=None):
+    """part: int32 [M, n_count, G] CUDA tensor."""
+    _check(_lib.mixllm_gemm_w4w8a8_partials(_ptr(aq), _ptr(sa), m, n, k, n8, _ptr(blob_dev),
+                                            blob_dev.numel(), n_begin, n_count, _ptr(part),
+                                            _stream(stream)))
+
+
+# ---------------------------------------------------------------------------- convenience
+
+class PackedLinear:
+    """A packed layer resident on the GPU plus the buffers one forward pass needs.
+
+    ``forward(a)`` runs the hot path: mixllm_quant_act then mixllm_gemm_w4w8a8.
+    """
+
+    def __init__(self, w_fp16: np.ndarray, idx8, device="cuda"):
+        self.n, self.k = w_fp16.shape
+        self.n8 = int(np.asarray(idx8).size)
+        self.g = self.k // GROUP
+        self.blob_host = mixllm_pack_weights(w_fp16, idx8)
+        self.blob = torch.from_numpy(self.blob_host).to(device)
+        self.device = device
+
+    def buffers(self, m: int):
+        dev = self.device
+        return dict(aq=torch.empty((m, self.k), dtype=torch.int8, device=dev),
+                    sa=torch.empty((self.g, m), dtype=torch.float32, device=dev),
+                    y=torch.empty((m, self.n), dtype=torch.float16, device=dev),
+                    ws=self._workspace(m))
+
+    def _workspace(self, m):
+        nbytes = mixllm_gemm_workspace_bytes(m, self.n, self.k, self.n8)
+        return torch.empty(nbytes, dtype=torch.uint8, device=self.device) if nbytes else None
+
+    def forward(self, a, bufs=None, stream=None):
+        m = a.shape[0]
+        bufs = bufs or self.buffers(m)
+        mixllm_quant_act(a, bufs["aq"], bufs["sa"], None, stream)
+        mixllm_gemm_w4w8a8(bufs["aq"], bufs["sa"], m, self.n, self.k, self.n8, self.blob, bufs["y"],
+                           bufs["ws"], stream)
+        return bufs["y"]

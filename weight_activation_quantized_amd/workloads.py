@@ -75,7 +75,13 @@ class Shape:
 
     @property
     def seed(self):
+        """Seed of the activations (one batch per token count)."""
         return (self.cfg, _LAYER_IDS[self.layer], self.m)
+
+    @property
+    def wseed(self):
+        """Seed of the weights and of the 8-bit channel set (shared by all token counts)."""
+        return (self.cfg, _LAYER_IDS[self.layer], 0, self.n, self.k)
 
     @property
     def name(self) -> str:
@@ -150,7 +156,9 @@ HEADLINE = Shape(1, "p10", 512, 4096, 4096, 410)
 
 def make_layer_inputs(shape: Shape):
     """(A fp16 [M, K], W fp16 [N, K], idx8 int32 [n8]) for a shape."""
-    a = make_acts(shape.m, shape.k, shape.seed, shape.dist)
-    w = make_weights(shape.n, shape.k, shape.seed)
-    idx8 = make_idx8(shape.n, shape.n8, shape.seed)
-    return a, w, idx8
+    return make_acts(shape.m, shape.k, shape.seed, shape.dist), *make_layer_weights(shape)
+
+
+def make_layer_weights(shape: Shape):
+    """(W fp16 [N, K], idx8 int32 [n8]) for a shape; independent of the token count."""
+    return make_weights(shape.n, shape.k, shape.wseed), make_idx8(shape.n, shape.n8, shape.wseed)
