@@ -37,23 +37,27 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compiles every source and links ``out``; ``defines`` are extra -D flags (tuning
+    knobs such as ring depths)."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     objs = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(BUILD, src + ".o")
+        tag = ("_" + "_".join(d.replace("=", "") for d in defines)) if defines else ""
+        obj = os.path.join(BUILD, src + tag + ".o")
+        dflags = [f"-D{d}" for d in defines]
         if src.endswith(".hip"):
-            cmd = [cc, "-x", "hip", *COMMON, *DEVICE, "-c", path, "-o", obj]
+            cmd = [cc, "-x", "hip", *COMMON, *dflags, *DEVICE, "-c", path, "-o", obj]
         else:
-            cmd = [cc, "-x", "c++", *COMMON, "-c", path, "-o", obj]
+            cmd = [cc, "-x", "c++", *COMMON, *dflags, "-c", path, "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, *DEVICE, "-shared", "-fPIC", "-o", tmp, *objs, "-Wl,-rpath,/opt/rocm/lib"], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def _run(cmd, verbose):

@@ -86,14 +86,218 @@ __device__ __forceinline__ v4i w4_operand(uint32_t x0, uint32_t x1, uint32_t zz)
 
 __device__ __forceinline__ v4i ldg16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
+// The zero point held in the low (odd = 0) or high (odd = 1) nibble of byte zb, copied
+// into all four bytes of a word (v_perm_b32 broadcast, then shift and mask).
+__device__ __forceinline__ uint32_t zero_point_x4(uint32_t zb, int odd) {
+  const uint32_t b4 = __builtin_amdgcn_perm(0u, zb, 0x00000000u);
+  return (b4 >> (odd * 4)) & 0x0F0F0F0Fu;
+}
+
 // k-chunk (16 inputs) read by half-wave h at 32-wide step s of a group, 32x32x32 kernels.
 // Steps 2p and 2p+1 of half h use chunks 2p+h and 2p+h+4: the two halves of one packed
 // 4-bit unit.
 __device__ __forceinline__ int chunk32(int s, int h) { return 4 * (s & 1) + 2 * (s >> 1) + h; }
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Calls f(IntC<B>{}), ..., f(IntC<E-1>{}): compile-time indices for register rings.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // ------------------------------------------------------------------------------------
-// Tile kernel: BM = 32 RB rows x 128 channels (4 blocks) per workgroup of 4 waves.
+// Tile kernel: BM = 32 RB rows x 128 channels (4 blocks) per workgroup of 4 waves; wave w
+// owns block 4 tn + w for all BM rows.
+//
+// Latency hiding: one workgroup per CU and one wave per SIMD is the natural fill at the
+// large shapes, so the loads must run far ahead.  Every thread keeps a ring of S groups
+// of its loads in registers (its share of the activation tile, its wave's weights and
+// scales); group g + S - 1 is requested while group g is computed, and the compiler's
+// per-register wait counters order each use after its load.  The activation tile goes
+// through a double-buffered, XOR-swizzled LDS tile (one barrier per group); weights stay
+// in the registers of the wave that owns them.  The loop body is instantiated per block
+// kind (4-bit only, 8-bit only, the one block holding both, none), so a wave only holds
+// the rings it uses.
 // ------------------------------------------------------------------------------------
+enum BlockKind { kNone = 0, kW4 = 1, kW8 = 2, kBoth = 3 };
+
+template <int RB, int S, int KIND, bool PARTIALS>
+__device__ __forceinline__ void tile_body(const GemmArgs &p, uint8_t (*a_lds)[32 * RB * 128],
+                                          float (*sa_lds)[32 * RB], int m0, int blk, int tid, int lane) {
+  constexpr int BM = 32 * RB;
+  constexpr bool H4 = (KIND & kW4) != 0;
+  constexpr bool H8 = (KIND & kW8) != 0;
+  const int ch32 = lane & 31, h = lane >> 5, half = ch32 >> 4, ch = ch32 & 15;
+  const int G = p.G;
+
+  // Ring slots hold raw loaded bits only: converting a value right after its load would
+  // make the wait for it a wait for every load issued before it.
+  v4i aR[S][RB];
+  float saR[S];
+  v4i b4R[S][2];
+  uint32_t z8R[S];   // byte holding this lane's zero point
+  uint32_t s4R[S];   // fp16 bits of the 4-bit scale
+  v4i b8R[S][4];
+  uint32_t s8R[S];   // fp16 bits of the 8-bit scale
+
+  auto issue = [&](auto slot_c, int g) {
+    constexpr int j = decltype(slot_c)::value;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int u = tid + 256 * q, r = u >> 3, c = u & 7;
+      const int row = min(m0 + r, p.M - 1);  // rows past M load a valid row; never stored
+      aR[j][q] = ldg16(p.aq + (int64_t)row * p.K + g * 128 + c * 16);
+    }
+    saR[j] = p.sa[(int64_t)g * p.M + min(m0 + (tid & (BM - 1)), p.M - 1)];  // unconditional: no branch
+    if (H4) {
+      const size_t cidx = (size_t)blk * G + g;
+      const uint8_t *chunk = p.w4 + cidx * kW4Chunk + half * 1024;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) b4R[j][q] = ldg16(chunk + ((2 * q + h) * 16 + ch) * 16);
+      s4R[j] = p.s4[cidx * 32 + ch32];
+      z8R[j] = p.z4[cidx * 16 + (ch32 >> 1)];
+    }
+    if (H8) {
+      const size_t cidx = (size_t)(blk - p.b8s) * G + g;
+      const uint8_t *chunk = p.w8 + cidx * kW8Chunk + half * 2048;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) b8R[j][s] = ldg16(chunk + (chunk32(s, h) * 16 + ch) * 16);
+      s8R[j] = p.s8[cidx * 32 + ch32];
+    }
+  };
+
+  float acc[RB][16];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[rb][r] = 0.0f;
+
+  const int jp = blk * 32 + ch32;
+  auto emit_partials = [&](const v16i(&P)[RB], int g, bool mine) {
+    const int orig = mine ? p.idx[jp] : -1;
+    if (orig < p.n_begin || orig >= p.n_begin + p.n_count) return;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < p.M) p.part[((int64_t)row * p.n_count + (orig - p.n_begin)) * G + g] = P[rb][r];
+      }
+  };
+  auto fold = [&](const v16i(&P)[RB], int st, float sw) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 s4v = *reinterpret_cast<const float4 *>(&sa_lds[st][rb * 32 + 8 * j + 4 * h]);
+        const float sv[4] = {s4v.x, s4v.y, s4v.z, s4v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[rb][4 * j + q] = fmaf((float)P[rb][4 * j + q], sw * sv[q], acc[rb][4 * j + q]);
+      }
+  };
+  auto a_operand = [&](int st, int rb, int chunk) {
+    const int r = rb * 32 + ch32;
+    return *reinterpret_cast<const v4i *>(&a_lds[st][r * 128 + ((chunk ^ (r & 7)) << 4)]);
+  };
+  auto compute = [&](auto slot_c, int st, int g) {
+    constexpr int j = decltype(slot_c)::value;
+    if (H4) {
+      const uint32_t zz = zero_point_x4(z8R[j], ch32 & 1);
+      v16i P[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) P[rb] = v16i{0};
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const v4i bA = w4_operand((uint32_t)b4R[j][q][0], (uint32_t)b4R[j][q][1], zz);
+        const v4i bB = w4_operand((uint32_t)b4R[j][q][2], (uint32_t)b4R[j][q][3], zz);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          P[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_operand(st, rb, 2 * q + h), bA, P[rb], 0, 0, 0);
+          P[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_operand(st, rb, 2 * q + h + 4), bB, P[rb], 0, 0, 0);
+        }
+      }
+      if (PARTIALS)
+        emit_partials(P, g, jp < p.n4);
+      else
+        fold(P, st, h2f((uint16_t)s4R[j]));
+    }
+    if (H8) {
+      v16i P[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) P[rb] = v16i{0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          P[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_operand(st, rb, chunk32(s, h)), b8R[j][s], P[rb], 0, 0, 0);
+      if (PARTIALS)
+        emit_partials(P, g, jp >= p.n4 && jp < p.N);
+      else
+        fold(P, st, h2f((uint16_t)s8R[j]));
+    }
+  };
+  auto store_a = [&](auto slot_c, int st) {
+    constexpr int j = decltype(slot_c)::value;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int u = tid + 256 * q, r = u >> 3, c = u & 7;
+      *reinterpret_cast<v4i *>(&a_lds[st][r * 128 + ((c ^ (r & 7)) << 4)]) = aR[j][q];
+    }
+    sa_lds[st][tid & (BM - 1)] = saR[j];  // all threads (duplicates agree): no branch
+  };
+
+  // prologue: groups 0 .. S-2 in flight
+  static_for<0, S - 1>([&](auto jc) { issue(jc, min((int)decltype(jc)::value, G - 1)); });
+  auto step = [&](auto jc, int g) {
+    constexpr int j = decltype(jc)::value;
+    const int st = g & 1;
+    store_a(jc, st);
+    __syncthreads();
+    // Always refill the ring (past the last group, reload the last group): a branch here
+    // would merge two load histories and make the compiler's waits conservative.
+    issue(IntC<(j + S - 1) % S>{}, min(g + S - 1, G - 1));
+    compute(jc, st, g);
+  };
+  // Whole turns of the ring carry no guards, so every wait the compiler derives is exact;
+  // the last partial turn is guarded.
+  int g0 = 0;
+  for (; g0 + S <= G; g0 += S) static_for<0, S>([&](auto jc) { step(jc, g0 + decltype(jc)::value); });
+  static_for<0, S>([&](auto jc) {
+    if (g0 + (int)decltype(jc)::value < G) step(jc, g0 + decltype(jc)::value);
+  });
+
+  if (PARTIALS || KIND == kNone) return;
+  const int orig = p.idx[jp];
+  if (orig < 0) return;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < p.M) p.y[(int64_t)row * p.ldy + orig] = f2h(acc[rb][r]);
+    }
+}
+
+// Register-ring depth (groups of loads in flight) per block kind.  The block holding both
+// subsets exists at most once per layer, so it gets the shallow ring.
+#ifndef MIXLLM_RING_W4
+#define MIXLLM_RING_W4 5
+#endif
+#ifndef MIXLLM_RING_W8
+#define MIXLLM_RING_W8 4
+#endif
+constexpr int kRingW4 = MIXLLM_RING_W4;
+constexpr int kRingW8 = MIXLLM_RING_W8;
+constexpr int kRingBoth = 2;
+
 template <int RB, bool PARTIALS>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmArgs p) {
   constexpr int BM = 32 * RB;
@@ -115,154 +319,13 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmArgs p) {
   const int blk = tn * 4 + wave;
   const bool has4 = blk < p.nb4;
   const bool has8 = blk >= p.b8s && blk < p.nb;
-  const int ch32 = lane & 31, h = lane >> 5, half = ch32 >> 4, ch = ch32 & 15;
-  const int G = p.G;
-
-  // ---- activation tile staging (global -> registers -> swizzled LDS)
-  v4i a_stage[RB];
-  float sa_stage = 0.0f;
-  auto load_a = [&](int g) {
-#pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int u = tid + 256 * j, r = u >> 3, c = u & 7, row = m0 + r;
-      a_stage[j] = row < p.M ? ldg16(p.aq + (int64_t)row * p.K + g * 128 + c * 16) : v4i{0, 0, 0, 0};
-    }
-    if (tid < BM) sa_stage = (m0 + tid < p.M) ? p.sa[(int64_t)g * p.M + m0 + tid] : 0.0f;
-  };
-  auto store_a = [&](int st) {
-#pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int u = tid + 256 * j, r = u >> 3, c = u & 7;
-      *reinterpret_cast<v4i *>(&a_lds[st][r * 128 + ((c ^ (r & 7)) << 4)]) = a_stage[j];
-    }
-    if (tid < BM) sa_lds[st][tid] = sa_stage;
-  };
-
-  // ---- this wave's weights, one group ahead
-  v4i b4c[2], b4n[2], b8c[4], b8n[4];
-  uint32_t zzc = 0, zzn = 0;
-  float sw4c = 0.f, sw4n = 0.f, sw8c = 0.f, sw8n = 0.f;
-  auto load_b = [&](int g, v4i (&b4)[2], uint32_t &zz, float &sw4, v4i (&b8)[4], float &sw8) {
-    if (has4) {
-      const size_t cidx = (size_t)blk * G + g;
-      const uint8_t *chunk = p.w4 + cidx * kW4Chunk + half * 1024;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) b4[q] = ldg16(chunk + ((2 * q + h) * 16 + ch) * 16);
-      sw4 = h2f(p.s4[cidx * 32 + ch32]);
-      const uint32_t z = (p.z4[cidx * 16 + (ch32 >> 1)] >> ((ch32 & 1) * 4)) & 15u;
-      zz = z * 0x01010101u;
-    }
-    if (has8) {
-      const size_t cidx = (size_t)(blk - p.b8s) * G + g;
-      const uint8_t *chunk = p.w8 + cidx * kW8Chunk + half * 2048;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) b8[s] = ldg16(chunk + (chunk32(s, h) * 16 + ch) * 16);
-      sw8 = h2f(p.s8[cidx * 32 + ch32]);
-    }
-  };
-
-  float acc[RB][16];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[rb][r] = 0.0f;
-
-  const int jp = blk * 32 + ch32;  // packed channel of this lane
-  auto emit_partials = [&](const v16i (&P)[RB], int g, bool mine) {
-    const int orig = (blk < p.nb && mine) ? p.idx[jp] : -1;
-    if (orig < p.n_begin || orig >= p.n_begin + p.n_count) return;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < p.M) p.part[((int64_t)row * p.n_count + (orig - p.n_begin)) * G + g] = P[rb][r];
-      }
-  };
-  auto fold = [&](const v16i (&P)[RB], int st, float sw) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 s4v = *reinterpret_cast<const float4 *>(&sa_lds[st][rb * 32 + 8 * j + 4 * h]);
-        const float sv[4] = {s4v.x, s4v.y, s4v.z, s4v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[rb][4 * j + q] = fmaf((float)P[rb][4 * j + q], sw * sv[q], acc[rb][4 * j + q]);
-      }
-  };
-  auto a_operand = [&](int st, int rb, int chunk) {
-    const int r = rb * 32 + ch32;
-    return *reinterpret_cast<const v4i *>(&a_lds[st][r * 128 + ((chunk ^ (r & 7)) << 4)]);
-  };
-
-  load_a(0);
-  store_a(0);
-  load_b(0, b4c, zzc, sw4c, b8c, sw8c);
-
-  for (int g = 0; g < G; ++g) {
-    const int st = g & 1;
-    __syncthreads();
-    const bool more = g + 1 < G;
-    if (more) {
-      load_a(g + 1);
-      load_b(g + 1, b4n, zzn, sw4n, b8n, sw8n);
-    }
-    if (has4) {
-      v16i P[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) P[rb] = v16i{0};
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const v4i bA = w4_operand((uint32_t)b4c[q][0], (uint32_t)b4c[q][1], zzc);
-        const v4i bB = w4_operand((uint32_t)b4c[q][2], (uint32_t)b4c[q][3], zzc);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          P[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_operand(st, rb, 2 * q + h), bA, P[rb], 0, 0, 0);
-          P[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_operand(st, rb, 2 * q + h + 4), bB, P[rb], 0, 0, 0);
-        }
-      }
-      if (PARTIALS)
-        emit_partials(P, g, jp < p.n4);
-      else
-        fold(P, st, sw4c);
-    }
-    if (has8) {
-      v16i P[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) P[rb] = v16i{0};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          P[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_operand(st, rb, chunk32(s, h)), b8c[s], P[rb], 0, 0, 0);
-      }
-      if (PARTIALS)
-        emit_partials(P, g, jp >= p.n4 && jp < p.N);
-      else
-        fold(P, st, sw8c);
-    }
-    if (more) {
-      store_a(st ^ 1);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) b4c[q] = b4n[q];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) b8c[s] = b8n[s];
-      zzc = zzn;
-      sw4c = sw4n;
-      sw8c = sw8n;
-    }
+  const int kind = (has4 ? kW4 : 0) | (has8 ? kW8 : 0);
+  switch (kind) {
+    case kW4: tile_body<RB, kRingW4, kW4, PARTIALS>(p, a_lds, sa_lds, m0, blk, tid, lane); break;
+    case kW8: tile_body<RB, kRingW8, kW8, PARTIALS>(p, a_lds, sa_lds, m0, blk, tid, lane); break;
+    case kBoth: tile_body<RB, kRingBoth, kBoth, PARTIALS>(p, a_lds, sa_lds, m0, blk, tid, lane); break;
+    default: tile_body<RB, kRingW4, kNone, PARTIALS>(p, a_lds, sa_lds, m0, blk, tid, lane); break;
   }
-
-  if (PARTIALS) return;
-  const int orig = blk < p.nb ? p.idx[jp] : -1;
-  if (orig < 0) return;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row < p.M) p.y[(int64_t)row * p.ldy + orig] = f2h(acc[rb][r]);
-    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -315,8 +378,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(const GemmArgs p, int
     if (has4) {
       const size_t cidx = (size_t)blk * G + g;
       const v4i x = ldg16(p.w4 + cidx * kW4Chunk + half * 1024 + lane * 16);
-      const uint32_t z = (p.z4[cidx * 16 + (ch32 >> 1)] >> ((ch32 & 1) * 4)) & 15u;
-      const uint32_t zz = z * 0x01010101u;
+      const uint32_t zz = zero_point_x4(p.z4[cidx * 16 + (ch32 >> 1)], ch32 & 1);
       const float sw = h2f(p.s4[cidx * 32 + ch32]);
       const v4i b0 = w4_operand((uint32_t)x[0], (uint32_t)x[1], zz);
       const v4i b1 = w4_operand((uint32_t)x[2], (uint32_t)x[3], zz);

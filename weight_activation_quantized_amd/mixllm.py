@@ -18,7 +18,7 @@ except ImportError:  # pragma: no cover - host-only use of the packer
     torch = None
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmixllm.so")
+LIB_PATH = os.environ.get("MIXLLM_LIB") or os.path.join(HERE, "libmixllm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "mixllm.h")
 GROUP = 128
 
