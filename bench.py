@@ -123,7 +123,7 @@ def main():
     # one packed layer + activations on the host, replicated into rotating device sets
     a16, w16, idx8 = WL.make_layer_inputs(sh)
     blob_host = L.mixllm_pack_weights(w16, idx8)
-    set_bytes = blob_host.size + m * k * 2 + m * k + 4 * g * m + 2 * m * n
+    set_bytes = blob_host.size + m * k * 2 + m * k + 8 * g * m + 2 * m * n
     sets = args.sets or max(4, int(np.ceil(512e6 / set_bytes)))
     base_blob = torch.from_numpy(blob_host).to(dev)
     base_a = torch.from_numpy(a16).to(dev)
@@ -132,19 +132,20 @@ def main():
         S.append(dict(blob=base_blob.clone(), a=base_a.clone(),
                       aq=torch.empty((m, k), dtype=torch.int8, device=dev),
                       sa=torch.empty((g, m), dtype=torch.float32, device=dev),
+                      asum=torch.empty((g, m), dtype=torch.int32, device=dev),
                       y=torch.empty((m, n), dtype=torch.float16, device=dev)))
     ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, n8)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
         s = S[i % sets]
         if ev is not None:
             ev[0].record(stream)
-        L.mixllm_quant_act(s["a"], s["aq"], s["sa"], None, stream)
+        L.mixllm_quant_act(s["a"], s["aq"], s["sa"], s["asum"], stream)
         if ev is not None:
             ev[1].record(stream)
-        L.mixllm_gemm_w4w8a8(s["aq"], s["sa"], m, n, k, n8, s["blob"], s["y"], ws, stream)
+        L.mixllm_gemm_w4w8a8(s["aq"], s["sa"], s["asum"], m, n, k, n8, s["blob"], s["y"], ws, stream)
         if ev is not None:
             ev[2].record(stream)
 

@@ -43,7 +43,7 @@ extern "C" {
 
 #define MIXLLM_GROUP 128
 #define MIXLLM_BLOB_MAGIC 0x344C584Du /* "MXL4" little-endian */
-#define MIXLLM_BLOB_VERSION 1u
+#define MIXLLM_BLOB_VERSION 2u
 
 typedef enum mixllm_status {
   MIXLLM_OK = 0,
@@ -62,10 +62,10 @@ typedef struct mixllm_blob_info {
   int32_t N, K, group, n8, n4;  /* n4 = N - n8 */
   int32_t G;                    /* K / 128 groups per channel */
   int32_t nb;                   /* 32-channel blocks: ceil(N / 32) */
-  int32_t nb4;                  /* blocks holding 4-bit data: ceil(n4 / 32) */
-  int32_t b8s;                  /* first block holding 8-bit data: floor(n4 / 32) (nb if n8 == 0) */
-  int32_t nb8;                  /* blocks holding 8-bit data: nb - b8s */
-  uint64_t off_w4, off_s4, off_z4, off_w8, off_s8, off_idx, total_bytes;
+  int32_t nb4;                  /* 4-bit blocks: floor(n4 / 32) */
+  int32_t nb8;                  /* 8-bit blocks: nb - nb4 */
+  int32_t n4_promoted;          /* n4 - 32 nb4 4-bit channels stored in the first 8-bit block */
+  uint64_t off_w4, off_s4, off_z4, off_w8, off_s8, off_zp, off_idx, total_bytes;
 } mixllm_blob_info;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -89,8 +89,11 @@ const char *mixllm_status_str(int status);
  *
  * Channel order inside the blob: the 4-bit channels in ascending original index, then
  * the 8-bit channels in ascending original index, padded with empty channels (index -1)
- * to a multiple of 32.  The blob is position independent: a byte copy of it to device
- * memory is what the GEMM reads.
+ * to a multiple of 32, in blocks of 32 channels.  Whole blocks of 4-bit channels keep
+ * packed nibbles; the n4 % 32 leftover 4-bit channels share the first 8-bit block,
+ * stored as their int8 partial dequantization (q - z) (the same two-step arithmetic).
+ * The blob is position independent: a byte copy of it to device memory is what the
+ * GEMM reads.
  * ------------------------------------------------------------------------------------ */
 
 /* Size in bytes of the blob for these parameters, or 0 if they are invalid. */
@@ -143,31 +146,40 @@ int mixllm_quant_act(const uint16_t *a_fp16_dev, int64_t lda, int32_t M, int32_t
  * int32 dot product of (W_q - z) with A_q on the int8 matrix cores, then one fp32
  * multiply-add by s_w * s_a into a per-element fp32 accumulator (double accumulator:
  * per group and global, summary page, 核心方法).  The 4-bit and 8-bit channel subsets
- * are two disjoint sub-GEMMs run in one grid (talk notes, 並列実行); the epilogue
- * writes each channel's fp16 result (round to nearest even) to its original index.
+ * are disjoint sub-GEMMs run in one grid (talk notes, 並列実行); the epilogue writes each
+ * channel's fp16 result (round to nearest even) to its original index.  The zero point
+ * of a 4-bit channel enters as sum_k (q - z) a_k = sum_k q a_k - z S_A, with S_A the
+ * group's activation code sum from mixllm_quant_act.
  *
- * aq_dev, sa_dev: as produced by mixllm_quant_act for the same M and K.
+ * aq_dev, sa_dev, asum_dev: as produced by mixllm_quant_act for the same M and K
+ *                 (asum_dev is required here).
  * blob_dev:       device copy of a blob packed for this N, K, n8 (blob_bytes long).
  * y_fp16_dev:     output fp16 [M][ldy], ldy >= N; only columns 0..N-1 are written.
- * workspace_dev:  scratch of at least mixllm_gemm_workspace_bytes(M, N, K, n8) bytes,
- *                 or NULL when that is 0.  Its contents need no initialization.
+ * workspace_dev:  scratch of at least mixllm_gemm_workspace_bytes(M, N, K, n8) bytes
+ *                 (16-byte aligned), or NULL when that is 0.  When the grid has too
+ *                 few output tiles to give every CU two workgroups, the groups of each
+ *                 tile are split over several workgroups; the workspace holds their
+ *                 partial tiles and per-tile arrival counters.  Zero-fill it before its
+ *                 first use; every call leaves the counters zero again, so one workspace
+ *                 serves any number of calls in sequence, but calls that overlap in time
+ *                 must not share one.
  * Errors: E_NULL, E_SHAPE, E_GROUP, E_INDEX, E_SPACE, E_HIP.
  * ------------------------------------------------------------------------------------ */
 size_t mixllm_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n8);
 
-int mixllm_gemm_w4w8a8(const int8_t *aq_dev, const float *sa_dev, int32_t M, int32_t N, int32_t K,
-                       int32_t n8, const void *blob_dev, size_t blob_bytes, uint16_t *y_fp16_dev,
+int mixllm_gemm_w4w8a8(const int8_t *aq_dev, const float *sa_dev, const int32_t *asum_dev, int32_t M, int32_t N,
+                       int32_t K, int32_t n8, const void *blob_dev, size_t blob_bytes, uint16_t *y_fp16_dev,
                        int64_t ldy, void *workspace_dev, size_t workspace_bytes, void *stream);
 
 /*
- * Test entry point: the same inner loop as mixllm_gemm_w4w8a8, but instead of folding,
- * it writes the int32 group partials P[m][j][g] = sum_{k in g} (W_q - z) * A_q for the
- * original channels n_begin + j, 0 <= j < n_count.
+ * Test entry point: the same integer inner loop as mixllm_gemm_w4w8a8, but instead of
+ * folding, it writes the int32 group partials P[m][j][g] = sum_{k in g} (W_q - z) * A_q
+ * for the original channels n_begin + j, 0 <= j < n_count.
  * p_dev: int32 [M][n_count][G].  Errors: as mixllm_gemm_w4w8a8, plus E_SHAPE when the
  * window is outside [0, N).
  */
-int mixllm_gemm_w4w8a8_partials(const int8_t *aq_dev, const float *sa_dev, int32_t M, int32_t N,
-                                int32_t K, int32_t n8, const void *blob_dev, size_t blob_bytes,
+int mixllm_gemm_w4w8a8_partials(const int8_t *aq_dev, const float *sa_dev, const int32_t *asum_dev, int32_t M,
+                                int32_t N, int32_t K, int32_t n8, const void *blob_dev, size_t blob_bytes,
                                 int32_t n_begin, int32_t n_count, int32_t *p_dev, void *stream);
 
 #ifdef __cplusplus

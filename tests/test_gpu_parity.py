@@ -97,12 +97,12 @@ def _run_gemm(L, a16, w16, idx8, ldy_pad=0):
     m, k = a16.shape
     n = w16.shape[0]
     blob = _dev(L.mixllm_pack_weights(w16, idx8))
-    aq, sa, _ = _quant(L, a16, with_sum=False)
+    aq, sa, asum = _quant(L, a16)
     y = torch.full((m, n + ldy_pad), float("nan"), dtype=torch.float16, device="cuda")
     ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, len(idx8))
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
-    L.mixllm_gemm_w4w8a8(aq, sa, m, n, k, len(idx8), blob, y, ws)
-    return blob, aq, sa, y
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+    L.mixllm_gemm_w4w8a8(aq, sa, asum, m, n, k, len(idx8), blob, y, ws)
+    return blob, aq, sa, asum, y
 
 
 @pytest.mark.parametrize("m,n,k,n8", SMALL)
@@ -110,7 +110,7 @@ def test_gemm_full_compare(L, m, n, k, n8):
     sh = WL.Shape(0, "edge", m, n, k, n8)
     a16, w16, idx8 = WL.make_layer_inputs(sh)
     U.say("gemm full", sh.name)
-    blob, aq, sa, y = _run_gemm(L, a16, w16, idx8, ldy_pad=5)
+    blob, aq, sa, asum, y = _run_gemm(L, a16, w16, idx8, ldy_pad=5)
     torch.cuda.synchronize()
     ref = U.oracle_at(a16, w16, idx8)
     yg = y.cpu().numpy()
@@ -120,9 +120,35 @@ def test_gemm_full_compare(L, m, n, k, n8):
     g = k // 128
     part = torch.zeros((m, n, g), dtype=torch.int32, device="cuda")
     U.say("gemm partials", sh.name)
-    L.mixllm_gemm_w4w8a8_partials(aq, sa, m, n, k, n8, blob, 0, n, part)
+    L.mixllm_gemm_w4w8a8_partials(aq, sa, asum, m, n, k, n8, blob, 0, n, part)
     torch.cuda.synchronize()
     assert np.array_equal(part.cpu().numpy().astype(np.int64), U.partials_at(ref))
+
+
+@pytest.mark.parametrize("m,n,k,n8", [(128, 256, 1024, 26), (512, 4096, 4096, 410), (65, 4100, 256, 500)])
+def test_gemm_split_workspace_reuse(L, m, n, k, n8):
+    """Split-K tiles: repeated calls on one workspace give bit-identical outputs, and the
+    arrival counters are back at zero after each call."""
+    sh = WL.Shape(0, "edge", m, n, k, n8)
+    a16, w16, idx8 = WL.make_layer_inputs(sh)
+    ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, n8)
+    U.say("gemm workspace reuse", sh.name, ws_bytes)
+    blob = _dev(L.mixllm_pack_weights(w16, idx8))
+    aq, sa, asum = _quant(L, a16)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    ys = []
+    for _ in range(3):
+        y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, m, n, k, n8, blob, y, ws if ws_bytes else None)
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy())
+    assert all(np.array_equal(ys[0].view(np.uint16), y.view(np.uint16)) for y in ys[1:])
+    if ws_bytes:
+        tiles = ((m + 63) // 64) * (((n + 31) // 32 + 3) // 4)
+        cnt_bytes = ((tiles * 4 + 255) // 256) * 256
+        assert int(ws[ws_bytes - cnt_bytes:].count_nonzero()) == 0
+    if m * n * k <= 2 ** 24:
+        U.assert_y_close(ys[0], U.oracle_at(a16, w16, idx8)["y16"], sh.name)
 
 
 def test_gemm_golden_tiny(L):
@@ -136,9 +162,9 @@ def test_gemm_golden_tiny(L):
     w4 = next(e for e in gold["weight4"] if e["name"] == "mixed_sign_ties")
     w16 = np.stack([pins._group_vec(w8), pins._group_vec(w4)]).astype(np.float16)
     U.say("gemm golden tiny")
-    blob, aq, sa, y = _run_gemm(L, a16, w16, np.array(t["idx8"], np.int32))
+    blob, aq, sa, asum, y = _run_gemm(L, a16, w16, np.array(t["idx8"], np.int32))
     part = torch.zeros((1, 2, 1), dtype=torch.int32, device="cuda")
-    L.mixllm_gemm_w4w8a8_partials(aq, sa, 1, 2, 128, 1, blob, 0, 2, part)
+    L.mixllm_gemm_w4w8a8_partials(aq, sa, asum, 1, 2, 128, 1, blob, 0, 2, part)
     torch.cuda.synchronize()
     assert [float(v) for v in y[0].cpu().numpy()] == t["y16"]
     assert [int(v) for v in part[0, :, 0].cpu().numpy()] == t["partials"]
@@ -148,12 +174,15 @@ def test_gemm_m_zero_and_errors(L):
     sh = WL.Shape(0, "edge", 4, 64, 256, 3)
     a16, w16, idx8 = WL.make_layer_inputs(sh)
     blob = _dev(L.mixllm_pack_weights(w16, idx8))
-    aq, sa, _ = _quant(L, a16)
+    aq, sa, asum = _quant(L, a16)
     y = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
-    L.mixllm_gemm_w4w8a8(aq, sa, 0, 64, 256, 3, blob, y)
+    L.mixllm_gemm_w4w8a8(aq, sa, asum, 0, 64, 256, 3, blob, y)
     with pytest.raises(L.MixLLMError) as e:
-        L.mixllm_gemm_w4w8a8(aq, sa, 4, 64, 256, 3, blob[:-1], y)
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, 4, 64, 256, 3, blob[:-1], y)
     assert e.value.status == -5
+    with pytest.raises(L.MixLLMError) as e:
+        L.mixllm_gemm_w4w8a8(aq, sa, None, 4, 64, 256, 3, blob, y)
+    assert e.value.status == -1
     torch.cuda.synchronize()
     assert float(y.abs().max()) == 0.0
 
@@ -185,15 +214,15 @@ def test_gemm_workloads_sampled(L, key, ms):
         a16 = WL.make_acts(m, k, sh.seed, dist)
         rows = U.sample_rows(m, rng)
         U.say("gemm sampled", sh.name)
-        aq, sa, _ = _quant(L, a16, with_sum=False)
+        aq, sa, asum = _quant(L, a16)
         y = torch.empty((m, n), dtype=torch.float16, device="cuda")
         ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, n8)
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
-        L.mixllm_gemm_w4w8a8(aq, sa, m, n, k, n8, blob, y, ws)
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, m, n, k, n8, blob, y, ws)
         win = int(rng.integers(0, n - 48)) if n > 48 else 0
         cnt = min(48, n - win)
         part = torch.zeros((m, cnt, k // 128), dtype=torch.int32, device="cuda")
-        L.mixllm_gemm_w4w8a8_partials(aq, sa, m, n, k, n8, blob, win, cnt, part)
+        L.mixllm_gemm_w4w8a8_partials(aq, sa, asum, m, n, k, n8, blob, win, cnt, part)
         torch.cuda.synchronize()
         ref = U.oracle_at(a16, w16, idx8, rows, cols)
         if m == ms[0]:

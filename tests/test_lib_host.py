@@ -52,6 +52,8 @@ def test_pack_matches_oracle(n, k, n8):
     info = L.mixllm_blob_get_info(blob)
     assert info["N"] == n and info["K"] == k and info["n8"] == n8 and info["n4"] == n - n8
     assert info["nb"] == (n + 31) // 32
+    assert info["nb4"] == (n - n8) // 32 and info["nb8"] == info["nb"] - info["nb4"]
+    assert info["n4_promoted"] == (n - n8) % 32
     assert info["total_bytes"] == blob.size == L.mixllm_packed_bytes(n, k, 128, n8)
 
 
@@ -84,15 +86,17 @@ def test_packed_bytes_formula():
     8-bit element) over the padded blocks, plus the channel index and alignment."""
     for n, k, n8 in [(4096, 4096, 410), (14336, 4096, 105), (1024, 4096, 729), (8192, 28672, 820)]:
         nb = (n + 31) // 32
-        nb4 = (n - n8 + 31) // 32
-        nb8 = nb - ((n - n8) // 32 if n8 else nb)
+        nb4 = (n - n8) // 32
+        nb8 = nb - nb4
+        g = k // 128
         w_bytes = 32 * k * (nb4 * O.weight_footprint(4) + nb8 * O.weight_footprint(8))
+        side = 32 * g  # zero points of the <= 31 promoted 4-bit channels (unpacking only)
         size = L.mixllm_packed_bytes(n, k, 128, n8)
-        assert w_bytes + 4 * 32 * nb <= size <= w_bytes + 4 * 32 * nb + 7 * 256 + 256
-        # the padding to 32-channel blocks costs at most one 8-bit block more than the
-        # algorithmic byte count
+        assert w_bytes + 4 * 32 * nb + side <= size <= w_bytes + 4 * 32 * nb + side + 8 * 256 + 256
+        # the padding to 32-channel blocks and the <= 31 4-bit channels stored as int8
+        # cost at most one 8-bit block more than the algorithmic byte count
         alg = O.algorithmic_bytes(0, n, k, n8)
-        assert alg <= size <= alg + 32 * k * (O.weight_footprint(4) + O.weight_footprint(8)) + 4096
+        assert alg <= size <= alg + 32 * k * O.weight_footprint(8) + side + 4096
 
 
 def test_pack_errors():
@@ -159,19 +163,21 @@ def test_device_entry_points_validate_on_host():
 
     nbytes = L.mixllm_packed_bytes(64, 256, 128, 2)
     gm = lib.mixllm_gemm_w4w8a8
-    assert gm(fake, fake, 4, 64, 200, 2, fake, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(fake, fake, 4, 64, 256, 65, fake, nbytes, fake, 64, None, 0, s) == -4
-    assert gm(fake, fake, -1, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(None, fake, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -1
-    assert gm(fake, fake, 4, 64, 256, 2, None, nbytes, fake, 64, None, 0, s) == -1
-    assert gm(fake, fake, 4, 64, 256, 2, fake, nbytes, None, 64, None, 0, s) == -1
-    assert gm(fake, fake, 4, 64, 256, 2, fake, nbytes - 1, fake, 64, None, 0, s) == -5
-    assert gm(fake, fake, 4, 64, 256, 2, fake, nbytes, fake, 63, None, 0, s) == -2
-    assert gm(odd, fake, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(fake, fake, 4, 64, 256, 2, odd, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(None, None, 0, 64, 256, 2, None, 0, None, 64, None, 0, s) == 0  # M = 0
+    assert gm(fake, fake, fake, 4, 64, 200, 2, fake, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(fake, fake, fake, 4, 64, 256, 65, fake, nbytes, fake, 64, None, 0, s) == -4
+    assert gm(fake, fake, fake, -1, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(None, fake, fake, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -1
+    assert gm(fake, fake, None, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -1
+    assert gm(fake, fake, fake, 4, 64, 256, 2, None, nbytes, fake, 64, None, 0, s) == -1
+    assert gm(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, None, 64, None, 0, s) == -1
+    assert gm(fake, fake, fake, 4, 64, 256, 2, fake, nbytes - 1, fake, 64, None, 0, s) == -5
+    assert gm(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, fake, 63, None, 0, s) == -2
+    assert gm(odd, fake, fake, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(fake, fake, odd, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(fake, fake, fake, 4, 64, 256, 2, odd, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(None, None, None, 0, 64, 256, 2, None, 0, None, 64, None, 0, s) == 0  # M = 0
     gp = lib.mixllm_gemm_w4w8a8_partials
-    assert gp(fake, fake, 4, 64, 256, 2, fake, nbytes, 60, 5, fake, s) == -2
-    assert gp(fake, fake, 4, 64, 256, 2, fake, nbytes, -1, 5, fake, s) == -2
-    assert gp(fake, fake, 4, 64, 256, 2, fake, nbytes, 0, 5, None, s) == -1
-    assert gp(fake, fake, 4, 64, 256, 2, fake, nbytes, 0, 0, None, s) == 0
+    assert gp(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, 60, 5, fake, s) == -2
+    assert gp(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, -1, 5, fake, s) == -2
+    assert gp(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, 0, 5, None, s) == -1
+    assert gp(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, 0, 0, None, s) == 0

@@ -2,19 +2,23 @@
 //
 // The blob is a 256-byte header followed by sections, each 256-byte aligned:
 //
-//   w4   [nb4 blocks][G groups] 2048 B: 32 channels x 128 nibble codes
-//   s4   [nb4][G][32]  fp16 scales of the 4-bit part
+//   w4   [nb4 blocks][G groups] 2048 B: 32 channels x 128 4-bit codes
+//   s4   [nb4][G][32]  fp16 scales of the 4-bit blocks
 //   z4   [nb4][G][16]  4-bit zero points, channel c in byte c/2 (low nibble for even c)
 //   w8   [nb8 blocks][G] 4096 B: 32 channels x 128 int8 codes
-//   s8   [nb8][G][32]  fp16 scales of the 8-bit part
+//   s8   [nb8][G][32]  fp16 scales of the 8-bit blocks
+//   zp   [32][G]       zero points of the promoted 4-bit channels (unpacking only)
 //   idx  [nb * 32]     int32 original channel index of every packed channel (-1: empty)
 //
 // Packed channel order: the n4 4-bit channels (ascending original index), then the n8
-// 8-bit channels (ascending), then empty channels up to nb * 32.  Block b holds packed
-// channels [32b, 32b + 32).  Blocks [0, nb4) carry 4-bit data, blocks [b8s, nb) carry
-// 8-bit data; when n4 is not a multiple of 32 the block b8s = nb4 - 1 carries both, each
-// part holding zero codes and zero scales for the other part's channels.  This keeps the
-// number of blocks at ceil(N / 32), so no tile is wasted on padding between the subsets.
+// 8-bit channels (ascending), then empty channels up to nb * 32 = 32 ceil(N / 32).
+// Block b holds packed channels [32b, 32b + 32).  The first nb4 = floor(n4 / 32) blocks
+// are 4-bit blocks.  The remaining nb8 = nb - nb4 blocks are 8-bit blocks; the first of
+// them starts with the r = n4 - 32 nb4 leftover 4-bit channels, stored as their partially
+// dequantized int8 codes (q - z) in [-15, 15] with their fp16 scale.  Two-step
+// dequantization computes the same partial sum_k (q - z) a_k and the same scale
+// product for them either way, so every block has one kind, and the block count is
+// ceil(N / 32): no tile is spent on padding between the two subsets.
 //
 // Inside a 4-bit (block, group) chunk of 2048 B, 16-byte unit u = ((half * 4 + a) * 16 + ch)
 // holds channel 16 * half + ch, k-chunks a (bytes 0..7) and a + 4 (bytes 8..15) of the
@@ -57,9 +61,8 @@ inline bool compute_layout(int32_t N, int32_t K, int32_t n8, mixllm_blob_info *L
   const int64_t G = K / kGroup;
   const int64_t n4 = (int64_t)N - n8;
   const int64_t nb = ((int64_t)N + kBlock - 1) / kBlock;
-  const int64_t nb4 = (n4 + kBlock - 1) / kBlock;
-  const int64_t b8s = n8 > 0 ? n4 / kBlock : nb;
-  const int64_t nb8 = nb - b8s;
+  const int64_t nb4 = n4 / kBlock;
+  const int64_t nb8 = nb - nb4;
   // Keep every byte count well inside 2^62 so the sums below cannot overflow.
   if (nb > (int64_t(1) << 26) || G > (int64_t(1) << 26)) return false;
   L->magic = MIXLLM_BLOB_MAGIC;
@@ -72,8 +75,8 @@ inline bool compute_layout(int32_t N, int32_t K, int32_t n8, mixllm_blob_info *L
   L->G = (int32_t)G;
   L->nb = (int32_t)nb;
   L->nb4 = (int32_t)nb4;
-  L->b8s = (int32_t)b8s;
   L->nb8 = (int32_t)nb8;
+  L->n4_promoted = (int32_t)(n4 - nb4 * kBlock);
   size_t off = kHeaderBytes;
   L->off_w4 = off;
   off = align256(off + (size_t)nb4 * G * kW4Chunk);
@@ -85,6 +88,8 @@ inline bool compute_layout(int32_t N, int32_t K, int32_t n8, mixllm_blob_info *L
   off = align256(off + (size_t)nb8 * G * kW8Chunk);
   L->off_s8 = off;
   off = align256(off + (size_t)nb8 * G * kS8Chunk);
+  L->off_zp = off;
+  off = align256(off + (size_t)kBlock * G);
   L->off_idx = off;
   off = align256(off + (size_t)nb * kBlock * 4);
   L->total_bytes = off;

@@ -197,10 +197,12 @@ int mixllm_pack_weights(const uint16_t *w, int32_t N, int32_t K, int32_t group, 
   uint8_t *z4 = base + L.off_z4;
   int8_t *w8 = (int8_t *)(base + L.off_w8);
   uint16_t *s8 = (uint16_t *)(base + L.off_s8);
+  uint8_t *zp = base + L.off_zp;
   int32_t *idx = (int32_t *)(base + L.off_idx);
 
   for (int64_t j = 0; j < (int64_t)L.nb * kBlock; ++j) idx[j] = j < N ? perm[(size_t)j] : -1;
 
+  const int64_t j8 = (int64_t)L.nb4 * kBlock;  // first packed channel of the 8-bit blocks
   uint8_t q4[kGroup];
   int8_t q8[kGroup];
   for (int64_t j = 0; j < N; ++j) {
@@ -208,8 +210,8 @@ int mixllm_pack_weights(const uint16_t *w, int32_t N, int32_t K, int32_t group, 
     const uint16_t *row = w + (size_t)n * (size_t)K;
     const int64_t b = j / kBlock;
     const int ch32 = (int)(j % kBlock);
-    if (j < L.n4) {
-      for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < G; ++g) {
+      if (j < j8) {  // a whole 4-bit block: packed nibbles
         uint8_t z;
         uint16_t s16;
         quant_group_w4(row + (size_t)g * kGroup, q4, &z, &s16);
@@ -223,17 +225,21 @@ int mixllm_pack_weights(const uint16_t *w, int32_t N, int32_t K, int32_t group, 
         }
         s4[cidx * 32 + ch32] = s16;
         z4[cidx * 16 + ch32 / 2] |= (uint8_t)(z << ((ch32 & 1) ? 4 : 0));
+        continue;
       }
-    } else {
-      const int64_t b8 = b - L.b8s;
-      for (int g = 0; g < G; ++g) {
-        uint16_t s16;
+      const size_t cidx = (size_t)(b - L.nb4) * G + g;
+      int8_t *chunk = w8 + cidx * mixllm::kW8Chunk;
+      uint16_t s16;
+      if (j < L.n4) {  // leftover 4-bit channel: int8 partial dequantization q - z
+        uint8_t z;
+        quant_group_w4(row + (size_t)g * kGroup, q4, &z, &s16);
+        for (int k = 0; k < kGroup; ++k) chunk[w8_code_pos(ch32, k)] = (int8_t)((int)q4[k] - (int)z);
+        zp[(size_t)(j - j8) * G + g] = z;
+      } else {
         quant_group_w8(row + (size_t)g * kGroup, q8, &s16);
-        const size_t cidx = (size_t)b8 * G + g;
-        int8_t *chunk = w8 + cidx * mixllm::kW8Chunk;
         for (int k = 0; k < kGroup; ++k) chunk[w8_code_pos(ch32, k)] = q8[k];
-        s8[cidx * 32 + ch32] = s16;
       }
+      s8[cidx * 32 + ch32] = s16;
     }
   }
   return MIXLLM_OK;
@@ -263,10 +269,12 @@ int mixllm_unpack_weights(const void *blob, size_t blob_bytes, uint8_t *q, uint8
   const uint8_t *w4 = base + L.off_w4;
   const uint16_t *s4 = (const uint16_t *)(base + L.off_s4);
   const uint8_t *z4 = base + L.off_z4;
-  const uint8_t *w8 = base + L.off_w8;
+  const int8_t *w8 = (const int8_t *)(base + L.off_w8);
   const uint16_t *s8 = (const uint16_t *)(base + L.off_s8);
+  const uint8_t *zp = base + L.off_zp;
   const int32_t *idx = (const int32_t *)(base + L.off_idx);
   const int G = L.G, K = L.K;
+  const int64_t j8 = (int64_t)L.nb4 * kBlock;
   for (int64_t j = 0; j < L.N; ++j) {
     const int32_t n = idx[j];
     if (n < 0 || n >= L.N) return MIXLLM_E_FORMAT;
@@ -274,25 +282,26 @@ int mixllm_unpack_weights(const void *blob, size_t blob_bytes, uint8_t *q, uint8
     const int ch32 = (int)(j % kBlock);
     is8[n] = j >= L.n4;
     for (int g = 0; g < G; ++g) {
-      if (j < L.n4) {
+      uint8_t *qrow = q + (size_t)n * K + (size_t)g * kGroup;
+      if (j < j8) {
         const size_t cidx = (size_t)b * G + g;
         const uint8_t *chunk = w4 + cidx * mixllm::kW4Chunk;
         for (int k = 0; k < kGroup; ++k) {
           size_t off;
           int hi;
           w4_code_pos(ch32, k, &off, &hi);
-          q[(size_t)n * K + (size_t)g * kGroup + k] = hi ? (chunk[off] >> 4) : (chunk[off] & 15);
+          qrow[k] = hi ? (chunk[off] >> 4) : (chunk[off] & 15);
         }
         s[(size_t)n * G + g] = s4[cidx * 32 + ch32];
         z[(size_t)n * G + g] = (z4[cidx * 16 + ch32 / 2] >> ((ch32 & 1) ? 4 : 0)) & 15;
-      } else {
-        const size_t cidx = (size_t)(b - L.b8s) * G + g;
-        const uint8_t *chunk = w8 + cidx * mixllm::kW8Chunk;
-        for (int k = 0; k < kGroup; ++k)
-          q[(size_t)n * K + (size_t)g * kGroup + k] = chunk[w8_code_pos(ch32, k)];
-        s[(size_t)n * G + g] = s8[cidx * 32 + ch32];
-        z[(size_t)n * G + g] = 0;
+        continue;
       }
+      const size_t cidx = (size_t)(b - L.nb4) * G + g;
+      const int8_t *chunk = w8 + cidx * mixllm::kW8Chunk;
+      const int zz = j < L.n4 ? zp[(size_t)(j - j8) * G + g] : 0;
+      for (int k = 0; k < kGroup; ++k) qrow[k] = (uint8_t)(chunk[w8_code_pos(ch32, k)] + zz);
+      s[(size_t)n * G + g] = s8[cidx * 32 + ch32];
+      z[(size_t)n * G + g] = (uint8_t)zz;
     }
   }
   return MIXLLM_OK;

@@ -50,11 +50,11 @@ class BlobInfo(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
                 ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("n8", ctypes.c_int32), ("n4", ctypes.c_int32), ("G", ctypes.c_int32),
-                ("nb", ctypes.c_int32), ("nb4", ctypes.c_int32), ("b8s", ctypes.c_int32),
-                ("nb8", ctypes.c_int32),
+                ("nb", ctypes.c_int32), ("nb4", ctypes.c_int32), ("nb8", ctypes.c_int32),
+                ("n4_promoted", ctypes.c_int32),
                 ("off_w4", ctypes.c_uint64), ("off_s4", ctypes.c_uint64), ("off_z4", ctypes.c_uint64),
-                ("off_w8", ctypes.c_uint64), ("off_s8", ctypes.c_uint64), ("off_idx", ctypes.c_uint64),
-                ("total_bytes", ctypes.c_uint64)]
+                ("off_w8", ctypes.c_uint64), ("off_s8", ctypes.c_uint64), ("off_zp", ctypes.c_uint64),
+                ("off_idx", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -69,9 +69,9 @@ _SIGS = {
     "mixllm_unpack_weights": ([_vp, _sz, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mixllm_quant_act": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mixllm_gemm_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
-    "mixllm_gemm_w4w8a8": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _i64, _vp, _sz, _vp],
+    "mixllm_gemm_w4w8a8": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _i64, _vp, _sz, _vp],
                            ctypes.c_int),
-    "mixllm_gemm_w4w8a8_partials": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp, _vp],
+    "mixllm_gemm_w4w8a8_partials": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp, _vp],
                                     ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -179,18 +179,20 @@ def mixllm_gemm_workspace_bytes(m: int, n: int, k: int, n8: int) -> int:
     return int(_lib.mixllm_gemm_workspace_bytes(m, n, k, n8))
 
 
-def mixllm_gemm_w4w8a8(aq, sa, m: int, n: int, k: int, n8: int, blob_dev, y, workspace=None, stream=None):
-    """y: fp16 [M, ldy] CUDA tensor; blob_dev: uint8 CUDA tensor holding the packed blob."""
+def mixllm_gemm_w4w8a8(aq, sa, asum, m: int, n: int, k: int, n8: int, blob_dev, y, workspace=None,
+                       stream=None):
+    """aq, sa, asum: outputs of mixllm_quant_act; y: fp16 [M, ldy] CUDA tensor;
+    blob_dev: uint8 CUDA tensor holding the packed blob."""
     ldy = y.stride(0) if y.dim() == 2 and m > 1 else n
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.mixllm_gemm_w4w8a8(_ptr(aq), _ptr(sa), m, n, k, n8, _ptr(blob_dev), blob_dev.numel(),
-                                   _ptr(y), ldy, _ptr(workspace), ws, _stream(stream)))
+    _check(_lib.mixllm_gemm_w4w8a8(_ptr(aq), _ptr(sa), _ptr(asum), m, n, k, n8, _ptr(blob_dev),
+                                   blob_dev.numel(), _ptr(y), ldy, _ptr(workspace), ws, _stream(stream)))
 
 
-def mixllm_gemm_w4w8a8_partials(aq, sa, m: int, n: int, k: int, n8: int, blob_dev, n_begin: int,
+def mixllm_gemm_w4w8a8_partials(aq, sa, asum, m: int, n: int, k: int, n8: int, blob_dev, n_begin: int,
                                 n_count: int, part, stream=None):
     """part: int32 [M, n_count, G] CUDA tensor."""
-    _check(_lib.mixllm_gemm_w4w8a8_partials(_ptr(aq), _ptr(sa), m, n, k, n8, _ptr(blob_dev),
+    _check(_lib.mixllm_gemm_w4w8a8_partials(_ptr(aq), _ptr(sa), _ptr(asum), m, n, k, n8, _ptr(blob_dev),
                                             blob_dev.numel(), n_begin, n_count, _ptr(part),
                                             _stream(stream)))
 
@@ -215,17 +217,18 @@ class PackedLinear:
         dev = self.device
         return dict(aq=torch.empty((m, self.k), dtype=torch.int8, device=dev),
                     sa=torch.empty((self.g, m), dtype=torch.float32, device=dev),
+                    asum=torch.empty((self.g, m), dtype=torch.int32, device=dev),
                     y=torch.empty((m, self.n), dtype=torch.float16, device=dev),
                     ws=self._workspace(m))
 
     def _workspace(self, m):
         nbytes = mixllm_gemm_workspace_bytes(m, self.n, self.k, self.n8)
-        return torch.empty(nbytes, dtype=torch.uint8, device=self.device) if nbytes else None
+        return torch.zeros(nbytes, dtype=torch.uint8, device=self.device) if nbytes else None
 
     def forward(self, a, bufs=None, stream=None):
         m = a.shape[0]
         bufs = bufs or self.buffers(m)
-        mixllm_quant_act(a, bufs["aq"], bufs["sa"], None, stream)
-        mixllm_gemm_w4w8a8(bufs["aq"], bufs["sa"], m, self.n, self.k, self.n8, self.blob, bufs["y"],
-                           bufs["ws"], stream)
+        mixllm_quant_act(a, bufs["aq"], bufs["sa"], bufs["asum"], stream)
+        mixllm_gemm_w4w8a8(bufs["aq"], bufs["sa"], bufs["asum"], m, self.n, self.k, self.n8, self.blob,
+                           bufs["y"], bufs["ws"], stream)
         return bufs["y"]
