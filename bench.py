@@ -30,6 +30,7 @@ sys.path.insert(0, HERE)
 
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, published
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+SPIN_CYCLES = 50_000_000    # head start of the timed region (about 20 ms of GPU clock)
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemm_w4w8a8_M512_N4096_K4096_p10_traffic.json")
 GEMM_SRC = os.path.join(HERE, "weight_activation_quantized_amd", "csrc", "mixllm_gemm.hip")
 
@@ -45,6 +46,9 @@ def parse():
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--k", type=int, default=4096)
     ap.add_argument("--p8", type=float, default=0.10)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB before the steps, as the "
+                         "known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -137,34 +141,66 @@ def main():
     ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, n8)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream()
+    if args.copy_calib_mib:
+        src = torch.ones(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
-    def step(i, ev=None):
-        s = S[i % sets]
-        if ev is not None:
-            ev[0].record(stream)
-        L.mixllm_quant_act(s["a"], s["aq"], s["sa"], s["asum"], stream)
-        if ev is not None:
-            ev[1].record(stream)
-        L.mixllm_gemm_w4w8a8(s["aq"], s["sa"], s["asum"], m, n, k, n8, s["blob"], s["y"], ws, stream)
-        if ev is not None:
-            ev[2].record(stream)
+    # Launch arguments of every set, prepared once: the timed loop makes two plain C calls
+    # per step, so the host enqueues steps faster than the GPU runs them.
+    lib = L.library_handle()
+    qa_fn, gm_fn = lib.mixllm_quant_act, lib.mixllm_gemm_w4w8a8
+    sp = stream.cuda_stream
+    wsp, wsb = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
+    qargs = [(s["a"].data_ptr(), k, m, k, 128, s["aq"].data_ptr(), s["sa"].data_ptr(), s["asum"].data_ptr(), sp)
+             for s in S]
+    gargs = [(s["aq"].data_ptr(), s["sa"].data_ptr(), s["asum"].data_ptr(), m, n, k, n8, s["blob"].data_ptr(),
+              s["blob"].numel(), s["y"].data_ptr(), n, wsp, wsb, sp) for s in S]
 
+    def quant(i):
+        return qa_fn(*qargs[i % sets])
+
+    def gemm(i):
+        return gm_fn(*gargs[i % sets])
+
+    rc = 0
     for i in range(args.warmup):
-        step(i)
+        rc = rc or quant(i) or gemm(i)
     torch.cuda.synchronize()
+    if rc:
+        raise L.MixLLMError(rc)
 
-    # timed region: exactly `steps` steps, HIP events on the launch stream before, between
-    # and after the two kernels of every step
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps, each quant_act + GEMM on its own batch (set).
+    # The steps run in chunks of `sets`: the chunk's quant_act launches, then its GEMM
+    # launches, with one HIP event on the launch stream after each run of launches, so
+    # the per-kernel durations come from events without an event between every two
+    # kernels (an event costs a few microseconds of queue time).  A spin kernel queued
+    # first keeps the GPU busy while the host enqueues; the step clock starts at the
+    # event after it.
+    chunks = [(i, min(sets, args.steps - i)) for i in range(0, args.steps, sets)]
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_q = [torch.cuda.Event(enable_timing=True) for _ in chunks]
+    e_g = [torch.cuda.Event(enable_timing=True) for _ in chunks]
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
+    torch.cuda._sleep(SPIN_CYCLES)
+    e_start.record(stream)
+    for c, (i0, cnt) in enumerate(chunks):
+        for i in range(i0, i0 + cnt):
+            rc = rc or quant(i)
+        e_q[c].record(stream)
+        for i in range(i0, i0 + cnt):
+            rc = rc or gemm(i)
+        e_g[c].record(stream)
     torch.cuda.synchronize()
-    step_ms = evs[0][0].elapsed_time(evs[-1][2]) / args.steps
-    q_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    g_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    gemm_us = 1e3 * float(np.mean(g_ms))
-    quant_us = 1e3 * float(np.mean(q_ms))
+    if rc:
+        raise L.MixLLMError(rc)
+    step_ms = e_start.elapsed_time(e_g[-1]) / args.steps
+    q_ms = sum((e_start if c == 0 else e_g[c - 1]).elapsed_time(e_q[c]) for c in range(len(chunks)))
+    g_ms = sum(e_q[c].elapsed_time(e_g[c]) for c in range(len(chunks)))
+    gemm_us = 1e3 * g_ms / args.steps
+    quant_us = 1e3 * q_ms / args.steps
 
     ops = 2.0 * m * n * k
     value = ops / (step_ms * 1e-3) / 1e12

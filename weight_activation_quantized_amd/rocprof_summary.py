@@ -1,0 +1,144 @@
+"""Turns rocprofv3 CSV output into the short text/JSON summaries kept under profiles/.
+
+  python -m weight_activation_quantized_amd.rocprof_summary stats DIR --cmd "..." > summary.txt
+      per-kernel dispatch count and mean/min/max duration from DIR's *_kernel_stats.csv.
+
+  python -m weight_activation_quantized_amd.rocprof_summary traffic --fetch DIR1 --write DIR2 \
+      --kernel NAME --copy-bytes B --cmd-fetch "..." --cmd-write "..." > traffic.json
+      HBM bytes per dispatch of kernel NAME from a FETCH_SIZE pass and a WRITE_SIZE pass
+      (KiB per dispatch), each scaled by what the same counter reads for the plain
+      device-to-device copy of B bytes (the runtime's copyBuffer kernel) in the same
+      pass: factor = B / counter bytes of the copy.
+
+Reads only CSV files; runs nothing.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+COPY_KERNEL = "copyBuffer"
+
+
+def _find(d, suffix):
+    out = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not out:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return out
+
+
+def short_name(name):
+    name = name.replace("(anonymous namespace)::", "")
+    cut = name.find("(")
+    if cut > 0:
+        name = name[:cut]
+    return name.replace("void ", "")
+
+
+def kernel_stats(d):
+    rows = []
+    for f in _find(d, "_kernel_stats.csv"):
+        for r in csv.DictReader(open(f)):
+            rows.append(dict(name=short_name(r["Name"]), calls=int(r["Calls"]),
+                             avg_us=float(r["AverageNs"]) / 1e3, min_us=float(r["MinNs"]) / 1e3,
+                             max_us=float(r["MaxNs"]) / 1e3, pct=float(r["Percentage"])))
+    return rows
+
+
+def counter_per_dispatch(d, counter):
+    """{kernel short name: [value per dispatch]} for one counter (rows of one dispatch summed)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for f in _find(d, "_counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            per[short_name(r["Kernel_Name"])][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def _pick(table, kernel):
+    hits = [k for k in table if kernel in k]
+    if len(hits) != 1:
+        raise SystemExit(f"kernel {kernel!r} matches {hits} in {sorted(table)}")
+    return table[hits[0]]
+
+
+def cmd_stats(a):
+    rows = kernel_stats(a.dir)
+    print(f"# rocprofv3 kernel-trace summary: {a.title}")
+    print(f"# command: {a.cmd}")
+    print("#")
+    print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'time%':>6s}")
+    for r in sorted(rows, key=lambda r: -r["pct"]):
+        print(f"{r['name'][:60]:60s} {r['calls']:6d} {r['avg_us']:9.3f} {r['min_us']:9.3f} "
+              f"{r['max_us']:9.3f} {r['pct']:6.2f}")
+
+
+def cmd_traffic(a):
+    fetch = counter_per_dispatch(a.fetch, "FETCH_SIZE")
+    write = counter_per_dispatch(a.write, "WRITE_SIZE")
+    kf, kw = _pick(fetch, a.kernel), _pick(write, a.kernel)
+    cf, cw = _pick(fetch, COPY_KERNEL), _pick(write, COPY_KERNEL)
+    # the largest copy dispatch is the calibration copy of --copy-bytes
+    ff = a.copy_bytes / (max(cf) * 1024.0)
+    fw = a.copy_bytes / (max(cw) * 1024.0)
+    f_kib, w_kib = statistics.mean(kf), statistics.mean(kw)
+    src_hash = None
+    if a.source:
+        with open(a.source, "rb") as f:
+            src_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+    out = {
+        "kernel": a.kernel,
+        "workload": a.workload,
+        "dispatches": [len(kf), len(kw)],
+        "fetch_kib_per_dispatch_raw": round(f_kib, 2),
+        "write_kib_per_dispatch_raw": round(w_kib, 2),
+        "copy_bytes": a.copy_bytes,
+        "copy_fetch_kib_raw": round(max(cf), 2),
+        "copy_write_kib_raw": round(max(cw), 2),
+        "fetch_scale": round(ff, 4),
+        "write_scale": round(fw, 4),
+        "hbm_read_bytes_per_launch": round(f_kib * 1024.0 * ff),
+        "hbm_write_bytes_per_launch": round(w_kib * 1024.0 * fw),
+        "hbm_bytes_per_launch": round(f_kib * 1024.0 * ff + w_kib * 1024.0 * fw),
+        "gemm_source_sha256_16": src_hash,
+        "command_fetch": a.cmd_fetch,
+        "command_write": a.cmd_write,
+    }
+    if a.algorithmic_bytes:
+        out["algorithmic_bytes"] = a.algorithmic_bytes
+        out["traffic_over_algorithmic"] = round(out["hbm_bytes_per_launch"] / a.algorithmic_bytes, 3)
+    json.dump(out, sys.stdout, indent=1)
+    print()
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--workload", default="")
+    t.add_argument("--source", default="")
+    t.add_argument("--algorithmic-bytes", type=float, default=0.0)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    a = ap.parse_args(argv)
+    (cmd_stats if a.what == "stats" else cmd_traffic)(a)
+
+
+if __name__ == "__main__":
+    main()
