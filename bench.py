@@ -127,7 +127,7 @@ def main():
     # one packed layer + activations on the host, replicated into rotating device sets
     a16, w16, idx8 = WL.make_layer_inputs(sh)
     blob_host = L.mixllm_pack_weights(w16, idx8)
-    set_bytes = blob_host.size + m * k * 2 + m * k + 8 * g * m + 2 * m * n
+    set_bytes = blob_host.size + m * k * 2 + m * k + 40 * g * m + 2 * m * n
     sets = args.sets or max(4, int(np.ceil(512e6 / set_bytes)))
     base_blob = torch.from_numpy(blob_host).to(dev)
     base_a = torch.from_numpy(a16).to(dev)
@@ -137,6 +137,7 @@ def main():
                       aq=torch.empty((m, k), dtype=torch.int8, device=dev),
                       sa=torch.empty((g, m), dtype=torch.float32, device=dev),
                       asum=torch.empty((g, m), dtype=torch.int32, device=dev),
+                      rowop=L.rowop_buffer(m, k, dev),
                       y=torch.empty((m, n), dtype=torch.float16, device=dev)))
     ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, n8)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
@@ -154,10 +155,10 @@ def main():
     qa_fn, gm_fn = lib.mixllm_quant_act, lib.mixllm_gemm_w4w8a8
     sp = stream.cuda_stream
     wsp, wsb = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
-    qargs = [(s["a"].data_ptr(), k, m, k, 128, s["aq"].data_ptr(), s["sa"].data_ptr(), s["asum"].data_ptr(), sp)
-             for s in S]
-    gargs = [(s["aq"].data_ptr(), s["sa"].data_ptr(), s["asum"].data_ptr(), m, n, k, n8, s["blob"].data_ptr(),
-              s["blob"].numel(), s["y"].data_ptr(), n, wsp, wsb, sp) for s in S]
+    qargs = [(s["a"].data_ptr(), k, m, k, 128, s["aq"].data_ptr(), s["sa"].data_ptr(), s["asum"].data_ptr(),
+              s["rowop"].data_ptr(), sp) for s in S]
+    gargs = [(s["aq"].data_ptr(), s["sa"].data_ptr(), s["asum"].data_ptr(), s["rowop"].data_ptr(), m, n, k, n8,
+              s["blob"].data_ptr(), s["blob"].numel(), s["y"].data_ptr(), n, wsp, wsb, sp) for s in S]
 
     def quant(i):
         return qa_fn(*qargs[i % sets])

@@ -43,7 +43,7 @@ extern "C" {
 
 #define MIXLLM_GROUP 128
 #define MIXLLM_BLOB_MAGIC 0x344C584Du /* "MXL4" little-endian */
-#define MIXLLM_BLOB_VERSION 2u
+#define MIXLLM_BLOB_VERSION 3u
 
 typedef enum mixllm_status {
   MIXLLM_OK = 0,
@@ -65,7 +65,7 @@ typedef struct mixllm_blob_info {
   int32_t nb4;                  /* 4-bit blocks: floor(n4 / 32) */
   int32_t nb8;                  /* 8-bit blocks: nb - nb4 */
   int32_t n4_promoted;          /* n4 - 32 nb4 4-bit channels stored in the first 8-bit block */
-  uint64_t off_w4, off_s4, off_z4, off_w8, off_s8, off_zp, off_idx, total_bytes;
+  uint64_t off_w4, off_s4, off_z4, off_w8, off_s8, off_zp, off_idx, off_pw, total_bytes;
 } mixllm_blob_info;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -92,8 +92,9 @@ const char *mixllm_status_str(int status);
  * to a multiple of 32, in blocks of 32 channels.  Whole blocks of 4-bit channels keep
  * packed nibbles; the n4 % 32 leftover 4-bit channels share the first 8-bit block,
  * stored as their int8 partial dequantization (q - z) (the same two-step arithmetic).
- * The blob is position independent: a byte copy of it to device memory is what the
- * GEMM reads.
+ * The blob also holds, per channel and group, s_w and -z * s_w as exact sums of two bf16
+ * values (the column operands of the GEMM's scale products).  The blob is position
+ * independent: a byte copy of it to device memory is what the GEMM reads.
  * ------------------------------------------------------------------------------------ */
 
 /* Size in bytes of the blob for these parameters, or 0 if they are invalid. */
@@ -134,10 +135,15 @@ int mixllm_unpack_weights(const void *blob_host, size_t blob_bytes, uint8_t *q, 
  * sa_dev:     output fp32 [G][M] (group-major: the scales of one group for consecutive
  *             tokens are contiguous).
  * asum_dev:   output int32 [G][M] code sums, or NULL to skip.
+ * rowop_dev:  output uint32 [G][2][M][4], or NULL to skip: the row operands of the GEMM's
+ *             scale products.  [g][0][m] holds s and [g][1][m] holds u = fp32(S_A * s), each
+ *             as three bf16 values p0 + p1 + p2 that sum to it exactly (p0 = s truncated to
+ *             bf16, p1 = the remainder truncated, p2 = the rest), stored as the words
+ *             {p0 | p0 << 16, p1 | p1 << 16, p2 | p2 << 16, 0}.
  * Errors: E_NULL, E_SHAPE, E_GROUP, E_HIP.
  * ------------------------------------------------------------------------------------ */
 int mixllm_quant_act(const uint16_t *a_fp16_dev, int64_t lda, int32_t M, int32_t K, int32_t group,
-                     int8_t *aq_dev, float *sa_dev, int32_t *asum_dev, void *stream);
+                     int8_t *aq_dev, float *sa_dev, int32_t *asum_dev, uint32_t *rowop_dev, void *stream);
 
 /* ------------------------------------------------------------------------------------
  * Mixed W4/W8 x A8 GEMM with scatter epilogue (device).
@@ -149,27 +155,22 @@ int mixllm_quant_act(const uint16_t *a_fp16_dev, int64_t lda, int32_t M, int32_t
  * are disjoint sub-GEMMs run in one grid (talk notes, 並列実行); the epilogue writes each
  * channel's fp16 result (round to nearest even) to its original index.  The zero point
  * of a 4-bit channel enters as sum_k (q - z) a_k = sum_k q a_k - z S_A, with S_A the
- * group's activation code sum from mixllm_quant_act.
+ * group's activation code sum.
  *
- * aq_dev, sa_dev, asum_dev: as produced by mixllm_quant_act for the same M and K
- *                 (asum_dev is required here).
+ * aq_dev, sa_dev, asum_dev, rowop_dev: as produced by mixllm_quant_act for the same M and K
+ *                 (all four are required here).
  * blob_dev:       device copy of a blob packed for this N, K, n8 (blob_bytes long).
  * y_fp16_dev:     output fp16 [M][ldy], ldy >= N; only columns 0..N-1 are written.
- * workspace_dev:  scratch of at least mixllm_gemm_workspace_bytes(M, N, K, n8) bytes
- *                 (16-byte aligned), or NULL when that is 0.  When the grid has too
- *                 few output tiles to give every CU two workgroups, the groups of each
- *                 tile are split over several workgroups; the workspace holds their
- *                 partial tiles and per-tile arrival counters.  Zero-fill it before its
- *                 first use; every call leaves the counters zero again, so one workspace
- *                 serves any number of calls in sequence, but calls that overlap in time
- *                 must not share one.
- * Errors: E_NULL, E_SHAPE, E_GROUP, E_INDEX, E_SPACE, E_HIP.
+ * workspace_dev:  reserved; pass NULL and 0 (mixllm_gemm_workspace_bytes returns 0: no
+ *                 kernel needs scratch memory).
+ * Errors: E_NULL, E_SHAPE (also when G * M * 32 exceeds 2^31 - 1 for M > 64), E_GROUP,
+ * E_INDEX, E_SPACE, E_HIP.
  * ------------------------------------------------------------------------------------ */
 size_t mixllm_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n8);
 
-int mixllm_gemm_w4w8a8(const int8_t *aq_dev, const float *sa_dev, const int32_t *asum_dev, int32_t M, int32_t N,
-                       int32_t K, int32_t n8, const void *blob_dev, size_t blob_bytes, uint16_t *y_fp16_dev,
-                       int64_t ldy, void *workspace_dev, size_t workspace_bytes, void *stream);
+int mixllm_gemm_w4w8a8(const int8_t *aq_dev, const float *sa_dev, const int32_t *asum_dev, const uint32_t *rowop_dev,
+                       int32_t M, int32_t N, int32_t K, int32_t n8, const void *blob_dev, size_t blob_bytes,
+                       uint16_t *y_fp16_dev, int64_t ldy, void *workspace_dev, size_t workspace_bytes, void *stream);
 
 /*
  * Test entry point: the same integer inner loop as mixllm_gemm_w4w8a8, but instead of
@@ -178,9 +179,10 @@ int mixllm_gemm_w4w8a8(const int8_t *aq_dev, const float *sa_dev, const int32_t 
  * p_dev: int32 [M][n_count][G].  Errors: as mixllm_gemm_w4w8a8, plus E_SHAPE when the
  * window is outside [0, N).
  */
-int mixllm_gemm_w4w8a8_partials(const int8_t *aq_dev, const float *sa_dev, const int32_t *asum_dev, int32_t M,
-                                int32_t N, int32_t K, int32_t n8, const void *blob_dev, size_t blob_bytes,
-                                int32_t n_begin, int32_t n_count, int32_t *p_dev, void *stream);
+int mixllm_gemm_w4w8a8_partials(const int8_t *aq_dev, const float *sa_dev, const int32_t *asum_dev,
+                                const uint32_t *rowop_dev, int32_t M, int32_t N, int32_t K, int32_t n8,
+                                const void *blob_dev, size_t blob_bytes, int32_t n_begin, int32_t n_count,
+                                int32_t *p_dev, void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,7 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
-Bit-exact: int8 activation codes, fp32 activation scales, code sums, int32 group
-partials.  Within tolerance (2 fp16 ulp of the oracle value + 1e-3 max|Y|): the fp16
+Bit-exact: int8 activation codes, fp32 activation scales, code sums, the bf16 row
+operands of the scale products, int32 group partials.  Within tolerance (2 fp16 ulp of the oracle value + 1e-3 max|Y|): the fp16
 layer output.  Small shapes compare every element; the five workloads at their full
 sizes compare sampled rows x columns (the oracle computes exactly those) and a window
 of group partials.
@@ -42,8 +42,25 @@ def _quant(L, a16, lda_pad=0, with_sum=True):
     aq = torch.empty((m, k), dtype=torch.int8, device="cuda")
     sa = torch.empty((k // 128, m), dtype=torch.float32, device="cuda")
     asum = torch.empty((k // 128, m), dtype=torch.int32, device="cuda") if with_sum else None
-    L.mixllm_quant_act(a, aq, sa, asum)
-    return aq, sa, asum
+    rowop = L.rowop_buffer(m, k)
+    L.mixllm_quant_act(a, aq, sa, asum, rowop)
+    return aq, sa, asum, rowop
+
+
+def _split3_words(x32):
+    """Host-side exact three-way bf16 split of fp32 values, as the row operand words
+    [p0 p0, p1 p1, p2 p2, 0] (uint32)."""
+    x32 = np.asarray(x32, np.float32)
+    b0 = x32.view(np.uint32) & np.uint32(0xFFFF0000)
+    r1 = (x32 - b0.view(np.float32)).astype(np.float32)
+    b1 = r1.view(np.uint32) & np.uint32(0xFFFF0000)
+    r2 = (r1 - b1.view(np.float32)).astype(np.float32)
+    b2 = r2.view(np.uint32) & np.uint32(0xFFFF0000)
+    # exactness: the three pieces sum to x in float64
+    tot = b0.view(np.float32).astype(np.float64) + b1.view(np.float32) + b2.view(np.float32)
+    assert np.array_equal(tot, x32.astype(np.float64))
+    words = [b | (b >> np.uint32(16)) for b in (b0, b1, b2)] + [np.zeros_like(b0)]
+    return np.stack(words, axis=-1)
 
 
 # --------------------------------------------------------------------------- quant_act
@@ -59,12 +76,16 @@ def test_quant_act_bitexact(L, m, k, dist):
     if m > 2:
         a16[1, :128] = 0  # an all-zero group
     U.say("quant_act", m, k, dist)
-    aq, sa, asum = _quant(L, a16, lda_pad=8 if m % 2 else 0)
+    aq, sa, asum, rowop = _quant(L, a16, lda_pad=8 if m % 2 else 0)
     torch.cuda.synchronize()
     oq, osa, osum = O.quant_act(a16)
     assert np.array_equal(aq.cpu().numpy(), oq)
     assert np.array_equal(sa.cpu().numpy().T.view(np.uint32), osa.view(np.uint32))
     assert np.array_equal(asum.cpu().numpy().T, osum)
+    # row operands: [g][0][m] splits s_a, [g][1][m] splits fp32(S_A * s_a)
+    ro = rowop.cpu().numpy().view(np.uint32)
+    assert np.array_equal(ro[:, 0], _split3_words(osa.T))
+    assert np.array_equal(ro[:, 1], _split3_words(osum.T.astype(np.float32) * osa.T))
 
 
 def test_quant_act_golden_ties(L):
@@ -74,7 +95,7 @@ def test_quant_act_golden_ties(L):
     rows = [pins._group_vec(ex) for ex in gold["activation"]]
     a16 = np.stack(rows).astype(np.float16)
     U.say("quant_act golden")
-    aq, sa, asum = _quant(L, a16)
+    aq, sa, asum, _ = _quant(L, a16)
     torch.cuda.synchronize()
     for i, ex in enumerate(gold["activation"]):
         assert float(sa[0, i].item()) == ex["scale"]
@@ -90,6 +111,8 @@ SMALL = [
     (16, 512, 1024, 52), (1, 512, 1024, 52), (4, 100, 256, 7), (17, 96, 384, 0), (31, 96, 384, 96),
     (33, 160, 256, 64), (64, 64, 128, 1), (65, 200, 512, 31), (100, 72, 256, 8), (130, 300, 384, 30),
     (1, 1, 128, 0), (3, 1, 128, 1), (256, 520, 640, 52), (200, 33, 256, 32),
+    # tile kernel: slices with an odd step count, the LDS stage ring wrapping several times
+    (160, 288, 1920, 40), (96, 130, 2688, 13),
 ]
 
 
@@ -97,12 +120,11 @@ def _run_gemm(L, a16, w16, idx8, ldy_pad=0):
     m, k = a16.shape
     n = w16.shape[0]
     blob = _dev(L.mixllm_pack_weights(w16, idx8))
-    aq, sa, asum = _quant(L, a16)
+    aq, sa, asum, rowop = _quant(L, a16)
     y = torch.full((m, n + ldy_pad), float("nan"), dtype=torch.float16, device="cuda")
-    ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, len(idx8))
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
-    L.mixllm_gemm_w4w8a8(aq, sa, asum, m, n, k, len(idx8), blob, y, ws)
-    return blob, aq, sa, asum, y
+    assert L.mixllm_gemm_workspace_bytes(m, n, k, len(idx8)) == 0
+    L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, m, n, k, len(idx8), blob, y)
+    return blob, (aq, sa, asum, rowop), y
 
 
 @pytest.mark.parametrize("m,n,k,n8", SMALL)
@@ -110,7 +132,7 @@ def test_gemm_full_compare(L, m, n, k, n8):
     sh = WL.Shape(0, "edge", m, n, k, n8)
     a16, w16, idx8 = WL.make_layer_inputs(sh)
     U.say("gemm full", sh.name)
-    blob, aq, sa, asum, y = _run_gemm(L, a16, w16, idx8, ldy_pad=5)
+    blob, qa, y = _run_gemm(L, a16, w16, idx8, ldy_pad=5)
     torch.cuda.synchronize()
     ref = U.oracle_at(a16, w16, idx8)
     yg = y.cpu().numpy()
@@ -120,33 +142,28 @@ def test_gemm_full_compare(L, m, n, k, n8):
     g = k // 128
     part = torch.zeros((m, n, g), dtype=torch.int32, device="cuda")
     U.say("gemm partials", sh.name)
-    L.mixllm_gemm_w4w8a8_partials(aq, sa, asum, m, n, k, n8, blob, 0, n, part)
+    L.mixllm_gemm_w4w8a8_partials(*qa, m, n, k, n8, blob, 0, n, part)
     torch.cuda.synchronize()
     assert np.array_equal(part.cpu().numpy().astype(np.int64), U.partials_at(ref))
 
 
-@pytest.mark.parametrize("m,n,k,n8", [(128, 256, 1024, 26), (512, 4096, 4096, 410), (65, 4100, 256, 500)])
-def test_gemm_split_workspace_reuse(L, m, n, k, n8):
-    """Split-K tiles: repeated calls on one workspace give bit-identical outputs, and the
-    arrival counters are back at zero after each call."""
+@pytest.mark.parametrize("m,n,k,n8", [(128, 256, 1024, 26), (512, 4096, 4096, 410), (65, 4100, 256, 500),
+                                    (192, 384, 128, 40)])
+def test_gemm_repeat_deterministic(L, m, n, k, n8):
+    """Repeated calls give bit-identical outputs (the group slices of a tile are summed in a
+    fixed order); one group per channel (K = 128) leaves some slices empty."""
     sh = WL.Shape(0, "edge", m, n, k, n8)
     a16, w16, idx8 = WL.make_layer_inputs(sh)
-    ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, n8)
-    U.say("gemm workspace reuse", sh.name, ws_bytes)
+    U.say("gemm repeat", sh.name)
     blob = _dev(L.mixllm_pack_weights(w16, idx8))
-    aq, sa, asum = _quant(L, a16)
-    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    qa = _quant(L, a16)
     ys = []
     for _ in range(3):
         y = torch.empty((m, n), dtype=torch.float16, device="cuda")
-        L.mixllm_gemm_w4w8a8(aq, sa, asum, m, n, k, n8, blob, y, ws if ws_bytes else None)
+        L.mixllm_gemm_w4w8a8(*qa, m, n, k, n8, blob, y)
         torch.cuda.synchronize()
         ys.append(y.cpu().numpy())
     assert all(np.array_equal(ys[0].view(np.uint16), y.view(np.uint16)) for y in ys[1:])
-    if ws_bytes:
-        tiles = ((m + 63) // 64) * (((n + 31) // 32 + 3) // 4)
-        cnt_bytes = ((tiles * 4 + 255) // 256) * 256
-        assert int(ws[ws_bytes - cnt_bytes:].count_nonzero()) == 0
     if m * n * k <= 2 ** 24:
         U.assert_y_close(ys[0], U.oracle_at(a16, w16, idx8)["y16"], sh.name)
 
@@ -162,9 +179,9 @@ def test_gemm_golden_tiny(L):
     w4 = next(e for e in gold["weight4"] if e["name"] == "mixed_sign_ties")
     w16 = np.stack([pins._group_vec(w8), pins._group_vec(w4)]).astype(np.float16)
     U.say("gemm golden tiny")
-    blob, aq, sa, asum, y = _run_gemm(L, a16, w16, np.array(t["idx8"], np.int32))
+    blob, qa, y = _run_gemm(L, a16, w16, np.array(t["idx8"], np.int32))
     part = torch.zeros((1, 2, 1), dtype=torch.int32, device="cuda")
-    L.mixllm_gemm_w4w8a8_partials(aq, sa, asum, 1, 2, 128, 1, blob, 0, 2, part)
+    L.mixllm_gemm_w4w8a8_partials(*qa, 1, 2, 128, 1, blob, 0, 2, part)
     torch.cuda.synchronize()
     assert [float(v) for v in y[0].cpu().numpy()] == t["y16"]
     assert [int(v) for v in part[0, :, 0].cpu().numpy()] == t["partials"]
@@ -174,14 +191,17 @@ def test_gemm_m_zero_and_errors(L):
     sh = WL.Shape(0, "edge", 4, 64, 256, 3)
     a16, w16, idx8 = WL.make_layer_inputs(sh)
     blob = _dev(L.mixllm_pack_weights(w16, idx8))
-    aq, sa, asum = _quant(L, a16)
+    aq, sa, asum, rowop = _quant(L, a16)
     y = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
-    L.mixllm_gemm_w4w8a8(aq, sa, asum, 0, 64, 256, 3, blob, y)
+    L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, 0, 64, 256, 3, blob, y)
     with pytest.raises(L.MixLLMError) as e:
-        L.mixllm_gemm_w4w8a8(aq, sa, asum, 4, 64, 256, 3, blob[:-1], y)
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, 4, 64, 256, 3, blob[:-1], y)
     assert e.value.status == -5
     with pytest.raises(L.MixLLMError) as e:
-        L.mixllm_gemm_w4w8a8(aq, sa, None, 4, 64, 256, 3, blob, y)
+        L.mixllm_gemm_w4w8a8(aq, sa, None, rowop, 4, 64, 256, 3, blob, y)
+    assert e.value.status == -1
+    with pytest.raises(L.MixLLMError) as e:
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, None, 4, 64, 256, 3, blob, y)
     assert e.value.status == -1
     torch.cuda.synchronize()
     assert float(y.abs().max()) == 0.0
@@ -214,15 +234,14 @@ def test_gemm_workloads_sampled(L, key, ms):
         a16 = WL.make_acts(m, k, sh.seed, dist)
         rows = U.sample_rows(m, rng)
         U.say("gemm sampled", sh.name)
-        aq, sa, asum = _quant(L, a16)
+        qa = _quant(L, a16)
+        aq = qa[0]
         y = torch.empty((m, n), dtype=torch.float16, device="cuda")
-        ws_bytes = L.mixllm_gemm_workspace_bytes(m, n, k, n8)
-        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
-        L.mixllm_gemm_w4w8a8(aq, sa, asum, m, n, k, n8, blob, y, ws)
+        L.mixllm_gemm_w4w8a8(*qa, m, n, k, n8, blob, y)
         win = int(rng.integers(0, n - 48)) if n > 48 else 0
         cnt = min(48, n - win)
         part = torch.zeros((m, cnt, k // 128), dtype=torch.int32, device="cuda")
-        L.mixllm_gemm_w4w8a8_partials(aq, sa, asum, m, n, k, n8, blob, win, cnt, part)
+        L.mixllm_gemm_w4w8a8_partials(*qa, m, n, k, n8, blob, win, cnt, part)
         torch.cuda.synchronize()
         ref = U.oracle_at(a16, w16, idx8, rows, cols)
         if m == ms[0]:

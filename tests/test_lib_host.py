@@ -57,6 +57,41 @@ def test_pack_matches_oracle(n, k, n8):
     assert info["total_bytes"] == blob.size == L.mixllm_packed_bytes(n, k, 128, n8)
 
 
+def _bf16_pair_value(words):
+    """Value of packed bf16 pairs (low half + high half), exactly, in float64."""
+    lo = ((words & 0xFFFF).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    hi = ((words >> 16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return lo + hi
+
+
+@pytest.mark.parametrize("n,k,n8", [(200, 512, 169), (100, 384, 7), (64, 256, 0)])
+def test_pack_scale_words(n, k, n8):
+    """The pw section holds s_w and -z * s_w of every packed channel as exact bf16 pairs
+    (0 in the second word for 8-bit, promoted and empty channels)."""
+    sh = WL.Shape(0, "edge", 1, n, k, n8)
+    w, idx8 = WL.make_layer_weights(sh)
+    blob = L.mixllm_pack_weights(w, idx8)
+    info = L.mixllm_blob_get_info(blob)
+    q, z, s16, is8 = L.mixllm_unpack_weights(blob)
+    g = k // 128
+    nb = info["nb"]
+    pw = blob[info["off_pw"]: info["off_pw"] + nb * g * 256].view(np.uint32).reshape(nb, g, 32, 2)
+    idx = blob[info["off_idx"]: info["off_idx"] + nb * 32 * 4].view(np.int32)
+    s64 = s16.astype(np.float64)
+    for j in range(nb * 32):
+        b, c = divmod(j, 32)
+        sw = _bf16_pair_value(pw[b, :, c, 0])
+        zw = _bf16_pair_value(pw[b, :, c, 1])
+        o = idx[j]
+        if o < 0:
+            assert not sw.any() and not zw.any()
+            continue
+        assert np.array_equal(sw, s64[o]), j
+        in_nibbles = j < 32 * info["nb4"]
+        expect_z = -(z[o].astype(np.float64) * s64[o]) if in_nibbles else np.zeros(g)
+        assert np.array_equal(zw, expect_z), j
+
+
 def test_pack_special_groups():
     """All-zero groups, one-signed groups, subnormal-range groups and the golden ties."""
     rng = np.random.default_rng(7)
@@ -91,6 +126,7 @@ def test_packed_bytes_formula():
         g = k // 128
         w_bytes = 32 * k * (nb4 * O.weight_footprint(4) + nb8 * O.weight_footprint(8))
         side = 32 * g  # zero points of the <= 31 promoted 4-bit channels (unpacking only)
+        side += nb * g * 256  # the tile kernel's scale words, 8 bytes per channel and group
         size = L.mixllm_packed_bytes(n, k, 128, n8)
         assert w_bytes + 4 * 32 * nb + side <= size <= w_bytes + 4 * 32 * nb + side + 8 * 256 + 256
         # the padding to 32-channel blocks and the <= 31 4-bit channels stored as int8
@@ -150,34 +186,42 @@ def test_device_entry_points_validate_on_host():
     odd = ctypes.c_void_p(0x10004)
     s = ctypes.c_void_p(0)
     qa = lib.mixllm_quant_act
-    assert qa(fake, 256, 4, 256, 64, fake, fake, None, s) == -3
-    assert qa(fake, 256, 4, 200, 128, fake, fake, None, s) == -2
-    assert qa(fake, 128, 4, 256, 128, fake, fake, None, s) == -2      # lda < K
-    assert qa(fake, 260, 4, 256, 128, fake, fake, None, s) == -2      # lda % 8
-    assert qa(fake, 256, -1, 256, 128, fake, fake, None, s) == -2
-    assert qa(None, 256, 4, 256, 128, fake, fake, None, s) == -1
-    assert qa(fake, 256, 4, 256, 128, None, fake, None, s) == -1
-    assert qa(odd, 256, 4, 256, 128, fake, fake, None, s) == -2
-    assert qa(fake, 256, 4, 256, 128, fake, fake, odd, s) == -2
-    assert qa(None, 256, 0, 256, 128, None, None, None, s) == 0       # M = 0: no-op
+    assert qa(fake, 256, 4, 256, 64, fake, fake, None, None, s) == -3
+    assert qa(fake, 256, 4, 200, 128, fake, fake, None, None, s) == -2
+    assert qa(fake, 128, 4, 256, 128, fake, fake, None, None, s) == -2      # lda < K
+    assert qa(fake, 260, 4, 256, 128, fake, fake, None, None, s) == -2      # lda % 8
+    assert qa(fake, 256, -1, 256, 128, fake, fake, None, None, s) == -2
+    assert qa(None, 256, 4, 256, 128, fake, fake, None, None, s) == -1
+    assert qa(fake, 256, 4, 256, 128, None, fake, None, None, s) == -1
+    assert qa(odd, 256, 4, 256, 128, fake, fake, None, None, s) == -2
+    assert qa(fake, 256, 4, 256, 128, fake, fake, odd, None, s) == -2
+    assert qa(fake, 256, 4, 256, 128, fake, fake, None, odd, s) == -2
+    assert qa(None, 256, 0, 256, 128, None, None, None, None, s) == 0       # M = 0: no-op
 
     nbytes = L.mixllm_packed_bytes(64, 256, 128, 2)
     gm = lib.mixllm_gemm_w4w8a8
-    assert gm(fake, fake, fake, 4, 64, 200, 2, fake, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(fake, fake, fake, 4, 64, 256, 65, fake, nbytes, fake, 64, None, 0, s) == -4
-    assert gm(fake, fake, fake, -1, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(None, fake, fake, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -1
-    assert gm(fake, fake, None, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -1
-    assert gm(fake, fake, fake, 4, 64, 256, 2, None, nbytes, fake, 64, None, 0, s) == -1
-    assert gm(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, None, 64, None, 0, s) == -1
-    assert gm(fake, fake, fake, 4, 64, 256, 2, fake, nbytes - 1, fake, 64, None, 0, s) == -5
-    assert gm(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, fake, 63, None, 0, s) == -2
-    assert gm(odd, fake, fake, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(fake, fake, odd, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(fake, fake, fake, 4, 64, 256, 2, odd, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(None, None, None, 0, 64, 256, 2, None, 0, None, 64, None, 0, s) == 0  # M = 0
+    f4 = (fake, fake, fake, fake)
+    assert gm(*f4, 4, 64, 200, 2, fake, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(*f4, 4, 64, 256, 65, fake, nbytes, fake, 64, None, 0, s) == -4
+    assert gm(*f4, -1, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
+    for i in range(4):
+        args = list(f4)
+        args[i] = None
+        assert gm(*args, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -1
+        args[i] = odd
+        assert gm(*args, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(*f4, 4, 64, 256, 2, None, nbytes, fake, 64, None, 0, s) == -1
+    assert gm(*f4, 4, 64, 256, 2, fake, nbytes, None, 64, None, 0, s) == -1
+    assert gm(*f4, 4, 64, 256, 2, fake, nbytes - 1, fake, 64, None, 0, s) == -5
+    assert gm(*f4, 4, 64, 256, 2, fake, nbytes, fake, 63, None, 0, s) == -2
+    assert gm(*f4, 4, 64, 256, 2, odd, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(None, None, None, None, 0, 64, 256, 2, None, 0, None, 64, None, 0, s) == 0  # M = 0
+    # the tile kernel's 32-bit operand offsets: G * M * 32 must stay below 2^31
+    big = L.mixllm_packed_bytes(64, 1 << 17, 128, 2)
+    assert gm(*f4, 1 << 16, 64, 1 << 17, 2, fake, big, fake, 64, None, 0, s) == -2
+    assert L.mixllm_gemm_workspace_bytes(512, 4096, 4096, 410) == 0
     gp = lib.mixllm_gemm_w4w8a8_partials
-    assert gp(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, 60, 5, fake, s) == -2
-    assert gp(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, -1, 5, fake, s) == -2
-    assert gp(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, 0, 5, None, s) == -1
-    assert gp(fake, fake, fake, 4, 64, 256, 2, fake, nbytes, 0, 0, None, s) == 0
+    assert gp(*f4, 4, 64, 256, 2, fake, nbytes, 60, 5, fake, s) == -2
+    assert gp(*f4, 4, 64, 256, 2, fake, nbytes, -1, 5, fake, s) == -2
+    assert gp(*f4, 4, 64, 256, 2, fake, nbytes, 0, 5, None, s) == -1
+    assert gp(*f4, 4, 64, 256, 2, fake, nbytes, 0, 0, None, s) == 0

@@ -52,6 +52,7 @@ struct GemmArgs {
   const int8_t *aq;
   const float *sa;
   const int32_t *asum;
+  const uint32_t *rowop;  // [G][2][M][4] row operands of the scale products
   int M, N, K, G;
   const uint8_t *w4;
   const uint16_t *s4;
@@ -59,15 +60,13 @@ struct GemmArgs {
   const uint8_t *w8;
   const uint16_t *s8;
   const int32_t *idx;
+  const uint32_t *pw;
   int n4, nb, nb4;
   uint16_t *y;
   int64_t ldy;
   int32_t *part;  // partials mode output [M][n_count][G]
   int n_begin, n_count;
   int tiles_m, tiles_n;
-  int ks;       // split-K factor of the tile kernel
-  float *ws;    // split-K partial tiles [tiles][ks][64 * 128]
-  int *cnt;     // split-K arrival counters [tiles], zero between launches
 };
 
 __device__ __forceinline__ float h2f(uint16_t bits) { return (float)__builtin_bit_cast(_Float16, bits); }
@@ -119,314 +118,382 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 // ------------------------------------------------------------------------------------
-// Tile kernel: a workgroup of 4 waves owns 64 rows x 128 channels (4 blocks of 32); wave w
-// computes block 4 tn + w for all 64 rows, one wave per SIMD.
+// Tile kernel (M > 64).  A workgroup of 4 x KS waves owns 64 rows x 128 channels (4
+// blocks of 32 channels).  Wave (b, q) computes block 4 tn + b for all 64 rows over the
+// q-th of KS contiguous slices of the groups; the KS partial accumulators are summed
+// through LDS at the end in slice order.  Several waves per SIMD let one wave's
+// matrix-core work cover another's VALU work and memory waits.
 //
-// Per group and 32x32 output block a wave issues
-//   * 4 x v_mfma_i32_32x32x32_i8: the group partial.  4-bit blocks feed the raw codes q;
-//     the zero point is removed in the float domain (below), so decoding costs 3 VALU
-//     ops per 8 codes;
-//   * 1 x v_mfma_f32_32x32x16_bf16: the scale products s_a[m] s_w[n] of the whole block
-//     as an outer product of exact bf16 splits (s_a = a0 + a1 + a2, s_w = b0 + b1);
-//   * 4-bit blocks only: 1 x v_mfma_f32_32x32x16_bf16 that subtracts
-//     (S_A[m] s_a[m]) (z[n] s_w[n]) from the accumulator, S_A being the group's code sum:
-//     sum_k (q - z) a_k s_a s_w = s_a s_w sum_k q a_k - (S_A s_a) (z s_w);
+// Per group and wave (two 32-row blocks):
+//   * 4 x 2 v_mfma_i32_32x32x32_i8: the exact group partials.  4-bit blocks feed the raw
+//     codes q (3 VALU ops per 8 codes); the zero point is removed in the float domain;
+//   * per block, 1 v_mfma_f32_32x32x16_bf16 for the scale products s_a[m] s_w[n] as an
+//     outer product of exact bf16 splits: the row operand [a0 a0 a1 a1 a2 a2 0 0]
+//     (s_a = a0 + a1 + a2, written by the activation quantizer) against the column
+//     operand [b0 b1] x 4 (s_w = b0 + b1, from the packed weights);
+//   * 4-bit blocks: 1 more that adds -(S_A[m] s_a[m]) (z[n] s_w[n]) to the accumulator,
+//     S_A being the group's activation code sum: sum_k (q - z) a_k s_a s_w =
+//     s_a s_w sum_k q a_k - (S_A s_a) (z s_w);
 //   * the fold acc += float(P) * scale: 2 VALU ops per output element.
 // The integer partial is exact; only the fp32 fold differs from the fp64 definition.
+// Software pipeline: block 0 of a group runs on the matrix cores while block 1 of the
+// previous group folds, then block 1 while block 0 folds.
 //
-// Two workgroups per CU: each CU runs two independent workgroups (two waves per SIMD)
-// with their own barriers, so one wave's matrix-core phase overlaps the other's VALU
-// phase.  When the grid has too few tiles for that, the groups of a tile are split over
-// KS workgroups (contiguous ranges); each writes its fp32 partial tile to the workspace
-// and the last one to arrive sums the KS partials in split order (deterministic) and
-// writes the output.
-//
-// Latency hiding: every thread keeps a ring of S groups of its loads in registers (its
-// share of the activation tile and of the scale/code-sum rows, its wave's weights and
-// scales), requesting group g + S - 1 while group g is computed.  The compiler's
-// per-register wait counters order each use after its load; the ring is refilled
-// unconditionally and whole ring turns carry no guards, so those waits stay exact.
+// Streams.  The activation tile of a group (64 rows x 128 B) and the rows' scale
+// operands (2 x 64 x 16 B) go from memory straight into LDS (buffer_load ... lds)
+// kD = kSA - 2 groups ahead of their use, in a ring of kSA stages (a stage is read during
+// its step and the next); a wave's weights and scale words stream into a register ring
+// SW groups deep.  Every wave issues the same fixed set of loads per step, so a wait for
+// "at most N loads outstanding" (N counting the later steps' loads) proves that the
+// current step's stage has landed; a workgroup barrier after that wait publishes it.  The
+// wait is explicit because the compiler does not track LDS written by these loads.
 // ------------------------------------------------------------------------------------
 constexpr int kTileBM = 64;
-constexpr int kTileThreads = 256;
+constexpr int kTileNB = 4;                          // channel blocks per workgroup
+#ifndef MIXLLM_TILE_KS
+#define MIXLLM_TILE_KS 2
+#endif
+constexpr int kKS = MIXLLM_TILE_KS;                 // group slices per workgroup
+constexpr int kTileWaves = kTileNB * kKS;
+constexpr int kTileThreads = 64 * kTileWaves;
+#ifndef MIXLLM_TILE_SA
+#define MIXLLM_TILE_SA 6
+#endif
+constexpr int kSA = MIXLLM_TILE_SA;                 // LDS stages
+constexpr int kD = kSA - 2;                         // prefetch distance (groups)
+#ifndef MIXLLM_SW4
+#define MIXLLM_SW4 2
+#endif
+constexpr int kSW4 = MIXLLM_SW4, kSW8 = 2;          // weight ring depth, 4-bit / 8-bit blocks
 
-// LDS bank swizzles.  A ds_read_b128 wave is served in groups of 16 lanes over 64 banks;
-// the rows one group reads must hit distinct banks.  Activation tile: 16-byte chunk c of
-// row r sits at chunk position c ^ swz_a(r) of the row's 128 bytes.  Piece rows (32
-// bytes): the two 16-byte halves are swapped when swz_p(r) is 1.
+// LDS bank swizzle of the activation tile: a ds_read_b128 wave is served in groups of
+// 16 lanes over 64 banks, and the rows one group reads must hit distinct banks; the
+// 16-byte chunk c of row r sits at position c ^ swz_a(r) of the row's 128 bytes.
 __device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz_p(int r) { return (r >> 3) & 1; }
 
-// The activation tile of group g lives in buffer g % 2 and is read only in step g.  The
-// scale pieces of group g live in buffer g % 3: they are read in step g + 1 too (the
-// delayed fold), and a wave may write step g + 2's pieces before a slower wave has left
-// step g + 1, so two buffers would race.
 struct TileSmem {
-  uint8_t a[2][kTileBM * 128];   // [buffer] activation tile, swizzled 16 B chunks
-  uint32_t pa[3][kTileBM][8];    // [buffer][row] bf16 pieces of s_a (one 16 B half) + zeros
-  uint32_t pu[3][kTileBM][8];    // same for S_A * s_a
-  int last;                      // split-K: this workgroup arrived last at its tile
+  uint8_t a[kSA][kKS][kTileBM * 128];           // [stage][slice] activation tiles
+  uint32_t rp[kSA][kKS][4][64][4];              // [stage][slice][row / 16][lane] row operands:
+                                                // lane < 16: s_a of row 16 b + lane; 16..31: S_A s_a; rest unused
 };
-
-__device__ __forceinline__ uint32_t pack_bf16(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
-
-// x = p0 + p1 + p2 exactly, each a bf16 (returned as 16-bit patterns): truncate to
-// bf16, the remainder keeps at most 16 significant bits, truncate again, the second
-// remainder has at most 8 and is itself a bf16.
-__device__ __forceinline__ void split3_bf16(float x, uint32_t &p0, uint32_t &p1, uint32_t &p2) {
-  const uint32_t b0 = __float_as_uint(x) & 0xFFFF0000u;
-  const float r1 = x - __uint_as_float(b0);
-  const uint32_t b1 = __float_as_uint(r1) & 0xFFFF0000u;
-  const float r2 = r1 - __uint_as_float(b1);
-  p0 = b0 >> 16;
-  p1 = b1 >> 16;
-  p2 = __float_as_uint(r2) >> 16;
-}
-
-// x = p0 + p1 exactly for x with at most 16 significant bits (fp16 scales, z * s_w).
-__device__ __forceinline__ void split2_bf16(float x, uint32_t &p0, uint32_t &p1) {
-  const uint32_t b0 = __float_as_uint(x) & 0xFFFF0000u;
-  p0 = b0 >> 16;
-  p1 = __float_as_uint(x - __uint_as_float(b0)) >> 16;
-}
+static_assert((kKS - 1) * kTileNB * kTileBM * 32 * 4 <= (int)sizeof(TileSmem::a), "reduction space");
 
 __device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
                                                  0, 0);
 }
 
-// Column operand of the piece products: lanes of the first half-wave carry
-// [b0, b1, b0, b1, b0, b1, 0, 0], the second half-wave zeros (its k slots are unused).
-__device__ __forceinline__ v4i col_pieces(float x, int h, bool negate) {
-  uint32_t b0, b1;
-  split2_bf16(x, b0, b1);
-  uint32_t w = pack_bf16(b0, b1) ^ (negate ? 0x80008000u : 0u);
-  w = h ? 0u : w;
-  return v4i{(int)w, (int)w, (int)w, 0};
-}
-
 enum BlockKind { kNone = 0, kW4 = 1, kW8 = 2 };
 
-template <int S, int KIND, bool PARTIALS>
-__device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int t, int ksplit, int m0, int blk,
-                                          int wave, int lane) {
-  constexpr int RB = kTileBM / 32;
-  constexpr bool H4 = KIND == kW4;
-  constexpr bool H8 = KIND == kW8;
-  const int tid = wave * 64 + lane;
+// Buffer resources: the 128-bit descriptor of a byte range [base, base + bytes).  Loads
+// through it take a per-lane 32-bit offset (computed once) plus a wave-uniform offset
+// (per group, scalar arithmetic), so the inner loop spends no vector ops on addresses,
+// and loads past `bytes` return zeros instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcFlags = 0x00020000;  // gfx9 raw buffer, 32-bit data format
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)n, kRsrcFlags);
+}
+__device__ __forceinline__ v4i bload16(Rsrc r, int voff, int soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload4(Rsrc r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+typedef __attribute__((address_space(3))) void *LdsPtr;
+// 16 bytes per lane from the buffer into LDS at dst + 16 * lane (dst wave-uniform).
+__device__ __forceinline__ void bload16_lds(Rsrc r, void *dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)dst, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count: wait until at most N vector-memory
+// operations of this wave are outstanding (gfx9 encoding: vmcnt low bits [3:0], high
+// bits [15:14]; expcnt 7 and lgkmcnt 15 mean "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait until at most N vector-memory operations are outstanding, N = min(s, CAP) * L.
+template <int L, int CAP>
+__device__ __forceinline__ void wait_vm_steps(int s) {
+  static_assert(CAP <= 3, "extend the cases below");
+  if (CAP >= 3 && s >= 3) {
+    wait_vm<(CAP >= 3 ? 3 : 0) * L>();
+  } else if (CAP >= 2 && s >= 2) {
+    wait_vm<(CAP >= 2 ? 2 : 0) * L>();
+  } else if (CAP >= 1 && s >= 1) {
+    wait_vm<L>();
+  } else {
+    wait_vm<0>();
+  }
+}
+
+// Workgroup barrier for LDS data: this wave's LDS reads and writes complete, then the
+// barrier.  The scheduler barriers keep the compiler from moving memory operations
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int KIND, bool PARTIALS>
+__device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m0, int blk, int bi, int q,
+                                          int lane) {
+  constexpr int SW = KIND == kW8 ? kSW8 : kSW4;
+  constexpr int NW = KIND == kW8 ? 4 : (KIND == kW4 ? 2 : 0);     // 16-byte weight loads per step
+  constexpr int NPW = KIND == kW4 ? 2 : (KIND == kW8 ? 1 : 0);    // scale words per step
+  constexpr int NZ = (PARTIALS && KIND == kW4) ? 1 : 0;           // zero-point word (partials)
+  constexpr int L = 3 + NW + NPW + NZ;                            // loads per step
+  static_assert(kD >= 2 && (kD - 1) * L < 64, "prefetch distance");
   const int ch32 = lane & 31, h = lane >> 5, half = ch32 >> 4, ch = ch32 & 15;
   const int G = p.G;
-  const int gb = (int)((int64_t)G * ksplit / p.ks), ge = (int)((int64_t)G * (ksplit + 1) / p.ks);
+  const int gb = G * q / kKS, ge = G * (q + 1) / kKS;             // this slice's groups
+  const int nsteps = (G + kKS - 1) / kKS;                          // same for every wave
+  const int glast = max(ge - 1, gb);
+  auto grp = [&](int s) { return min(gb + s, glast); };            // clamped: always a valid group
 
-  // Ring slots hold raw loaded bits only: converting a value right after its load would
-  // make the wait for it a wait for every load issued before it.
-  v4i aR[S][RB];
-  float saR[S];
-  int32_t asR[S];
-  v4i b4R[S][2];
-  uint32_t z8R[S];
-  uint32_t s4R[S];
-  v4i b8R[S][4];
-  uint32_t s8R[S];
+  // Descriptors.  Activation rows past M load zeros; operand rows past M read other
+  // rows (finite, never stored) or zeros past the end.
+  const Rsrc ra = make_rsrc(p.aq + (int64_t)m0 * p.K, (int64_t)(p.M - m0) * p.K);
+  const Rsrc rro = make_rsrc(p.rowop, (int64_t)G * 2 * p.M * 16);
+  const int bq = KIND == kW8 ? blk - p.nb4 : blk;
+  const Rsrc rw = KIND == kW8 ? make_rsrc(p.w8 + (size_t)bq * G * kW8Chunk, (int64_t)G * kW8Chunk)
+                              : make_rsrc(p.w4 + (size_t)bq * G * kW4Chunk, (int64_t)G * kW4Chunk);
+  const Rsrc rpw = make_rsrc((const uint8_t *)p.pw + (size_t)blk * G * kPwChunk, (int64_t)G * kPwChunk);
 
-  const int prow = min(m0 + lane, p.M - 1);  // row whose scales this lane loads
-  auto issue = [&](auto slot_c, int g) {
-    constexpr int j = decltype(slot_c)::value;
+  // Per-lane offsets.
+  int vdma[2];  // this wave loads rows [16 bi, 16 bi + 16) of the slice's tile, 8 rows per load
 #pragma unroll
-    for (int q = 0; q < RB; ++q) {
-      const int u = tid + 256 * q, r = u >> 3, c = u & 7;
-      const int row = min(m0 + r, p.M - 1);  // rows past M load a valid row; never stored
-      aR[j][q] = ldg16(p.aq + (int64_t)row * p.K + g * 128 + c * 16);
-    }
-    saR[j] = p.sa[(int64_t)g * p.M + prow];
-    asR[j] = p.asum[(int64_t)g * p.M + prow];
-    if (H4) {
-      const size_t cidx = (size_t)blk * G + g;
-      const uint8_t *chunk = p.w4 + cidx * kW4Chunk + half * 1024;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) b4R[j][q] = ldg16(chunk + ((2 * q + h) * 16 + ch) * 16);
-      // whole words only: the word holding this channel's scale, the one holding its zero
-      s4R[j] = reinterpret_cast<const uint32_t *>(p.s4)[cidx * 16 + (ch32 >> 1)];
-      z8R[j] = reinterpret_cast<const uint32_t *>(p.z4)[cidx * 4 + (ch32 >> 3)];
-    }
-    if (H8) {
-      const size_t cidx = (size_t)(blk - p.nb4) * G + g;
-      const uint8_t *chunk = p.w8 + cidx * kW8Chunk + half * 2048;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) b8R[j][s] = ldg16(chunk + (chunk32(s, h) * 16 + ch) * 16);
-      s8R[j] = reinterpret_cast<const uint32_t *>(p.s8)[cidx * 16 + (ch32 >> 1)];
-    }
-  };
-
-  // The activation tile and the row pieces of group slot j into LDS buffer `buf`.  The
-  // pieces of all 64 rows (lane = row) are computed by wave g % 4, so the work rotates.
-  auto store_a = [&](auto slot_c, int buf, int pbuf, int g) {
-    constexpr int j = decltype(slot_c)::value;
-#pragma unroll
-    for (int q = 0; q < RB; ++q) {
-      const int u = tid + 256 * q, r = u >> 3, c = u & 7;
-      *reinterpret_cast<v4i *>(&sm.a[buf][r * 128 + ((c ^ swz_a(r)) << 4)]) = aR[j][q];
-    }
-    if (wave == (g & 3)) {
-      uint32_t a0, a1, a2, u0, u1, u2;
-      split3_bf16(saR[j], a0, a1, a2);
-      split3_bf16((float)asR[j] * saR[j], u0, u1, u2);
-      const int sw = swz_p(lane) * 4;
-      *reinterpret_cast<v4i *>(&sm.pa[pbuf][lane][sw]) =
-          v4i{(int)pack_bf16(a0, a0), (int)pack_bf16(a1, a1), (int)pack_bf16(a2, a2), 0};
-      *reinterpret_cast<v4i *>(&sm.pu[pbuf][lane][sw]) =
-          v4i{(int)pack_bf16(u0, u0), (int)pack_bf16(u1, u1), (int)pack_bf16(u2, u2), 0};
-    }
-  };
-
-  const int jp = blk * 32 + ch32;
-  auto a_operand = [&](int buf, int rb, int chunk) {
-    const int r = rb * 32 + ch32;
-    return *reinterpret_cast<const v4i *>(&sm.a[buf][r * 128 + ((chunk ^ swz_a(r)) << 4)]);
-  };
-  auto row_pieces = [&](uint32_t (*arr)[kTileBM][8], int buf, int rb) {
-    const int r = rb * 32 + ch32;
-    return *reinterpret_cast<const v4i *>(&arr[buf][r][(h * 4) ^ (swz_p(r) * 4)]);
-  };
-
-  v16f acc[RB];
-  v16i Pprev[RB];  // int32 partials of the previous group, folded during this step
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    acc[rb] = v16f{0};
-    Pprev[rb] = v16i{0};
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * bi + 8 * i + (lane >> 3), pos = lane & 7;
+    vdma[i] = r * p.K + ((pos ^ swz_a(r)) << 4);
   }
-  uint32_t swprev = 0, zprev = 0;  // that group's scale word and zero-point word
-  int pbufprev = 0;                // and the LDS buffer of its scale pieces
+  // ... and the operands of the same 16 rows: lanes 0-15 s_a, lanes 16-31 S_A s_a (lanes
+  // 32-63 repeat them into the unused half of the wave's operand area)
+  const int vro = (((lane >> 4) & 1) * p.M + m0 + 16 * bi + (lane & 15)) * 16;
+  const int vpw = ch32 * 8;
+  int vw[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    vw[s] = KIND == kW8 ? ((half * 8 + chunk32(s, h)) * 16 + ch) * 16 : ((half * 4 + 2 * (s & 1) + h) * 16 + ch) * 16;
+  int va[4];  // LDS byte offset of this lane's A operand for k-step s, 32-row block 0
+#pragma unroll
+  for (int s = 0; s < 4; ++s) va[s] = ch32 * 128 + ((chunk32(s, h) ^ swz_a(ch32)) << 4);
+  // (row + 32 has the same swizzle as row, so block 1 is block 0 + 32 * 128.)
+  // byte offset of row ch32's s_a operand within a [stage][slice] operand area (S_A s_a at
+  // + 256 bytes, block 1 at + 2 * 1024 bytes)
+  const int vrp = ((ch32 >> 4) * 64 + (ch32 & 15)) * 16;
+  constexpr int kAStage = kKS * kTileBM * 128, kRStage = kKS * 4 * 64 * 16;  // bytes per stage
+  uint8_t *const abase = &sm.a[0][q][0];
+  uint8_t *const rbase = reinterpret_cast<uint8_t *>(&sm.rp[0][q][0][0][0]);
 
-  // Fold the previous group: its scale products come from the bf16 MFMA on the pieces
-  // still held in its LDS buffer (written two steps apart) and its scale/zero words.
-  auto fold_prev = [&]() {
-    const float sw = h2f((uint16_t)(swprev >> ((ch32 & 1) * 16)));
-    const uint32_t z = H4 ? ((zprev >> ((ch32 & 7) * 4)) & 15u) : 0u;
-    const v4i bp = col_pieces(sw, h, false);
-    const v4i bu = col_pieces((float)z * sw, h, true);
+  // Register ring (raw loaded bits only), two steps deep: slot = step parity.
+  static_assert(SW == 2, "the step loop is unrolled by two");
+  v4i bR[2][NW > 0 ? NW : 1];
+  uint32_t swR[2], zwR[2];
+  uint32_t zpR[2];
+
+  // Stage st: the activation tile and the row operands of group g, straight into LDS.
+  auto issue_a = [&](int st, int g) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const v16f sc = mfma_bf16(row_pieces(sm.pa, pbufprev, rb), bp, v16f{0});
+    for (int i = 0; i < 2; ++i) bload16_lds(ra, abase + st * kAStage + (16 * bi + 8 * i) * 128, vdma[i], g * 128);
+    bload16_lds(rro, rbase + st * kRStage + bi * 1024, vro, g * 2 * p.M * 16);
+  };
+  // Ring slot j: this wave's weights and scale words of group g.
+  auto issue_w = [&](auto j_c, int g) {
+    constexpr int j = decltype(j_c)::value;
+    if constexpr (KIND != kNone) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rb][r] = fmaf((float)Pprev[rb][r], sc[r], acc[rb][r]);
-      if (H4) acc[rb] = mfma_bf16(row_pieces(sm.pu, pbufprev, rb), bu, acc[rb]);
+      for (int s = 0; s < NW; ++s) bR[j][s] = bload16(rw, vw[s], g * (KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk));
+      swR[j] = bload4(rpw, vpw, g * (int)kPwChunk);
+      if constexpr (KIND == kW4) zwR[j] = bload4(rpw, vpw + 4, g * (int)kPwChunk);
+      if constexpr (NZ) zpR[j] = bload4(make_rsrc(p.z4, (int64_t)p.nb4 * G * kZ4Chunk), (ch32 >> 3) * 4,
+                                        (int)(((size_t)blk * G + g) * kZ4Chunk));
     }
   };
 
-  // Group g on the matrix core; returns its partials.  In the partials mode the
-  // partials are written out instead.
-  auto mma = [&](auto slot_c, int buf, int g, v16i (&Pi)[RB]) {
-    constexpr int j = decltype(slot_c)::value;
-    v4i bq[4];
-    if (H4) {
+  v16f acc[2] = {v16f{0}, v16f{0}};
+  v16i P1[2] = {v16i{0}, v16i{0}};  // block-1 partials of the even / odd steps
+  uint32_t swprev = 0, zwprev = 0;  // column words of the previous step (0: nothing to fold)
+  const int jp = blk * 32 + ch32;
+
+  // The row operands (s_a and S_A s_a pieces) of one 32-row block of stage st.
+  auto load_rows = [&](int rb, int st, v4i &rs, v4i &ru) {
+    const uint8_t *o = rbase + st * kRStage + vrp + rb * 2048;
+    rs = *reinterpret_cast<const v4i *>(o);
+    if constexpr (KIND == kW4) ru = *reinterpret_cast<const v4i *>(o + 256);
+  };
+  // Scale products of one 32-row block on the matrix cores (row operand rs, column word
+  // sw).  The column words are zero in the second half-wave (its k slots must add
+  // nothing) and for a step that folds nothing.
+  auto scales = [&](const v4i &rs, uint32_t sw) {
+    return mfma_bf16(rs, v4i{(int)sw, (int)sw, (int)sw, (int)sw}, v16f{0});
+  };
+  // acc[rb] += float(P) * scale, then (4-bit blocks) the zero-point term.
+  auto fold = [&](int rb, const v16i &Pp, const v16f &sc, const v4i &ru, uint32_t zw) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t x0 = (uint32_t)b4R[j][q][2 * e], x1 = (uint32_t)b4R[j][q][2 * e + 1];
-          bq[2 * q + e] = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
-                              (int)((x1 >> 4) & 0x0F0F0F0Fu)};
-        }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) bq[s] = b8R[j][s];
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) Pi[rb] = v16i{0};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        Pi[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_operand(buf, rb, chunk32(s, h)), bq[s], Pi[rb], 0, 0, 0);
-    if (PARTIALS) {
-      const uint32_t z = H4 ? ((z8R[j] >> ((ch32 & 7) * 4)) & 15u) : 0u;
-      const int orig = p.idx[jp];
-      if (orig >= p.n_begin && orig < p.n_begin + p.n_count) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (row < p.M) {
-              const int corr = H4 ? (int)z * p.asum[(int64_t)g * p.M + row] : 0;
-              p.part[((int64_t)row * p.n_count + (orig - p.n_begin)) * G + g] = Pi[rb][r] - corr;
-            }
-          }
-      }
-    }
+    for (int r = 0; r < 16; ++r) acc[rb][r] = fmaf((float)Pp[r], sc[r], acc[rb][r]);
+    if constexpr (KIND == kW4) acc[rb] = mfma_bf16(ru, v4i{(int)zw, (int)zw, (int)zw, (int)zw}, acc[rb]);
   };
 
-  // One step: group g's activation tile into LDS, barrier, refill the ring, then the
-  // matrix-core work of group g interleaved with the VALU fold of group g - 1.
-  auto step = [&](auto jc, int g) {
-    constexpr int j = decltype(jc)::value;
-    const int buf = g & 1;
-    const int pbuf = g % 3;
-    store_a(jc, buf, pbuf, g);
-    __syncthreads();
-    // the words of group g leave the ring slot that the refill below reuses later
-    const uint32_t swcur = H4 ? s4R[j] : s8R[j];
-    const uint32_t zcur = H4 ? z8R[j] : 0u;
-    // Always refill the ring (past the range end, reload the last group): a branch here
-    // would merge two load histories and make the compiler's waits conservative.
-    issue(IntC<(j + S - 1) % S>{}, min(g + S - 1, ge - 1));
-    if (KIND != kNone) {
-      v16i Pi[RB];
-      mma(jc, buf, g, Pi);
-      if (!PARTIALS) fold_prev();
+  // The A operands of both 32-row blocks of stage st (8 LDS reads, issued together).
+  auto load_a = [&](int st, v4i (&av)[2][4]) {
+    const uint8_t *at = abase + st * kAStage;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) Pprev[rb] = Pi[rb];
-    }
-    swprev = swcur;
-    zprev = zcur;
-    pbufprev = pbuf;
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) av[rb][k] = *reinterpret_cast<const v4i *>(at + va[k] + rb * 32 * 128);
+  };
+  // The group partial of one 32-row block on the matrix cores.
+  auto block_mma = [&](const v4i (&av)[4], const v4i (&bq)[4]) {
+    v16i P = v16i{0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) P = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[k], bq[k], P, 0, 0, 0);
+    return P;
   };
 
-  static_for<0, S - 1>([&](auto jc) { issue(jc, min(gb + (int)decltype(jc)::value, ge - 1)); });
-  int g0 = gb;
-  for (; g0 + S <= ge; g0 += S) static_for<0, S>([&](auto jc) { step(jc, g0 + decltype(jc)::value); });
-  static_for<0, S>([&](auto jc) {
-    if (g0 + (int)decltype(jc)::value < ge) step(jc, g0 + decltype(jc)::value);
-  });
-  if (!PARTIALS && KIND != kNone) fold_prev();  // the last group's fold
-  if (PARTIALS) return;
-
-  if (p.ks > 1) {
-    // Split-K: publish this split's partial tile; the last workgroup of the tile to
-    // arrive sums all splits in split order and writes the output.
-    float *slots = p.ws + (size_t)t * p.ks * (kTileBM * 128);
-    float *mine = slots + (size_t)ksplit * (kTileBM * 128);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mine[((wave * RB + rb) * 16 + r) * 64 + lane] = acc[rb][r];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) sm.last = atomicAdd(&p.cnt[t], 1) == p.ks - 1;
-    __syncthreads();
-    if (!sm.last) return;
-    __threadfence();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+  // Partials mode: the exact group partials of an active step, zero point removed.
+  auto emit = [&](int rb, const v16i &Pc, int g, uint32_t zword) {
+    const int orig = p.idx[jp];
+    const uint32_t z = KIND == kW4 ? ((zword >> ((ch32 & 7) * 4)) & 15u) : 0u;
+    if (orig >= p.n_begin && orig < p.n_begin + p.n_count) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v = 0.0f;
-        for (int k = 0; k < p.ks; ++k) {
-          const float o = __builtin_nontemporal_load(&slots[(size_t)k * (kTileBM * 128) +
-                                                            ((wave * RB + rb) * 16 + r) * 64 + lane]);
-          v += k == ksplit ? acc[rb][r] : o;
+        const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < p.M) {
+          const int corr = KIND == kW4 ? (int)z * p.asum[(int64_t)g * p.M + row] : 0;
+          p.part[((int64_t)row * p.n_count + (orig - p.n_begin)) * G + g] = Pc[r] - corr;
         }
-        acc[rb][r] = v;
       }
-    if (tid == 0) p.cnt[t] = 0;  // leave the counter zero for the next launch
+    }
+  };
+
+  // One step s (parity j = s % 2 known at compile time; stage st = s mod kSA).  The
+  // prologue waited for stages 0 .. kD - 1; stage s >= kD was issued at step s - kD, and
+  // the kD - 1 later steps issued L loads each, so "at most (kD - 1) L outstanding" means
+  // stage s has landed.
+  auto step = [&](auto j_c, int s, int st) {
+    constexpr int j = decltype(j_c)::value;
+    wait_vm<(kD - 1) * L>();
+    lds_barrier();
+    // the column words of step s leave the ring slot that the refill below reuses
+    const uint32_t swcur = KIND != kNone ? swR[j] : 0u;
+    const uint32_t zwcur = KIND == kW4 ? zwR[j] : 0u;
+    // Refill (unconditionally, clamped, so every step issues the same loads): stage
+    // s + kD (the slot of step s - 2, read for the last time during step s - 1), and the
+    // weights of step s + 1 (the slot of step s - 1).
+    const int st_next = st + kD >= kSA ? st + kD - kSA : st + kD;
+    issue_a(st_next, grp(s + kD));
+    issue_w(IntC<1 - j>{}, grp(s + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KIND != kNone) {
+      // Branch-free: an inactive step (past this slice's range, on clamped data) computes
+      // partials that are never folded (its column words are replaced by zeros).
+      const bool act = gb + s < ge;
+      const uint32_t sw = (act && h == 0) ? swcur : 0u, zw = (act && h == 0) ? zwcur : 0u;
+      // LDS operand reads first, fenced off, so their latency overlaps the decode and the
+      // first matrix-core ops instead of preceding each op.
+      v4i av[2][4];
+      load_a(st, av);
+      const int st_prev = st == 0 ? kSA - 1 : st - 1;
+      v4i rs1, ru1, rs0, ru0;
+      if constexpr (!PARTIALS) {
+        load_rows(1, st_prev, rs1, ru1);
+        load_rows(0, st, rs0, ru0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      v4i bq[4];
+      if constexpr (KIND == kW4) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint32_t x0 = (uint32_t)bR[j][e][2 * u], x1 = (uint32_t)bR[j][e][2 * u + 1];
+            bq[2 * e + u] = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
+                                (int)((x1 >> 4) & 0x0F0F0F0Fu)};
+          }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) bq[k] = bR[j][k];
+      }
+      if constexpr (PARTIALS) {
+        const v16i P0 = block_mma(av[0], bq);
+        if (act) emit(0, P0, gb + s, zpR[j]);
+        const v16i Pb = block_mma(av[1], bq);
+        if (act) emit(1, Pb, gb + s, zpR[j]);
+      } else {
+        // Block 0 of this step on the matrix cores while block 1 of the previous step
+        // folds, then block 1 of this step while block 0 of this step folds.
+        const v16f sc1 = scales(rs1, swprev);
+        const v16i P0 = block_mma(av[0], bq);
+        fold(1, P1[1 - j], sc1, ru1, zwprev);
+        const v16f sc0 = scales(rs0, sw);
+        P1[j] = block_mma(av[1], bq);
+        fold(0, P0, sc0, ru0, zw);
+      }
+      swprev = sw;
+      zwprev = zw;
+    }
+  };
+
+  // Prologue: stages 0 .. kD - 1 and the weights of step 0, all landed before step 0.
+  for (int st = 0; st < kD; ++st) issue_a(st, grp(st));
+  issue_w(IntC<0>{}, grp(0));
+  wait_vm<0>();
+
+  int s = 0, st = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    step(IntC<0>{}, s, st);
+    st = st + 1 == kSA ? 0 : st + 1;
+    step(IntC<1>{}, s + 1, st);
+    st = st + 1 == kSA ? 0 : st + 1;
   }
-  if (KIND == kNone) return;
+  if (s < nsteps) {
+    step(IntC<0>{}, s, st);
+    ++s;
+  }
+  // Block 1 of the last step still has to fold; its stage is intact (the last refill went
+  // to the slot of step nsteps - 2).
+  if constexpr (!PARTIALS && KIND != kNone) {
+    v4i rs, ru;
+    load_rows(1, (nsteps - 1) % kSA, rs, ru);
+    const v16f sc = scales(rs, swprev);
+    if ((nsteps - 1) & 1)
+      fold(1, P1[1], sc, ru, zwprev);
+    else
+      fold(1, P1[0], sc, ru, zwprev);
+  }
+  // All direct-to-LDS loads (including the clamped refills) have landed before the
+  // stages' space is reused.
+  wait_vm<0>();
+  lds_barrier();
+  if constexpr (PARTIALS) return;
+
+  // Sum the slices' accumulators in slice order and write the output.
+  float *red = reinterpret_cast<float *>(&sm.a[0][0][0]);
+  if (q > 0) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((((q - 1) * kTileNB + bi) * 2 + rb) * 16 + r) * 64 + lane] = acc[rb][r];
+  }
+  lds_barrier();
+  if (q > 0 || KIND == kNone) return;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int qq = 1; qq < kKS; ++qq) acc[rb][r] += red[((((qq - 1) * kTileNB + bi) * 2 + rb) * 16 + r) * 64 + lane];
   const int orig = p.idx[jp];
   if (orig < 0) return;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -434,45 +501,37 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int t
     }
 }
 
-// Register-ring depth (groups of loads in flight) per block kind.
-#ifndef MIXLLM_RING_W4
-#define MIXLLM_RING_W4 3
-#endif
-#ifndef MIXLLM_RING_W8
-#define MIXLLM_RING_W8 2
-#endif
-constexpr int kRingW4 = MIXLLM_RING_W4;
-constexpr int kRingW8 = MIXLLM_RING_W8;
-
 template <bool PARTIALS>
-__global__ __launch_bounds__(kTileThreads, 2) void gemm_tile_kernel(const GemmArgs p) {
+__global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs p) {
   __shared__ __attribute__((aligned(16))) TileSmem sm;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave: uniform
+  const int bi = wave & 3, q = wave >> 2;
 
-  // Zero the piece arrays once: only one 16-byte half of each row is rewritten per group.
-  for (int e = tid; e < (int)(sizeof(sm.pa) / 16); e += kTileThreads) {
-    reinterpret_cast<v4i *>(&sm.pa[0][0][0])[e] = v4i{0, 0, 0, 0};
-    reinterpret_cast<v4i *>(&sm.pu[0][0][0])[e] = v4i{0, 0, 0, 0};
-  }
-  __syncthreads();  // before any wave writes its first pieces
+  // Zero the operand stages: a fold before the first group reads a stage not loaded yet
+  // (with zero column words, which must meet finite values).
+  for (int e = tid; e < (int)(sizeof(sm.rp) / 16); e += kTileThreads)
+    reinterpret_cast<v4i *>(&sm.rp[0][0][0][0][0])[e] = v4i{0, 0, 0, 0};
+  __syncthreads();
 
-  // Workgroup w runs on XCD w % 8.  Give each XCD a contiguous range of tasks (tile,
-  // split) with the split fastest and then the M tile, so the splits of a tile share an
-  // XCD's L2 and its workgroups share weight blocks and activation tiles there.
-  const int T = p.tiles_m * p.tiles_n * p.ks;
+  // Workgroup w runs on XCD w % 8.  Give each XCD a contiguous range of tiles, ordered in
+  // bands of kBandM M tiles (M tile fastest within a band), so the workgroups an XCD runs
+  // at once share both activation rows and weight blocks in its L2.
+  constexpr int kBandM = 4;
+  const int T = p.tiles_m * p.tiles_n;
   const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
   const int per = T >> 3, rem = T & 7;
-  const int task = xcd * per + (xcd < rem ? xcd : rem) + i;
-  const int ksplit = task % p.ks, t = task / p.ks;
-  const int tm = t % p.tiles_m, tn = t / p.tiles_m;
+  const int t = xcd * per + (xcd < rem ? xcd : rem) + i;
+  const int band = t / (kBandM * p.tiles_n), in_band = t - band * (kBandM * p.tiles_n);
+  const int bm = min(kBandM, p.tiles_m - band * kBandM);  // M tiles in this band
+  const int tm = band * kBandM + in_band % bm, tn = in_band / bm;
   const int m0 = tm * kTileBM;
-  const int blk = tn * 4 + wave;
+  const int blk = tn * kTileNB + bi;
   const int kind = blk >= p.nb ? kNone : (blk < p.nb4 ? kW4 : kW8);
   switch (kind) {
-    case kW4: tile_body<kRingW4, kW4, PARTIALS>(p, sm, t, ksplit, m0, blk, wave, lane); break;
-    case kW8: tile_body<kRingW8, kW8, PARTIALS>(p, sm, t, ksplit, m0, blk, wave, lane); break;
-    default: tile_body<kRingW4, kNone, PARTIALS>(p, sm, t, ksplit, m0, blk, wave, lane); break;
+    case kW4: tile_body<kW4, PARTIALS>(p, sm, m0, blk, bi, q, lane); break;
+    case kW8: tile_body<kW8, PARTIALS>(p, sm, m0, blk, bi, q, lane); break;
+    default: tile_body<kNone, PARTIALS>(p, sm, m0, blk, bi, q, lane); break;
   }
 }
 
@@ -575,24 +634,26 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(const GemmArgs p, int
 // Host side
 // ------------------------------------------------------------------------------------
 
-int check_common(const int8_t *aq, const float *sa, const int32_t *asum, int32_t M, int32_t N, int32_t K,
-                 int32_t n8, const void *blob, size_t blob_bytes, mixllm_blob_info *L) {
+int check_common(const int8_t *aq, const float *sa, const int32_t *asum, const uint32_t *rowop, int32_t M,
+                 int32_t N, int32_t K, int32_t n8, const void *blob, size_t blob_bytes, mixllm_blob_info *L) {
   if (M < 0 || N <= 0 || K <= 0 || K % kGroup != 0) return MIXLLM_E_SHAPE;
   if (n8 < 0 || n8 > N) return MIXLLM_E_INDEX;
   if (!compute_layout(N, K, n8, L)) return MIXLLM_E_SHAPE;
   if (M == 0) return MIXLLM_OK;
-  if (!aq || !sa || !asum || !blob) return MIXLLM_E_NULL;
-  if (!is_aligned16(aq) || !is_aligned16(sa) || !is_aligned16(asum) || !is_aligned16(blob)) return MIXLLM_E_SHAPE;
+  if (!aq || !sa || !asum || !rowop || !blob) return MIXLLM_E_NULL;
+  if (!is_aligned16(aq) || !is_aligned16(sa) || !is_aligned16(asum) || !is_aligned16(rowop) || !is_aligned16(blob))
+    return MIXLLM_E_SHAPE;
   if (blob_bytes < L->total_bytes) return MIXLLM_E_SPACE;
   return MIXLLM_OK;
 }
 
-void fill_args(GemmArgs &a, const int8_t *aq, const float *sa, const int32_t *asum, int32_t M,
-               const void *blob, const mixllm_blob_info &L) {
+void fill_args(GemmArgs &a, const int8_t *aq, const float *sa, const int32_t *asum, const uint32_t *rowop,
+               int32_t M, const void *blob, const mixllm_blob_info &L) {
   const uint8_t *base = (const uint8_t *)blob;
   a.aq = aq;
   a.sa = sa;
   a.asum = asum;
+  a.rowop = rowop;
   a.M = M;
   a.N = L.N;
   a.K = L.K;
@@ -603,6 +664,7 @@ void fill_args(GemmArgs &a, const int8_t *aq, const float *sa, const int32_t *as
   a.w8 = base + L.off_w8;
   a.s8 = (const uint16_t *)(base + L.off_s8);
   a.idx = (const int32_t *)(base + L.off_idx);
+  a.pw = (const uint32_t *)(base + L.off_pw);
   a.n4 = L.n4;
   a.nb = L.nb;
   a.nb4 = L.nb4;
@@ -612,27 +674,17 @@ void fill_args(GemmArgs &a, const int8_t *aq, const float *sa, const int32_t *as
   a.n_begin = 0;
   a.n_count = 0;
   a.tiles_m = a.tiles_n = 0;
-  a.ks = 1;
-  a.ws = nullptr;
-  a.cnt = nullptr;
 }
 
-// Launch plan of one GEMM call, a pure function of the shape (also sizes the workspace).
+// Launch plan of one GEMM call, a pure function of the shape.
 struct Plan {
   bool skinny;
   int rb;                      // skinny: 16-row blocks
-  int ks;                      // skinny: waves per workgroup; tile: split-K factor
-  int tiles_m, tiles_n;
-  size_t ws_slots, ws_bytes;   // tile split-K: partial-tile bytes, total workspace bytes
+  int ks;                      // skinny: waves per workgroup
+  int tiles_m, tiles_n;        // tile kernel grid
 };
 
-constexpr int kCUs = 256;      // compute units of the MI355X
-// Splitting the groups of a tile over workgroups needs an agent-scope release per
-// workgroup, which costs a full L2 write-back here; measured slower than no split at
-// every shape tried, so it is off.
-constexpr bool kSplitK = false;
-
-Plan make_plan(int M, const mixllm_blob_info &L, bool partials) {
+Plan make_plan(int M, const mixllm_blob_info &L) {
   Plan pl{};
   if (M <= 64) {
     pl.skinny = true;
@@ -644,25 +696,19 @@ Plan make_plan(int M, const mixllm_blob_info &L, bool partials) {
     return pl;
   }
   pl.tiles_m = (M + kTileBM - 1) / kTileBM;
-  pl.tiles_n = (L.nb + 3) / 4;
-  const int64_t T = (int64_t)pl.tiles_m * pl.tiles_n;
-  // Two workgroups per CU: split the groups of each tile when there are too few tiles.
-  int ks = 1;
-  if (kSplitK && !partials && T < 2 * kCUs) {
-    ks = (int)((2 * kCUs + T - 1) / T);
-    ks = ks > 8 ? 8 : ks;
-    ks = ks > L.G ? L.G : ks;
-  }
-  pl.ks = ks;
-  if (ks > 1) {
-    pl.ws_slots = align256((size_t)T * ks * kTileBM * 128 * sizeof(float));
-    pl.ws_bytes = pl.ws_slots + align256((size_t)T * sizeof(int));
-  }
+  pl.tiles_n = (L.nb + kTileNB - 1) / kTileNB;
   return pl;
 }
 
+// The tile kernel addresses the row operands with 32-bit offsets (G * M * 32 bytes) and a
+// block's weights likewise (G * 4096).
+bool tile_offsets_fit(int M, const mixllm_blob_info &L) {
+  return (int64_t)L.G * M * 32 <= 0x7FFFFFFF && (int64_t)L.G * (int64_t)kW8Chunk <= 0x7FFFFFFF &&
+         (int64_t)kTileBM * L.K + (int64_t)L.G * 128 <= 0x7FFFFFFF;
+}
+
 template <bool PARTIALS>
-int launch(GemmArgs &a, const Plan &pl, void *workspace, hipStream_t stream) {
+int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
   (void)hipGetLastError();
   if (pl.skinny) {
     const int ks = pl.ks;
@@ -676,10 +722,7 @@ int launch(GemmArgs &a, const Plan &pl, void *workspace, hipStream_t stream) {
   } else {
     a.tiles_m = pl.tiles_m;
     a.tiles_n = pl.tiles_n;
-    a.ks = pl.ks;
-    a.ws = pl.ks > 1 ? (float *)workspace : nullptr;
-    a.cnt = pl.ks > 1 ? (int *)((uint8_t *)workspace + pl.ws_slots) : nullptr;
-    const int64_t T = (int64_t)a.tiles_m * a.tiles_n * a.ks;
+    const int64_t T = (int64_t)a.tiles_m * a.tiles_n;
     if (T > 0x7FFFFFFF) return MIXLLM_E_SHAPE;
     hipLaunchKernelGGL((gemm_tile_kernel<PARTIALS>), dim3((unsigned)T), dim3(kTileThreads), 0, stream, a);
   }
@@ -689,45 +732,49 @@ int launch(GemmArgs &a, const Plan &pl, void *workspace, hipStream_t stream) {
 }  // namespace
 
 extern "C" size_t mixllm_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n8) {
-  mixllm_blob_info L;
-  if (M <= 0 || !compute_layout(N, K, n8, &L)) return 0;
-  return make_plan(M, L, false).ws_bytes;
+  // No kernel needs scratch memory: the slices of a tile are reduced inside its workgroup.
+  (void)M;
+  (void)N;
+  (void)K;
+  (void)n8;
+  return 0;
 }
 
-extern "C" int mixllm_gemm_w4w8a8(const int8_t *aq, const float *sa, const int32_t *asum, int32_t M, int32_t N,
-                                  int32_t K, int32_t n8, const void *blob, size_t blob_bytes, uint16_t *y,
-                                  int64_t ldy, void *workspace, size_t workspace_bytes, void *stream) {
+extern "C" int mixllm_gemm_w4w8a8(const int8_t *aq, const float *sa, const int32_t *asum, const uint32_t *rowop,
+                                  int32_t M, int32_t N, int32_t K, int32_t n8, const void *blob, size_t blob_bytes,
+                                  uint16_t *y, int64_t ldy, void *workspace, size_t workspace_bytes, void *stream) {
   mixllm_blob_info L;
-  int st = check_common(aq, sa, asum, M, N, K, n8, blob, blob_bytes, &L);
+  int st = check_common(aq, sa, asum, rowop, M, N, K, n8, blob, blob_bytes, &L);
   if (st != MIXLLM_OK || M == 0) return st;
   if (!y) return MIXLLM_E_NULL;
   if (ldy < N) return MIXLLM_E_SHAPE;
-  const Plan pl = make_plan(M, L, false);
-  if (pl.ws_bytes) {
-    if (!workspace) return MIXLLM_E_NULL;
-    if (workspace_bytes < pl.ws_bytes) return MIXLLM_E_SPACE;
-    if (!is_aligned16(workspace)) return MIXLLM_E_SHAPE;
-  }
+  (void)workspace;
+  (void)workspace_bytes;
+  const Plan pl = make_plan(M, L);
+  if (!pl.skinny && !tile_offsets_fit(M, L)) return MIXLLM_E_SHAPE;
   GemmArgs a;
-  fill_args(a, aq, sa, asum, M, blob, L);
+  fill_args(a, aq, sa, asum, rowop, M, blob, L);
   a.y = y;
   a.ldy = ldy;
-  return launch<false>(a, pl, workspace, (hipStream_t)stream);
+  return launch<false>(a, pl, (hipStream_t)stream);
 }
 
-extern "C" int mixllm_gemm_w4w8a8_partials(const int8_t *aq, const float *sa, const int32_t *asum, int32_t M,
-                                           int32_t N, int32_t K, int32_t n8, const void *blob, size_t blob_bytes,
-                                           int32_t n_begin, int32_t n_count, int32_t *part, void *stream) {
+extern "C" int mixllm_gemm_w4w8a8_partials(const int8_t *aq, const float *sa, const int32_t *asum,
+                                           const uint32_t *rowop, int32_t M, int32_t N, int32_t K, int32_t n8,
+                                           const void *blob, size_t blob_bytes, int32_t n_begin, int32_t n_count,
+                                           int32_t *part, void *stream) {
   mixllm_blob_info L;
-  int st = check_common(aq, sa, asum, M, N, K, n8, blob, blob_bytes, &L);
+  int st = check_common(aq, sa, asum, rowop, M, N, K, n8, blob, blob_bytes, &L);
   if (st != MIXLLM_OK) return st;
   if (n_begin < 0 || n_count < 0 || (int64_t)n_begin + n_count > N) return MIXLLM_E_SHAPE;
   if (M == 0 || n_count == 0) return MIXLLM_OK;
   if (!part) return MIXLLM_E_NULL;
+  const Plan pl = make_plan(M, L);
+  if (!pl.skinny && !tile_offsets_fit(M, L)) return MIXLLM_E_SHAPE;
   GemmArgs a;
-  fill_args(a, aq, sa, asum, M, blob, L);
+  fill_args(a, aq, sa, asum, rowop, M, blob, L);
   a.part = part;
   a.n_begin = n_begin;
   a.n_count = n_count;
-  return launch<true>(a, make_plan(M, L, true), nullptr, (hipStream_t)stream);
+  return launch<true>(a, pl, (hipStream_t)stream);
 }

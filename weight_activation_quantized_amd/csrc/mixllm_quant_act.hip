@@ -13,6 +13,11 @@
 // Arithmetic matches the definition bit for bit: the maximum of |x| is exact, the scale
 // is an IEEE fp32 division amax / 127, each code is rne(x / s) with an IEEE division
 // (hipcc's default correctly rounded division; no fast-math), clamped to [-127, 127].
+//
+// Optionally the kernel also writes the row operands of the GEMM's scale products: s and
+// u = fp32(S_A * s) each as an exact sum of three bf16 values (truncate to bf16, the
+// remainder has at most 16 significant bits, truncate again, the second remainder has
+// at most 8), laid out as the bf16 MFMA row operand [p0 p0 p1 p1 p2 p2 0 0].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,9 +48,20 @@ __device__ __forceinline__ int quarter_sum(int v) {
   return v;
 }
 
+// x = p0 + p1 + p2 exactly, each a bf16; returns the row operand words
+// [p0 p0 | p1 p1 | p2 p2 | 0].
+__device__ __forceinline__ uint4 row_operand(float x) {
+  const uint32_t b0 = __float_as_uint(x) & 0xFFFF0000u;
+  const float r1 = x - __uint_as_float(b0);
+  const uint32_t b1 = __float_as_uint(r1) & 0xFFFF0000u;
+  const uint32_t b2 = __float_as_uint(r1 - __uint_as_float(b1)) & 0xFFFF0000u;
+  return make_uint4(b0 | (b0 >> 16), b1 | (b1 >> 16), b2 | (b2 >> 16), 0u);
+}
+
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__restrict__ a, int64_t lda,
                                                              int32_t M, int32_t K, int8_t *__restrict__ aq,
-                                                             float *__restrict__ sa, int32_t *__restrict__ asum) {
+                                                             float *__restrict__ sa, int32_t *__restrict__ asum,
+                                                             uint4 *__restrict__ rowop) {
   const int G = K / MIXLLM_GROUP;
   const int64_t pair = (int64_t)blockIdx.x * kPairsPerBlock + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -91,23 +107,27 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__r
     sa[(int64_t)g * M + m] = s;
     if (asum) asum[(int64_t)g * M + m] = qsum;
   }
+  if (rowop && sub < 2) {
+    const float v = sub == 0 ? s : (float)qsum * s;
+    rowop[((int64_t)g * 2 + sub) * M + m] = row_operand(v);
+  }
 }
 
 }  // namespace
 
 extern "C" int mixllm_quant_act(const uint16_t *a, int64_t lda, int32_t M, int32_t K, int32_t group,
-                                int8_t *aq, float *sa, int32_t *asum, void *stream) {
+                                int8_t *aq, float *sa, int32_t *asum, uint32_t *rowop, void *stream) {
   if (group != MIXLLM_GROUP) return MIXLLM_E_GROUP;
   if (M < 0 || K <= 0 || K % MIXLLM_GROUP != 0 || lda < K || lda % 8 != 0) return MIXLLM_E_SHAPE;
   if (M == 0) return MIXLLM_OK;
   if (!a || !aq || !sa) return MIXLLM_E_NULL;
   if (!mixllm::is_aligned16(a) || !mixllm::is_aligned16(aq) || !mixllm::is_aligned16(sa) ||
-      (asum && !mixllm::is_aligned16(asum)))
+      (asum && !mixllm::is_aligned16(asum)) || (rowop && !mixllm::is_aligned16(rowop)))
     return MIXLLM_E_SHAPE;
   const int64_t npairs = (int64_t)M * (K / MIXLLM_GROUP);
   const int64_t blocks = (npairs + kPairsPerBlock - 1) / kPairsPerBlock;
   if (blocks > 0x7FFFFFFF) return MIXLLM_E_SHAPE;
   hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a,
-                     lda, M, K, aq, sa, asum);
+                     lda, M, K, aq, sa, asum, reinterpret_cast<uint4 *>(rowop));
   return hipGetLastError() == hipSuccess ? MIXLLM_OK : MIXLLM_E_HIP;
 }

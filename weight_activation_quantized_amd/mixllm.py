@@ -54,7 +54,7 @@ class BlobInfo(ctypes.Structure):
                 ("n4_promoted", ctypes.c_int32),
                 ("off_w4", ctypes.c_uint64), ("off_s4", ctypes.c_uint64), ("off_z4", ctypes.c_uint64),
                 ("off_w8", ctypes.c_uint64), ("off_s8", ctypes.c_uint64), ("off_zp", ctypes.c_uint64),
-                ("off_idx", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
+                ("off_idx", ctypes.c_uint64), ("off_pw", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -67,12 +67,12 @@ _SIGS = {
     "mixllm_pack_weights": ([_vp, _i32, _i32, _i32, _vp, _i32, _vp, _sz], ctypes.c_int),
     "mixllm_blob_get_info": ([_vp, _sz, ctypes.POINTER(BlobInfo)], ctypes.c_int),
     "mixllm_unpack_weights": ([_vp, _sz, _vp, _vp, _vp, _vp], ctypes.c_int),
-    "mixllm_quant_act": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mixllm_quant_act": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mixllm_gemm_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
-    "mixllm_gemm_w4w8a8": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _i64, _vp, _sz, _vp],
+    "mixllm_gemm_w4w8a8": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _i64, _vp, _sz, _vp],
                            ctypes.c_int),
-    "mixllm_gemm_w4w8a8_partials": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp, _vp],
-                                    ctypes.c_int),
+    "mixllm_gemm_w4w8a8_partials": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp,
+                                     _vp], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -165,36 +165,42 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def mixllm_quant_act(a, aq, sa, asum=None, stream=None):
+def mixllm_quant_act(a, aq, sa, asum=None, rowop=None, stream=None):
     """a: fp16 [M, K] CUDA tensor (rows may be strided); aq: int8 [M, K];
-    sa: fp32 [G, M]; asum: int32 [G, M] or None."""
+    sa: fp32 [G, M]; asum: int32 [G, M] or None; rowop: 32-bit [G, 2, M, 4] or None."""
     m, k = a.shape
     if a.dtype != torch.float16 or a.stride(1) != 1:
         raise ValueError("a must be fp16 with unit column stride")
     lda = a.stride(0) if m > 1 else k
-    _check(_lib.mixllm_quant_act(_ptr(a), lda, m, k, GROUP, _ptr(aq), _ptr(sa), _ptr(asum), _stream(stream)))
+    _check(_lib.mixllm_quant_act(_ptr(a), lda, m, k, GROUP, _ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop),
+                                 _stream(stream)))
 
 
 def mixllm_gemm_workspace_bytes(m: int, n: int, k: int, n8: int) -> int:
     return int(_lib.mixllm_gemm_workspace_bytes(m, n, k, n8))
 
 
-def mixllm_gemm_w4w8a8(aq, sa, asum, m: int, n: int, k: int, n8: int, blob_dev, y, workspace=None,
+def mixllm_gemm_w4w8a8(aq, sa, asum, rowop, m: int, n: int, k: int, n8: int, blob_dev, y, workspace=None,
                        stream=None):
-    """aq, sa, asum: outputs of mixllm_quant_act; y: fp16 [M, ldy] CUDA tensor;
+    """aq, sa, asum, rowop: outputs of mixllm_quant_act; y: fp16 [M, ldy] CUDA tensor;
     blob_dev: uint8 CUDA tensor holding the packed blob."""
     ldy = y.stride(0) if y.dim() == 2 and m > 1 else n
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.mixllm_gemm_w4w8a8(_ptr(aq), _ptr(sa), _ptr(asum), m, n, k, n8, _ptr(blob_dev),
+    _check(_lib.mixllm_gemm_w4w8a8(_ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop), m, n, k, n8, _ptr(blob_dev),
                                    blob_dev.numel(), _ptr(y), ldy, _ptr(workspace), ws, _stream(stream)))
 
 
-def mixllm_gemm_w4w8a8_partials(aq, sa, asum, m: int, n: int, k: int, n8: int, blob_dev, n_begin: int,
+def mixllm_gemm_w4w8a8_partials(aq, sa, asum, rowop, m: int, n: int, k: int, n8: int, blob_dev, n_begin: int,
                                 n_count: int, part, stream=None):
     """part: int32 [M, n_count, G] CUDA tensor."""
-    _check(_lib.mixllm_gemm_w4w8a8_partials(_ptr(aq), _ptr(sa), _ptr(asum), m, n, k, n8, _ptr(blob_dev),
-                                            blob_dev.numel(), n_begin, n_count, _ptr(part),
+    _check(_lib.mixllm_gemm_w4w8a8_partials(_ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop), m, n, k, n8,
+                                            _ptr(blob_dev), blob_dev.numel(), n_begin, n_count, _ptr(part),
                                             _stream(stream)))
+
+
+def rowop_buffer(m: int, k: int, device="cuda"):
+    """Storage for mixllm_quant_act's row operands: 32-bit words [G, 2, M, 4]."""
+    return torch.empty((k // GROUP, 2, m, 4), dtype=torch.int32, device=device)
 
 
 # ---------------------------------------------------------------------------- convenience
@@ -218,6 +224,7 @@ class PackedLinear:
         return dict(aq=torch.empty((m, self.k), dtype=torch.int8, device=dev),
                     sa=torch.empty((self.g, m), dtype=torch.float32, device=dev),
                     asum=torch.empty((self.g, m), dtype=torch.int32, device=dev),
+                    rowop=rowop_buffer(m, self.k, dev),
                     y=torch.empty((m, self.n), dtype=torch.float16, device=dev),
                     ws=self._workspace(m))
 
@@ -228,7 +235,7 @@ class PackedLinear:
     def forward(self, a, bufs=None, stream=None):
         m = a.shape[0]
         bufs = bufs or self.buffers(m)
-        mixllm_quant_act(a, bufs["aq"], bufs["sa"], bufs["asum"], stream)
-        mixllm_gemm_w4w8a8(bufs["aq"], bufs["sa"], bufs["asum"], m, self.n, self.k, self.n8, self.blob,
-                           bufs["y"], bufs["ws"], stream)
+        mixllm_quant_act(a, bufs["aq"], bufs["sa"], bufs["asum"], bufs["rowop"], stream)
+        mixllm_gemm_w4w8a8(bufs["aq"], bufs["sa"], bufs["asum"], bufs["rowop"], m, self.n, self.k, self.n8,
+                           self.blob, bufs["y"], bufs["ws"], stream)
         return bufs["y"]
