@@ -341,13 +341,11 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     if constexpr (KIND == kW4) acc[rb] = mfma_bf16(ru, v4i{(int)zw, (int)zw, (int)zw, (int)zw}, acc[rb]);
   };
 
-  // The A operands of both 32-row blocks of stage st (8 LDS reads, issued together).
-  auto load_a = [&](int st, v4i (&av)[2][4]) {
-    const uint8_t *at = abase + st * kAStage;
+  // The A operands of one 32-row block of stage st (4 LDS reads, issued together).
+  auto load_a = [&](int st, int rb, v4i (&av)[4]) {
+    const uint8_t *at = abase + st * kAStage + rb * 32 * 128;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) av[rb][k] = *reinterpret_cast<const v4i *>(at + va[k] + rb * 32 * 128);
+    for (int k = 0; k < 4; ++k) av[k] = *reinterpret_cast<const v4i *>(at + va[k]);
   };
   // The group partial of one 32-row block on the matrix cores.
   auto block_mma = [&](const v4i (&av)[4], const v4i (&bq)[4]) {
@@ -396,17 +394,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
       // partials that are never folded (its column words are replaced by zeros).
       const bool act = gb + s < ge;
       const uint32_t sw = (act && h == 0) ? swcur : 0u, zw = (act && h == 0) ? zwcur : 0u;
-      // LDS operand reads first, fenced off, so their latency overlaps the decode and the
-      // first matrix-core ops instead of preceding each op.
-      v4i av[2][4];
-      load_a(st, av);
-      const int st_prev = st == 0 ? kSA - 1 : st - 1;
-      v4i rs1, ru1, rs0, ru0;
-      if constexpr (!PARTIALS) {
-        load_rows(1, st_prev, rs1, ru1);
-        load_rows(0, st, rs0, ru0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
       v4i bq[4];
       if constexpr (KIND == kW4) {
 #pragma unroll
@@ -421,20 +408,32 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
 #pragma unroll
         for (int k = 0; k < 4; ++k) bq[k] = bR[j][k];
       }
+      const int st_prev = st == 0 ? kSA - 1 : st - 1;
       if constexpr (PARTIALS) {
-        const v16i P0 = block_mma(av[0], bq);
+        v4i av[4];
+        load_a(st, 0, av);
+        const v16i P0 = block_mma(av, bq);
         if (act) emit(0, P0, gb + s, zpR[j]);
-        const v16i Pb = block_mma(av[1], bq);
+        load_a(st, 1, av);
+        const v16i Pb = block_mma(av, bq);
         if (act) emit(1, Pb, gb + s, zpR[j]);
       } else {
         // Block 0 of this step on the matrix cores while block 1 of the previous step
-        // folds, then block 1 of this step while block 0 of this step folds.
-        const v16f sc1 = scales(rs1, swprev);
-        const v16i P0 = block_mma(av[0], bq);
-        fold(1, P1[1 - j], sc1, ru1, zwprev);
-        const v16f sc0 = scales(rs0, sw);
-        P1[j] = block_mma(av[1], bq);
-        fold(0, P0, sc0, ru0, zw);
+        // folds, then block 1 of this step while block 0 of this step folds.  Each block's
+        // LDS operand reads are issued together ahead of its matrix-core ops.
+        v4i av[4], rs, ru;
+        load_a(st, 0, av);
+        load_rows(1, st_prev, rs, ru);
+        __builtin_amdgcn_sched_barrier(0);
+        const v16f sc1 = scales(rs, swprev);
+        const v16i P0 = block_mma(av, bq);
+        fold(1, P1[1 - j], sc1, ru, zwprev);
+        load_a(st, 1, av);
+        load_rows(0, st, rs, ru);
+        __builtin_amdgcn_sched_barrier(0);
+        const v16f sc0 = scales(rs, sw);
+        P1[j] = block_mma(av, bq);
+        fold(0, P0, sc0, ru, zw);
       }
       swprev = sw;
       zwprev = zw;
