@@ -43,7 +43,7 @@ extern "C" {
 
 #define MIXLLM_GROUP 128
 #define MIXLLM_BLOB_MAGIC 0x344C584Du /* "MXL4" little-endian */
-#define MIXLLM_BLOB_VERSION 3u
+#define MIXLLM_BLOB_VERSION 4u
 
 typedef enum mixllm_status {
   MIXLLM_OK = 0,
@@ -135,11 +135,12 @@ int mixllm_unpack_weights(const void *blob_host, size_t blob_bytes, uint8_t *q, 
  * sa_dev:     output fp32 [G][M] (group-major: the scales of one group for consecutive
  *             tokens are contiguous).
  * asum_dev:   output int32 [G][M] code sums, or NULL to skip.
- * rowop_dev:  output uint32 [G][2][M][4], or NULL to skip: the row operands of the GEMM's
- *             scale products.  [g][0][m] holds s and [g][1][m] holds u = fp32(S_A * s), each
- *             as three bf16 values p0 + p1 + p2 that sum to it exactly (p0 = s truncated to
- *             bf16, p1 = the remainder truncated, p2 = the rest), stored as the words
- *             {p0 | p0 << 16, p1 | p1 << 16, p2 | p2 << 16, 0}.
+ * rowop_dev:  output uint32 [G][M][8], or NULL to skip: the row operands of the GEMM's
+ *             scale products.  s and u = fp32(S_A * s) are each split into three bf16
+ *             values p0 + p1 + p2 that sum to them exactly (p0 = the value truncated to
+ *             bf16, p1 = the remainder truncated, p2 = the rest); with the word
+ *             w(p) = p | p << 16, record [g][m] is {w(u0), w(u1), w(s0), w(s1),
+ *             w(u2), 0, w(s2), 0}.
  * Errors: E_NULL, E_SHAPE, E_GROUP, E_HIP.
  * ------------------------------------------------------------------------------------ */
 int mixllm_quant_act(const uint16_t *a_fp16_dev, int64_t lda, int32_t M, int32_t K, int32_t group,

@@ -47,20 +47,27 @@ def _quant(L, a16, lda_pad=0, with_sum=True):
     return aq, sa, asum, rowop
 
 
-def _split3_words(x32):
-    """Host-side exact three-way bf16 split of fp32 values, as the row operand words
-    [p0 p0, p1 p1, p2 p2, 0] (uint32)."""
+def _split3(x32):
+    """Host-side exact three-way bf16 split of fp32 values: the words p | p << 16 of the
+    pieces p0, p1, p2 (uint32), checked to sum to x exactly."""
     x32 = np.asarray(x32, np.float32)
     b0 = x32.view(np.uint32) & np.uint32(0xFFFF0000)
     r1 = (x32 - b0.view(np.float32)).astype(np.float32)
     b1 = r1.view(np.uint32) & np.uint32(0xFFFF0000)
     r2 = (r1 - b1.view(np.float32)).astype(np.float32)
     b2 = r2.view(np.uint32) & np.uint32(0xFFFF0000)
-    # exactness: the three pieces sum to x in float64
     tot = b0.view(np.float32).astype(np.float64) + b1.view(np.float32) + b2.view(np.float32)
     assert np.array_equal(tot, x32.astype(np.float64))
-    words = [b | (b >> np.uint32(16)) for b in (b0, b1, b2)] + [np.zeros_like(b0)]
-    return np.stack(words, axis=-1)
+    return [b | (b >> np.uint32(16)) for b in (b0, b1, b2)]
+
+
+def _rowop_records(sa_gm, u_gm):
+    """The row operand records [G][M][8] of s_a and u = fp32(S_A s_a):
+    {w(u0), w(u1), w(s0), w(s1), w(u2), 0, w(s2), 0}."""
+    s0, s1, s2 = _split3(sa_gm)
+    u0, u1, u2 = _split3(u_gm)
+    z = np.zeros_like(s0)
+    return np.stack([u0, u1, s0, s1, u2, z, s2, z], axis=-1)
 
 
 # --------------------------------------------------------------------------- quant_act
@@ -82,10 +89,9 @@ def test_quant_act_bitexact(L, m, k, dist):
     assert np.array_equal(aq.cpu().numpy(), oq)
     assert np.array_equal(sa.cpu().numpy().T.view(np.uint32), osa.view(np.uint32))
     assert np.array_equal(asum.cpu().numpy().T, osum)
-    # row operands: [g][0][m] splits s_a, [g][1][m] splits fp32(S_A * s_a)
+    # row operand records of s_a and fp32(S_A * s_a)
     ro = rowop.cpu().numpy().view(np.uint32)
-    assert np.array_equal(ro[:, 0], _split3_words(osa.T))
-    assert np.array_equal(ro[:, 1], _split3_words(osum.T.astype(np.float32) * osa.T))
+    assert np.array_equal(ro, _rowop_records(osa.T, osum.T.astype(np.float32) * osa.T))
 
 
 def test_quant_act_golden_ties(L):

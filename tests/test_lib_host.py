@@ -66,8 +66,9 @@ def _bf16_pair_value(words):
 
 @pytest.mark.parametrize("n,k,n8", [(200, 512, 169), (100, 384, 7), (64, 256, 0)])
 def test_pack_scale_words(n, k, n8):
-    """The pw section holds s_w and -z * s_w of every packed channel as exact bf16 pairs
-    (0 in the second word for 8-bit, promoted and empty channels)."""
+    """The pw section holds s_w, -z * s_w and -1.5 * 2^23 * s_w of every packed channel as
+    exact bf16 pairs (0 in the second word for 8-bit, promoted and empty channels), and a
+    zero group after each block's G groups."""
     sh = WL.Shape(0, "edge", 1, n, k, n8)
     w, idx8 = WL.make_layer_weights(sh)
     blob = L.mixllm_pack_weights(w, idx8)
@@ -75,18 +76,21 @@ def test_pack_scale_words(n, k, n8):
     q, z, s16, is8 = L.mixllm_unpack_weights(blob)
     g = k // 128
     nb = info["nb"]
-    pw = blob[info["off_pw"]: info["off_pw"] + nb * g * 256].view(np.uint32).reshape(nb, g, 32, 2)
+    pw = blob[info["off_pw"]: info["off_pw"] + nb * (g + 1) * 384].view(np.uint32).reshape(nb, g + 1, 32, 3)
+    assert not pw[:, g].any()
     idx = blob[info["off_idx"]: info["off_idx"] + nb * 32 * 4].view(np.int32)
     s64 = s16.astype(np.float64)
     for j in range(nb * 32):
         b, c = divmod(j, 32)
-        sw = _bf16_pair_value(pw[b, :, c, 0])
-        zw = _bf16_pair_value(pw[b, :, c, 1])
+        sw = _bf16_pair_value(pw[b, :g, c, 0])
+        zw = _bf16_pair_value(pw[b, :g, c, 1])
+        cw = _bf16_pair_value(pw[b, :g, c, 2])
         o = idx[j]
         if o < 0:
-            assert not sw.any() and not zw.any()
+            assert not sw.any() and not zw.any() and not cw.any()
             continue
         assert np.array_equal(sw, s64[o]), j
+        assert np.array_equal(cw, -12582912.0 * s64[o]), j
         in_nibbles = j < 32 * info["nb4"]
         expect_z = -(z[o].astype(np.float64) * s64[o]) if in_nibbles else np.zeros(g)
         assert np.array_equal(zw, expect_z), j
@@ -126,7 +130,7 @@ def test_packed_bytes_formula():
         g = k // 128
         w_bytes = 32 * k * (nb4 * O.weight_footprint(4) + nb8 * O.weight_footprint(8))
         side = 32 * g  # zero points of the <= 31 promoted 4-bit channels (unpacking only)
-        side += nb * g * 256  # the tile kernel's scale words, 8 bytes per channel and group
+        side += nb * (g + 1) * 384  # the tile kernel's column words: 12 bytes per channel and group, plus a zero group
         size = L.mixllm_packed_bytes(n, k, 128, n8)
         assert w_bytes + 4 * 32 * nb + side <= size <= w_bytes + 4 * 32 * nb + side + 8 * 256 + 256
         # the padding to 32-channel blocks and the <= 31 4-bit channels stored as int8

@@ -10,15 +10,19 @@
 // subset, and the epilogue writes every channel's fp16 result to its original index.
 //
 // Differences from the pages' A100 design, for CDNA4:
-//  * (W_q - z) is formed with byte-wise SWAR arithmetic on packed nibbles:
-//    ((q | 0x80) - z) ^ 0x80 per byte, four codes per 32-bit op (the role of the pages'
-//    vsub4; CDNA has no byte-vector subtract).
-//  * int32 -> fp32 uses v_cvt_f32_i32, a full-rate VALU op on CDNA; the pages' 0x4b400000
-//    bias trick replaces a slow conversion on their GPU and buys nothing here.
-//  * The tile kernel stages the activation tile through LDS (shared by the four waves of
-//    a workgroup) and streams each wave's own weights straight from HBM into registers,
-//    one group ahead; the skinny kernel (small M) streams both from L2/HBM and splits the
-//    groups over the waves of a workgroup, reducing through LDS.
+//  * The tile kernel feeds raw 4-bit codes to the matrix cores and removes the zero point
+//    in the float domain with one more matrix-core op per block (-(S_A s_a)(z s_w));
+//    the scale products s_a s_w are matrix-core outer products of exact bf16 splits.
+//    The skinny kernel (small M, bandwidth-bound) forms (W_q - z) with byte-wise SWAR
+//    arithmetic: ((q | 0x80) - z) ^ 0x80 per byte, four codes per 32-bit op (the role of
+//    the pages' vsub4; CDNA has no byte-vector subtract).
+//  * int32 -> fp32: the tile kernel either converts with v_cvt_f32_i32 (exact fold) or
+//    uses the pages' float-bits bias with the bias seeded into the MFMA accumulator and
+//    its subtraction moved onto the matrix cores (bias fold, one VALU op per element).
+//  * The tile kernel stages the activation tile and the row operands through LDS
+//    (shared by the eight waves of a workgroup) with direct-to-LDS loads and streams
+//    each wave's own weights into registers; the skinny kernel streams both from L2/HBM
+//    and splits the groups over the waves of a workgroup, reducing through LDS.
 //
 // MFMA layouts used (gfx950):
 //  * v_mfma_i32_32x32x32_i8: lane l supplies row/column (l % 32) and 16 bytes of k; the
@@ -30,6 +34,7 @@
 //  long as both operands use the same one; the packer lays the weights out for the
 //  assignment below and the activation reads follow it.
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "mixllm.h"
@@ -118,53 +123,63 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 // ------------------------------------------------------------------------------------
-// Tile kernel (M > 64).  A workgroup of 4 x KS waves owns 64 rows x 128 channels (4
-// blocks of 32 channels).  Wave (b, q) computes block 4 tn + b for all 64 rows over the
-// q-th of KS contiguous slices of the groups; the KS partial accumulators are summed
-// through LDS at the end in slice order.  Several waves per SIMD let one wave's
-// matrix-core work cover another's VALU work and memory waits.
+// Tile kernel (M > 64).  A workgroup of 8 waves owns 64 rows x 128 channels (4 blocks of
+// 32 channels).  Wave (b, q) computes block 4 tn + b for all 64 rows over the groups
+// g = q, q + 2, q + 4, ... (two interleaved group slices, two waves per SIMD); the
+// slices' accumulators are summed through LDS at the end in slice order.
 //
 // Per group and wave (two 32-row blocks):
-//   * 4 x 2 v_mfma_i32_32x32x32_i8: the exact group partials.  4-bit blocks feed the raw
+//   * 4 x 2 v_mfma_i32_32x32x32_i8: the group partials.  4-bit blocks feed the raw
 //     codes q (3 VALU ops per 8 codes); the zero point is removed in the float domain;
 //   * per block, 1 v_mfma_f32_32x32x16_bf16 for the scale products s_a[m] s_w[n] as an
-//     outer product of exact bf16 splits: the row operand [a0 a0 a1 a1 a2 a2 0 0]
-//     (s_a = a0 + a1 + a2, written by the activation quantizer) against the column
-//     operand [b0 b1] x 4 (s_w = b0 + b1, from the packed weights);
-//   * 4-bit blocks: 1 more that adds -(S_A[m] s_a[m]) (z[n] s_w[n]) to the accumulator,
-//     S_A being the group's activation code sum: sum_k (q - z) a_k s_a s_w =
-//     s_a s_w sum_k q a_k - (S_A s_a) (z s_w);
-//   * the fold acc += float(P) * scale: 2 VALU ops per output element.
-// The integer partial is exact; only the fp32 fold differs from the fp64 definition.
+//     outer product of exact bf16 splits (s_a = a0 + a1 + a2 from the activation
+//     quantizer, s_w = b0 + b1 from the packed weights);
+//   * per block, 1 more that adds the correction -(S_A[m] s_a[m]) (z[n] s_w[n]) to the
+//     accumulator (sum_k (q - z) a_k = sum_k q a_k - z S_A, S_A the group's code sum),
+//     and with the bias fold also -B s_a s_w; both MFMAs read the same row operand;
+//   * the fold: acc += float(P) * scale.  Two forms:
+//       exact: v_cvt_f32_i32 then fma (2 VALU ops per output element);
+//       bias:  the partial's MFMA chain starts from the integer bias 0x4B400000, so the
+//              bits of the result read as a float are exactly B + P (B = 1.5 * 2^23,
+//              |P| < 2^22), and one fma adds (B + P) * scale; the correction MFMA
+//              subtracts B s_a s_w.  This is the float-bits conversion of the talk notes
+//              (高速 I2F 変換) with the subtraction moved onto the matrix cores; it costs
+//              one VALU op per element, and the fold differs from the exact one by at
+//              most B |s_a s_w - fp32(s_a s_w)| plus one rounding at magnitude B s_a s_w,
+//              about s_a s_w per group (an error of order one unit of the integer partial).
 // Software pipeline: block 0 of a group runs on the matrix cores while block 1 of the
 // previous group folds, then block 1 while block 0 folds.
 //
-// Streams.  The activation tile of a group (64 rows x 128 B) and the rows' scale
-// operands (2 x 64 x 16 B) go from memory straight into LDS (buffer_load ... lds)
-// kD = kSA - 2 groups ahead of their use, in a ring of kSA stages (a stage is read during
-// its step and the next); a wave's weights and scale words stream into a register ring
-// SW groups deep.  Every wave issues the same fixed set of loads per step, so a wait for
-// "at most N loads outstanding" (N counting the later steps' loads) proves that the
-// current step's stage has landed; a workgroup barrier after that wait publishes it.  The
+// Streams.  The activation tile of a group (64 rows x 128 B) and the rows' operands
+// (64 rows x 32 B) go from memory straight into LDS (buffer_load ... lds), and each
+// wave's weights and column words into registers, kSA - 1 groups ahead of their use, in
+// rings of kSA stages; the step loop is unrolled by kSA so every stage and ring index is
+// a compile-time constant.  Every wave issues the same fixed set of loads per step, so
+// a wait for "at most 2 steps' loads outstanding" proves that the current step's stage
+// and weights have landed; a workgroup barrier after that wait publishes the stage.  The
 // wait is explicit because the compiler does not track LDS written by these loads.
+// Loads address the group through the scalar offset, clamped to a valid group; steps past
+// the slice's last group read a zero group of column words and so add nothing.
 // ------------------------------------------------------------------------------------
 constexpr int kTileBM = 64;
 constexpr int kTileNB = 4;                          // channel blocks per workgroup
-#ifndef MIXLLM_TILE_KS
-#define MIXLLM_TILE_KS 2
-#endif
-constexpr int kKS = MIXLLM_TILE_KS;                 // group slices per workgroup
+constexpr int kKS = 2;                              // interleaved group slices
 constexpr int kTileWaves = kTileNB * kKS;
 constexpr int kTileThreads = 64 * kTileWaves;
-#ifndef MIXLLM_TILE_SA
-#define MIXLLM_TILE_SA 6
+constexpr int kSA = 4;                              // LDS stages = ring slots = unroll
+#ifndef MIXLLM_WRING
+#define MIXLLM_WRING 4
 #endif
-constexpr int kSA = MIXLLM_TILE_SA;                 // LDS stages
-constexpr int kD = kSA - 2;                         // prefetch distance (groups)
-#ifndef MIXLLM_SW4
-#define MIXLLM_SW4 2
+constexpr int kWR = MIXLLM_WRING;                   // weight ring slots (2 or 4)
+static_assert(kWR == 2 || kWR == 4, "weight ring");
+#ifndef MIXLLM_TILE_PHASE
+#define MIXLLM_TILE_PHASE 1
 #endif
-constexpr int kSW4 = MIXLLM_SW4, kSW8 = 2;          // weight ring depth, 4-bit / 8-bit blocks
+#ifndef MIXLLM_FOLD_BIAS
+#define MIXLLM_FOLD_BIAS 0
+#endif
+constexpr bool kFoldBias = MIXLLM_FOLD_BIAS != 0;
+constexpr int kBiasBits = 0x4B400000;               // float bits of B = 1.5 * 2^23
 
 // LDS bank swizzle of the activation tile: a ds_read_b128 wave is served in groups of
 // 16 lanes over 64 banks, and the rows one group reads must hit distinct banks; the
@@ -173,10 +188,13 @@ __device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
 
 struct TileSmem {
   uint8_t a[kSA][kKS][kTileBM * 128];           // [stage][slice] activation tiles
-  uint32_t rp[kSA][kKS][4][64][4];              // [stage][slice][row / 16][lane] row operands:
-                                                // lane < 16: s_a of row 16 b + lane; 16..31: S_A s_a; rest unused
+  uint8_t r[kSA][kKS][kTileBM * 32];            // [stage][slice] row operand records
 };
-static_assert((kKS - 1) * kTileNB * kTileBM * 32 * 4 <= (int)sizeof(TileSmem::a), "reduction space");
+constexpr int kAStage = kKS * kTileBM * 128;        // bytes per activation stage
+constexpr int kRBase = kSA * kAStage;               // offset of the row operand stages
+constexpr int kRStage = kKS * kTileBM * 32;
+static_assert(offsetof(TileSmem, r) == kRBase, "LDS layout");
+static_assert(kKS * kTileNB * 16 * 64 * 4 <= (int)sizeof(TileSmem::a), "reduction space");
 
 __device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
@@ -187,8 +205,9 @@ enum BlockKind { kNone = 0, kW4 = 1, kW8 = 2 };
 
 // Buffer resources: the 128-bit descriptor of a byte range [base, base + bytes).  Loads
 // through it take a per-lane 32-bit offset (computed once) plus a wave-uniform offset
-// (per group, scalar arithmetic), so the inner loop spends no vector ops on addresses,
-// and loads past `bytes` return zeros instead of touching memory.
+// (per group, scalar arithmetic), so the inner loop spends no vector ops on addresses.
+// Lanes whose per-lane offset is past `bytes` read zeros; the scalar offsets used here
+// always stay inside the range.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcFlags = 0x00020000;  // gfx9 raw buffer, 32-bit data format
 
@@ -201,6 +220,10 @@ __device__ __forceinline__ v4i bload16(Rsrc r, int voff, int soff) {
 }
 __device__ __forceinline__ uint32_t bload4(Rsrc r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+typedef uint32_t v3u __attribute__((ext_vector_type(3)));
+__device__ __forceinline__ v3u bload12(Rsrc r, int voff, int soff) {
+  return __builtin_bit_cast(v3u, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0));
 }
 typedef __attribute__((address_space(3))) void *LdsPtr;
 // 16 bytes per lane from the buffer into LDS at dst + 16 * lane (dst wave-uniform).
@@ -216,20 +239,6 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// Wait until at most N vector-memory operations are outstanding, N = min(s, CAP) * L.
-template <int L, int CAP>
-__device__ __forceinline__ void wait_vm_steps(int s) {
-  static_assert(CAP <= 3, "extend the cases below");
-  if (CAP >= 3 && s >= 3) {
-    wait_vm<(CAP >= 3 ? 3 : 0) * L>();
-  } else if (CAP >= 2 && s >= 2) {
-    wait_vm<(CAP >= 2 ? 2 : 0) * L>();
-  } else if (CAP >= 1 && s >= 1) {
-    wait_vm<L>();
-  } else {
-    wait_vm<0>();
-  }
-}
 
 // Workgroup barrier for LDS data: this wave's LDS reads and writes complete, then the
 // barrier.  The scheduler barriers keep the compiler from moving memory operations
@@ -241,30 +250,33 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int KIND, bool PARTIALS>
+template <int KIND, bool PARTIALS, int PHASE, bool RDMA>
 __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m0, int blk, int bi, int q,
                                           int lane) {
-  constexpr int SW = KIND == kW8 ? kSW8 : kSW4;
+  constexpr bool HASW = KIND != kNone;
   constexpr int NW = KIND == kW8 ? 4 : (KIND == kW4 ? 2 : 0);     // 16-byte weight loads per step
-  constexpr int NPW = KIND == kW4 ? 2 : (KIND == kW8 ? 1 : 0);    // scale words per step
   constexpr int NZ = (PARTIALS && KIND == kW4) ? 1 : 0;           // zero-point word (partials)
-  constexpr int L = 3 + NW + NPW + NZ;                            // loads per step
-  static_assert(kD >= 2 && (kD - 1) * L < 64, "prefetch distance");
-  const int ch32 = lane & 31, h = lane >> 5, half = ch32 >> 4, ch = ch32 & 15;
+  constexpr int LD = RDMA ? 3 : 2;                                // direct-to-LDS loads per step
+  constexpr int LW = HASW ? NW + 1 + NZ : 0;                      // weight-ring loads per step
+  // Loads that may still be outstanding when a step's loads have landed.  Ring of four:
+  // a step's weights and stage are both issued kSA - 1 steps ahead, so the batches of the
+  // two later steps.  Ring of two: the weights are issued one step ahead, so the stage
+  // batch of the previous step (or, for a wave without weights, of the two previous).
+  constexpr int WAIT = kWR == 4 ? 2 * (LW + LD) : (HASW ? LD : 2 * LD);
+  constexpr bool CORR = KIND == kW4 || (kFoldBias && KIND == kW8);
+  const int ch32 = lane & 31, h = lane >> 5;
   const int G = p.G;
-  const int gb = G * q / kKS, ge = G * (q + 1) / kKS;             // this slice's groups
   const int nsteps = (G + kKS - 1) / kKS;                          // same for every wave
-  const int glast = max(ge - 1, gb);
-  auto grp = [&](int s) { return min(gb + s, glast); };            // clamped: always a valid group
+  const int niter = (nsteps + kSA - 1) / kSA;
 
-  // Descriptors.  Activation rows past M load zeros; operand rows past M read other
-  // rows (finite, never stored) or zeros past the end.
+  // Descriptors.  Activation rows past M load zeros; operand rows past M repeat row M - 1.
   const Rsrc ra = make_rsrc(p.aq + (int64_t)m0 * p.K, (int64_t)(p.M - m0) * p.K);
-  const Rsrc rro = make_rsrc(p.rowop, (int64_t)G * 2 * p.M * 16);
+  const Rsrc rro = make_rsrc(p.rowop, (int64_t)G * p.M * 32);
   const int bq = KIND == kW8 ? blk - p.nb4 : blk;
-  const Rsrc rw = KIND == kW8 ? make_rsrc(p.w8 + (size_t)bq * G * kW8Chunk, (int64_t)G * kW8Chunk)
-                              : make_rsrc(p.w4 + (size_t)bq * G * kW4Chunk, (int64_t)G * kW4Chunk);
-  const Rsrc rpw = make_rsrc((const uint8_t *)p.pw + (size_t)blk * G * kPwChunk, (int64_t)G * kPwChunk);
+  constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
+  const Rsrc rw = make_rsrc((KIND == kW8 ? p.w8 : p.w4) + (size_t)bq * G * kWChunk, (int64_t)G * kWChunk);
+  const Rsrc rpw = make_rsrc((const uint8_t *)p.pw + (size_t)blk * (G + 1) * kPwChunk, (int64_t)(G + 1) * kPwChunk);
+  const Rsrc rz = make_rsrc(p.z4 + (size_t)blk * G * kZ4Chunk, NZ ? (int64_t)G * kZ4Chunk : 0);
 
   // Per-lane offsets.
   int vdma[2];  // this wave loads rows [16 bi, 16 bi + 16) of the slice's tile, 8 rows per load
@@ -273,87 +285,80 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     const int r = 16 * bi + 8 * i + (lane >> 3), pos = lane & 7;
     vdma[i] = r * p.K + ((pos ^ swz_a(r)) << 4);
   }
-  // ... and the operands of the same 16 rows: lanes 0-15 s_a, lanes 16-31 S_A s_a (lanes
-  // 32-63 repeat them into the unused half of the wave's operand area)
-  const int vro = (((lane >> 4) & 1) * p.M + m0 + 16 * bi + (lane & 15)) * 16;
-  const int vpw = ch32 * 8;
+  // ... and (waves 0 and 1 of a slice) the 32-byte operand records of rows [32 bi, 32 bi + 32)
+  const int vro = min(m0 + 32 * bi + (lane >> 1), p.M - 1) * 32 + (lane & 1) * 16;
+  const int vpw = ch32 * (int)(kPwWords * 4);
   int vw[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    vw[s] = KIND == kW8 ? ((half * 8 + chunk32(s, h)) * 16 + ch) * 16 : ((half * 4 + 2 * (s & 1) + h) * 16 + ch) * 16;
-  int va[4];  // LDS byte offset of this lane's A operand for k-step s, 32-row block 0
+    vw[s] = KIND == kW8 ? ((ch32 >> 4) * 8 + chunk32(s, h)) * 256 + (ch32 & 15) * 16
+                        : (((ch32 >> 4) * 4 + 2 * (s & 1) + h) * 16 + (ch32 & 15)) * 16;
+  // LDS byte offsets of this lane's operands in stage 0, block 0 (block 1: + 32 rows)
+  int va[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) va[s] = ch32 * 128 + ((chunk32(s, h) ^ swz_a(ch32)) << 4);
-  // (row + 32 has the same swizzle as row, so block 1 is block 0 + 32 * 128.)
-  // byte offset of row ch32's s_a operand within a [stage][slice] operand area (S_A s_a at
-  // + 256 bytes, block 1 at + 2 * 1024 bytes)
-  const int vrp = ((ch32 >> 4) * 64 + (ch32 & 15)) * 16;
-  constexpr int kAStage = kKS * kTileBM * 128, kRStage = kKS * 4 * 64 * 16;  // bytes per stage
-  uint8_t *const abase = &sm.a[0][q][0];
-  uint8_t *const rbase = reinterpret_cast<uint8_t *>(&sm.rp[0][q][0][0][0]);
+  for (int s = 0; s < 4; ++s) va[s] = q * kTileBM * 128 + ch32 * 128 + ((chunk32(s, h) ^ swz_a(ch32)) << 4);
+  const int vr = kRBase + q * kTileBM * 32 + ch32 * 32 + h * 16;
+  uint8_t *const smb = reinterpret_cast<uint8_t *>(&sm);
 
-  // Register ring (raw loaded bits only), two steps deep: slot = step parity.
-  static_assert(SW == 2, "the step loop is unrolled by two");
-  v4i bR[2][NW > 0 ? NW : 1];
-  uint32_t swR[2], zwR[2];
-  uint32_t zpR[2];
+  // Weight ring (raw loaded bits): slot s % kWR holds step s.
+  v4i bR[kWR][NW > 0 ? NW : 1];
+  v3u pwR[kWR];
+  uint32_t zR[kWR];
 
-  // Stage st: the activation tile and the row operands of group g, straight into LDS.
-  auto issue_a = [&](int st, int g) {
+  // Stage s % kSA: the activation tile and the row operands of step s.
+  auto issue_a = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    const int gl = min(kKS * s + q, G - 1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) bload16_lds(ra, abase + st * kAStage + (16 * bi + 8 * i) * 128, vdma[i], g * 128);
-    bload16_lds(rro, rbase + st * kRStage + bi * 1024, vro, g * 2 * p.M * 16);
+    for (int i = 0; i < 2; ++i)
+      bload16_lds(ra, smb + J * kAStage + q * kTileBM * 128 + (16 * bi + 8 * i) * 128, vdma[i], gl * 128);
+    if constexpr (RDMA) bload16_lds(rro, smb + kRBase + J * kRStage + q * kTileBM * 32 + bi * 1024, vro, gl * p.M * 32);
   };
-  // Ring slot j: this wave's weights and scale words of group g.
-  auto issue_w = [&](auto j_c, int g) {
-    constexpr int j = decltype(j_c)::value;
-    if constexpr (KIND != kNone) {
+  // Ring slot s % kWR: this wave's weights and column words of step s.
+  auto issue_w = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    if constexpr (HASW) {
+      const int g = kKS * s + q;
+      const int gl = min(g, G - 1);
 #pragma unroll
-      for (int s = 0; s < NW; ++s) bR[j][s] = bload16(rw, vw[s], g * (KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk));
-      swR[j] = bload4(rpw, vpw, g * (int)kPwChunk);
-      if constexpr (KIND == kW4) zwR[j] = bload4(rpw, vpw + 4, g * (int)kPwChunk);
-      if constexpr (NZ) zpR[j] = bload4(make_rsrc(p.z4, (int64_t)p.nb4 * G * kZ4Chunk), (ch32 >> 3) * 4,
-                                        (int)(((size_t)blk * G + g) * kZ4Chunk));
+      for (int t = 0; t < NW; ++t) bR[J][t] = bload16(rw, vw[t], gl * kWChunk);
+      pwR[J] = bload12(rpw, vpw, min(g, G) * (int)kPwChunk);
+      if constexpr (NZ) zR[J] = bload4(rz, (ch32 >> 3) * 4, gl * (int)kZ4Chunk);
     }
   };
 
-  v16f acc[2] = {v16f{0}, v16f{0}};
-  v16i P1[2] = {v16i{0}, v16i{0}};  // block-1 partials of the even / odd steps
-  uint32_t swprev = 0, zwprev = 0;  // column words of the previous step (0: nothing to fold)
+  v16f acc0 = v16f{0}, acc1 = v16f{0};  // folded products
+  v16f cr0 = v16f{0}, cr1 = v16f{0};    // corrections (matrix cores only)
+  v16i P1 = v16i{0};                    // block 1 partials of the previous step
+  v16f sc1 = v16f{0};                   // and their scale products
+  v16i pinit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) pinit[r] = (kFoldBias && !PARTIALS) ? kBiasBits : 0;
   const int jp = blk * 32 + ch32;
 
-  // The row operands (s_a and S_A s_a pieces) of one 32-row block of stage st.
-  auto load_rows = [&](int rb, int st, v4i &rs, v4i &ru) {
-    const uint8_t *o = rbase + st * kRStage + vrp + rb * 2048;
-    rs = *reinterpret_cast<const v4i *>(o);
-    if constexpr (KIND == kW4) ru = *reinterpret_cast<const v4i *>(o + 256);
-  };
-  // Scale products of one 32-row block on the matrix cores (row operand rs, column word
-  // sw).  The column words are zero in the second half-wave (its k slots must add
-  // nothing) and for a step that folds nothing.
-  auto scales = [&](const v4i &rs, uint32_t sw) {
-    return mfma_bf16(rs, v4i{(int)sw, (int)sw, (int)sw, (int)sw}, v16f{0});
-  };
-  // acc[rb] += float(P) * scale, then (4-bit blocks) the zero-point term.
-  auto fold = [&](int rb, const v16i &Pp, const v16f &sc, const v4i &ru, uint32_t zw) {
+  auto load_a = [&](auto j_c, int rb, v4i (&av)[4]) {
+    constexpr int J = decltype(j_c)::value;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[rb][r] = fmaf((float)Pp[r], sc[r], acc[rb][r]);
-    if constexpr (KIND == kW4) acc[rb] = mfma_bf16(ru, v4i{(int)zw, (int)zw, (int)zw, (int)zw}, acc[rb]);
+    for (int k = 0; k < 4; ++k) av[k] = *reinterpret_cast<const v4i *>(smb + va[k] + J * kAStage + rb * 32 * 128);
   };
-
-  // The A operands of one 32-row block of stage st (4 LDS reads, issued together).
-  auto load_a = [&](int st, int rb, v4i (&av)[4]) {
-    const uint8_t *at = abase + st * kAStage + rb * 32 * 128;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) av[k] = *reinterpret_cast<const v4i *>(at + va[k]);
+  auto load_rows = [&](auto j_c, int rb) {
+    constexpr int J = decltype(j_c)::value;
+    return *reinterpret_cast<const v4i *>(smb + vr + J * kRStage + rb * 32 * 32);
   };
-  // The group partial of one 32-row block on the matrix cores.
-  auto block_mma = [&](const v4i (&av)[4], const v4i (&bq)[4]) {
-    v16i P = v16i{0};
+  auto chain = [&](const v4i (&av)[4], const v4i (&bw)[4]) {
+    v16i P = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[0], bw[0], pinit, 0, 0, 0);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) P = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[k], bq[k], P, 0, 0, 0);
+    for (int k = 1; k < 4; ++k) P = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[k], bw[k], P, 0, 0, 0);
     return P;
   };
+  auto fold = [&](v16f &acc, const v16i &P, const v16f &sc) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int pr = P[r];
+      acc[r] = fmaf(kFoldBias ? __int_as_float(pr) : (float)pr, sc[r], acc[r]);
+    }
+  };
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
   // Partials mode: the exact group partials of an active step, zero point removed.
   auto emit = [&](int rb, const v16i &Pc, int g, uint32_t zword) {
@@ -371,133 +376,138 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     }
   };
 
-  // One step s (parity j = s % 2 known at compile time; stage st = s mod kSA).  The
-  // prologue waited for stages 0 .. kD - 1; stage s >= kD was issued at step s - kD, and
-  // the kD - 1 later steps issued L loads each, so "at most (kD - 1) L outstanding" means
-  // stage s has landed.
-  auto step = [&](auto j_c, int s, int st) {
-    constexpr int j = decltype(j_c)::value;
-    wait_vm<(kD - 1) * L>();
+  // One step s: stage J = s % kSA, weight slot J % 2.
+  auto step = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    constexpr int W = J % kWR;
+    if constexpr (PARTIALS)
+      wait_vm<0>();  // the partials' stores count too: wait for everything
+    else
+      wait_vm<WAIT>();
     lds_barrier();
-    // the column words of step s leave the ring slot that the refill below reuses
-    const uint32_t swcur = KIND != kNone ? swR[j] : 0u;
-    const uint32_t zwcur = KIND == kW4 ? zwR[j] : 0u;
-    // Refill (unconditionally, clamped, so every step issues the same loads): stage
-    // s + kD (the slot of step s - 2, read for the last time during step s - 1), and the
-    // weights of step s + 1 (the slot of step s - 1).
-    const int st_next = st + kD >= kSA ? st + kD - kSA : st + kD;
-    issue_a(st_next, grp(s + kD));
-    issue_w(IntC<1 - j>{}, grp(s + 1));
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (KIND != kNone) {
-      // Branch-free: an inactive step (past this slice's range, on clamped data) computes
-      // partials that are never folded (its column words are replaced by zeros).
-      const bool act = gb + s < ge;
-      const uint32_t sw = (act && h == 0) ? swcur : 0u, zw = (act && h == 0) ? zwcur : 0u;
-      v4i bq[4];
+    // Refill the weight slot and the stage of step s - 1 (whose reads all finished before
+    // the barrier): the weights of step s + kWR - 1 and the stage of step s + kSA - 1.
+    issue_w(IntC<(J + kWR - 1) % kWR>{}, s + kWR - 1);
+    issue_a(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1);
+    fence();
+    if constexpr (HASW) {
+      v4i av0[4], av1[4];
+      load_a(j_c, 0, av0);
+      v4i bw[4];
       if constexpr (KIND == kW4) {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const uint32_t x0 = (uint32_t)bR[j][e][2 * u], x1 = (uint32_t)bR[j][e][2 * u + 1];
-            bq[2 * e + u] = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
+            const uint32_t x0 = (uint32_t)bR[W][e][2 * u], x1 = (uint32_t)bR[W][e][2 * u + 1];
+            bw[2 * e + u] = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
                                 (int)((x1 >> 4) & 0x0F0F0F0Fu)};
           }
       } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) bq[k] = bR[j][k];
+        for (int k = 0; k < 4; ++k) bw[k] = bR[W][k];
       }
-      const int st_prev = st == 0 ? kSA - 1 : st - 1;
       if constexpr (PARTIALS) {
-        v4i av[4];
-        load_a(st, 0, av);
-        const v16i P0 = block_mma(av, bq);
-        if (act) emit(0, P0, gb + s, zpR[j]);
-        load_a(st, 1, av);
-        const v16i Pb = block_mma(av, bq);
-        if (act) emit(1, Pb, gb + s, zpR[j]);
+        const int g = kKS * s + q;
+        const v16i P0 = chain(av0, bw);
+        if (g < G) emit(0, P0, g, zR[W]);
+        load_a(j_c, 1, av1);
+        const v16i Pb = chain(av1, bw);
+        if (g < G) emit(1, Pb, g, zR[W]);
       } else {
-        // Block 0 of this step on the matrix cores while block 1 of the previous step
-        // folds, then block 1 of this step while block 0 of this step folds.  Each block's
-        // LDS operand reads are issued together ahead of its matrix-core ops.
-        v4i av[4], rs, ru;
-        load_a(st, 0, av);
-        load_rows(1, st_prev, rs, ru);
-        __builtin_amdgcn_sched_barrier(0);
-        const v16f sc1 = scales(rs, swprev);
-        const v16i P0 = block_mma(av, bq);
-        fold(1, P1[1 - j], sc1, ru, zwprev);
-        load_a(st, 1, av);
-        load_rows(0, st, rs, ru);
-        __builtin_amdgcn_sched_barrier(0);
-        const v16f sc0 = scales(rs, sw);
-        P1[j] = block_mma(av, bq);
-        fold(0, P0, sc0, ru, zw);
+        const v4i r0 = load_rows(j_c, 0), r1 = load_rows(j_c, 1);
+        const int sw = (int)pwR[W].x, zw = (int)pwR[W].y, cw = kFoldBias ? (int)pwR[W].z : 0;
+        const v4i bs = v4i{0, 0, sw, sw}, bc = v4i{zw, zw, cw, cw};
+        if constexpr (PHASE == 0) {
+          // the previous step's block 1 folds while this step's operands arrive
+          fold(acc1, P1, sc1);
+          fence();
+          const v16i P0 = chain(av0, bw);
+          load_a(j_c, 1, av1);
+          const v16f sc0 = mfma_bf16(r0, bs, v16f{0});
+          if constexpr (CORR) cr0 = mfma_bf16(r0, bc, cr0);
+          P1 = chain(av1, bw);
+          fold(acc0, P0, sc0);
+          sc1 = mfma_bf16(r1, bs, v16f{0});
+          if constexpr (CORR) cr1 = mfma_bf16(r1, bc, cr1);
+        } else {
+          // block 0 runs on the matrix cores while the previous block 1 folds
+          const v16i P0 = chain(av0, bw);
+          load_a(j_c, 1, av1);
+          fold(acc1, P1, sc1);
+          const v16f sc0 = mfma_bf16(r0, bs, v16f{0});
+          if constexpr (CORR) cr0 = mfma_bf16(r0, bc, cr0);
+          fence();
+          P1 = chain(av1, bw);
+          fold(acc0, P0, sc0);
+          sc1 = mfma_bf16(r1, bs, v16f{0});
+          if constexpr (CORR) cr1 = mfma_bf16(r1, bc, cr1);
+        }
       }
-      swprev = sw;
-      zwprev = zw;
     }
   };
 
-  // Prologue: stages 0 .. kD - 1 and the weights of step 0, all landed before step 0.
-  for (int st = 0; st < kD; ++st) issue_a(st, grp(st));
-  issue_w(IntC<0>{}, grp(0));
-  wait_vm<0>();
-
-  int s = 0, st = 0;
-  for (; s + 2 <= nsteps; s += 2) {
-    step(IntC<0>{}, s, st);
-    st = st + 1 == kSA ? 0 : st + 1;
-    step(IntC<1>{}, s + 1, st);
-    st = st + 1 == kSA ? 0 : st + 1;
+  // Prologue: the loads of steps 0 .. kSA - 2 in the order the steps issue them.
+  static_assert(kSA == 4, "prologue and loop are written for four stages");
+  if constexpr (kWR == 4) {
+    issue_w(IntC<0>{}, 0);
+    issue_a(IntC<0>{}, 0);
+    issue_w(IntC<1>{}, 1);
+    issue_a(IntC<1>{}, 1);
+    issue_w(IntC<2>{}, 2);
+    issue_a(IntC<2>{}, 2);
+  } else {
+    issue_a(IntC<0>{}, 0);
+    issue_a(IntC<1>{}, 1);
+    issue_w(IntC<0>{}, 0);
+    issue_a(IntC<2>{}, 2);
   }
-  if (s < nsteps) {
-    step(IntC<0>{}, s, st);
-    ++s;
+  for (int it = 0; it < niter; ++it) {
+    const int s = it * kSA;
+    step(IntC<0>{}, s);
+    step(IntC<1>{}, s + 1);
+    step(IntC<2>{}, s + 2);
+    step(IntC<3>{}, s + 3);
   }
-  // Block 1 of the last step still has to fold; its stage is intact (the last refill went
-  // to the slot of step nsteps - 2).
-  if constexpr (!PARTIALS && KIND != kNone) {
-    v4i rs, ru;
-    load_rows(1, (nsteps - 1) % kSA, rs, ru);
-    const v16f sc = scales(rs, swprev);
-    if ((nsteps - 1) & 1)
-      fold(1, P1[1], sc, ru, zwprev);
-    else
-      fold(1, P1[0], sc, ru, zwprev);
+  if constexpr (!PARTIALS && HASW) {
+    fold(acc1, P1, sc1);
+    if constexpr (CORR) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc0[r] += cr0[r];
+        acc1[r] += cr1[r];
+      }
+    }
   }
-  // All direct-to-LDS loads (including the clamped refills) have landed before the
+  // All direct-to-LDS loads (including those past the last step) have landed before the
   // stages' space is reused.
   wait_vm<0>();
   lds_barrier();
   if constexpr (PARTIALS) return;
 
-  // Sum the slices' accumulators in slice order and write the output.
-  float *red = reinterpret_cast<float *>(&sm.a[0][0][0]);
-  if (q > 0) {
+  // Sum the two slices' accumulators and write the output: slice 0 finishes rows 0-31
+  // (block 0) and slice 1 rows 32-63 (block 1), each adding the other slice's partial
+  // sums taken from LDS; both compute slice 0's value + slice 1's value.
+  static_assert(kKS == 2, "the epilogue pairs two slices");
+  float *red = reinterpret_cast<float *>(&sm.a[0][0][0]);  // [block kept by the reader][wave][r][lane]
+  const int give = 1 - q;                                   // the block this wave hands over
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[((((q - 1) * kTileNB + bi) * 2 + rb) * 16 + r) * 64 + lane] = acc[rb][r];
-  }
+  for (int r = 0; r < 16; ++r) red[((give * kTileNB + bi) * 16 + r) * 64 + lane] = q == 0 ? acc1[r] : acc0[r];
   lds_barrier();
-  if (q > 0 || KIND == kNone) return;
+  if (KIND == kNone) return;
+  v16f mine = q == 0 ? acc0 : acc1;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-#pragma unroll
-      for (int qq = 1; qq < kKS; ++qq) acc[rb][r] += red[((((qq - 1) * kTileNB + bi) * 2 + rb) * 16 + r) * 64 + lane];
+  for (int r = 0; r < 16; ++r) {
+    const float other = red[((q * kTileNB + bi) * 16 + r) * 64 + lane];
+    mine[r] = q == 0 ? mine[r] + other : other + mine[r];
+  }
   const int orig = p.idx[jp];
   if (orig < 0) return;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + rb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row < p.M) p.y[(int64_t)row * p.ldy + orig] = f2h(acc[rb][r]);
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + q * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (row < p.M) p.y[(int64_t)row * p.ldy + orig] = f2h(mine[r]);
+  }
 }
 
 template <bool PARTIALS>
@@ -506,12 +516,6 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave: uniform
   const int bi = wave & 3, q = wave >> 2;
-
-  // Zero the operand stages: a fold before the first group reads a stage not loaded yet
-  // (with zero column words, which must meet finite values).
-  for (int e = tid; e < (int)(sizeof(sm.rp) / 16); e += kTileThreads)
-    reinterpret_cast<v4i *>(&sm.rp[0][0][0][0][0])[e] = v4i{0, 0, 0, 0};
-  __syncthreads();
 
   // Workgroup w runs on XCD w % 8.  Give each XCD a contiguous range of tiles, ordered in
   // bands of kBandM M tiles (M tile fastest within a band), so the workgroups an XCD runs
@@ -527,10 +531,20 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
   const int m0 = tm * kTileBM;
   const int blk = tn * kTileNB + bi;
   const int kind = blk >= p.nb ? kNone : (blk < p.nb4 ? kW4 : kW8);
-  switch (kind) {
-    case kW4: tile_body<kW4, PARTIALS>(p, sm, m0, blk, bi, q, lane); break;
-    case kW8: tile_body<kW8, PARTIALS>(p, sm, m0, blk, bi, q, lane); break;
-    default: tile_body<kNone, PARTIALS>(p, sm, m0, blk, bi, q, lane); break;
+  // Waves 0 and 1 of each slice also load the row operand records (32 rows each).
+  constexpr int PH = MIXLLM_TILE_PHASE;
+  if (bi < 2) {
+    switch (kind) {
+      case kW4: tile_body<kW4, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
+      case kW8: tile_body<kW8, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
+      default: tile_body<kNone, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
+    }
+  } else {
+    switch (kind) {
+      case kW4: tile_body<kW4, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
+      case kW8: tile_body<kW8, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
+      default: tile_body<kNone, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
+    }
   }
 }
 
@@ -699,10 +713,11 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
   return pl;
 }
 
-// The tile kernel addresses the row operands with 32-bit offsets (G * M * 32 bytes) and a
-// block's weights likewise (G * 4096).
+// The tile kernel addresses the row operands with 32-bit offsets (G * M * 32 bytes), a
+// block's weights and column words likewise, and an activation tile as 64 rows of K.
 bool tile_offsets_fit(int M, const mixllm_blob_info &L) {
   return (int64_t)L.G * M * 32 <= 0x7FFFFFFF && (int64_t)L.G * (int64_t)kW8Chunk <= 0x7FFFFFFF &&
+         ((int64_t)L.G + 1) * (int64_t)kPwChunk <= 0x7FFFFFFF &&
          (int64_t)kTileBM * L.K + (int64_t)L.G * 128 <= 0x7FFFFFFF;
 }
 

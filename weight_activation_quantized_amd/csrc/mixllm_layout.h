@@ -9,9 +9,10 @@
 //   s8   [nb8][G][32]  fp16 scales of the 8-bit blocks
 //   zp   [32][G]       zero points of the promoted 4-bit channels (unpacking only)
 //   idx  [nb * 32]     int32 original channel index of every packed channel (-1: empty)
-//   pw   [nb][G][32]   two words per channel: the scale s_w and the product -z * s_w, each
-//                      as an exact sum of two bf16 values (low half first); zero for
-//                      8-bit, promoted and empty channels in the second word
+//   pw   [nb][G + 1][32] three words per channel: s_w, -z * s_w and -B * s_w with
+//                      B = 1.5 * 2^23, each as an exact sum of two bf16 values (low half
+//                      first); the second word is zero for 8-bit, promoted and empty
+//                      channels; group G of every block is all zeros
 //
 // Packed channel order: the n4 4-bit channels (ascending original index), then the n8
 // 8-bit channels (ascending), then empty channels up to nb * 32 = 32 ceil(N / 32).
@@ -24,8 +25,10 @@
 // ceil(N / 32): no tile is spent on padding between the two subsets.
 //
 // The pw words feed the matrix-core scale products of the tile kernel directly: s_w (an
-// fp16, at most 11 significant bits) and z * s_w (at most 15) both split exactly into a
-// bf16 holding the leading 8 significant bits plus a bf16 remainder.
+// fp16, at most 11 significant bits), z * s_w (at most 15) and B * s_w (at most 12) all
+// split exactly into a bf16 holding the leading 8 significant bits plus a bf16
+// remainder.  B is the bias of the float-bits integer conversion: the bits of the
+// integer P + 0x4B400000 read as a float are exactly B + P for |P| < 2^22.
 //
 // Inside a 4-bit (block, group) chunk of 2048 B, 16-byte unit u = ((half * 4 + a) * 16 + ch)
 // holds channel 16 * half + ch, k-chunks a (bytes 0..7) and a + 4 (bytes 8..15) of the
@@ -58,7 +61,8 @@ constexpr size_t kW8Chunk = 4096;   // bytes per (block, group), 8-bit part
 constexpr size_t kS4Chunk = 64;     // 32 fp16 scales
 constexpr size_t kZ4Chunk = 16;     // 32 nibbles
 constexpr size_t kS8Chunk = 64;
-constexpr size_t kPwChunk = 256;    // 32 channels x 2 words
+constexpr size_t kPwWords = 3;      // words per channel and group in pw
+constexpr size_t kPwChunk = 32 * kPwWords * 4;  // bytes per (block, group) in pw
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -101,7 +105,7 @@ inline bool compute_layout(int32_t N, int32_t K, int32_t n8, mixllm_blob_info *L
   L->off_idx = off;
   off = align256(off + (size_t)nb * kBlock * 4);
   L->off_pw = off;
-  off = align256(off + (size_t)nb * G * kPwChunk);
+  off = align256(off + (size_t)nb * (G + 1) * kPwChunk);
   L->total_bytes = off;
   return true;
 }

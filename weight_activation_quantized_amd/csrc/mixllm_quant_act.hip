@@ -17,7 +17,8 @@
 // Optionally the kernel also writes the row operands of the GEMM's scale products: s and
 // u = fp32(S_A * s) each as an exact sum of three bf16 values (truncate to bf16, the
 // remainder has at most 16 significant bits, truncate again, the second remainder has
-// at most 8), laid out as the bf16 MFMA row operand [p0 p0 p1 p1 p2 p2 0 0].
+// at most 8), laid out as the two 16-byte halves of a bf16 MFMA row operand (one per
+// half-wave): [u0 u0 u1 u1 s0 s0 s1 s1] and [u2 u2 0 0 s2 s2 0 0].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,6 +30,12 @@ bool is_aligned16(const void *p);
 
 namespace {
 
+#ifndef MIXLLM_QA_PPL
+#define MIXLLM_QA_PPL 1
+#endif
+#ifndef MIXLLM_QA_MAXBLOCKS
+#define MIXLLM_QA_MAXBLOCKS 0x7FFFFFFF
+#endif
 constexpr int kThreads = 256;
 constexpr int kPairsPerBlock = kThreads / 16;
 
@@ -48,30 +55,21 @@ __device__ __forceinline__ int quarter_sum(int v) {
   return v;
 }
 
-// x = p0 + p1 + p2 exactly, each a bf16; returns the row operand words
-// [p0 p0 | p1 p1 | p2 p2 | 0].
-__device__ __forceinline__ uint4 row_operand(float x) {
+// x = p0 + p1 + p2 exactly, each a bf16 (returned as p | p << 16 words).
+__device__ __forceinline__ void split3(float x, uint32_t w[3]) {
   const uint32_t b0 = __float_as_uint(x) & 0xFFFF0000u;
   const float r1 = x - __uint_as_float(b0);
   const uint32_t b1 = __float_as_uint(r1) & 0xFFFF0000u;
   const uint32_t b2 = __float_as_uint(r1 - __uint_as_float(b1)) & 0xFFFF0000u;
-  return make_uint4(b0 | (b0 >> 16), b1 | (b1 >> 16), b2 | (b2 >> 16), 0u);
+  w[0] = b0 | (b0 >> 16);
+  w[1] = b1 | (b1 >> 16);
+  w[2] = b2 | (b2 >> 16);
 }
 
-__global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__restrict__ a, int64_t lda,
-                                                             int32_t M, int32_t K, int8_t *__restrict__ aq,
-                                                             float *__restrict__ sa, int32_t *__restrict__ asum,
-                                                             uint4 *__restrict__ rowop) {
-  const int G = K / MIXLLM_GROUP;
-  const int64_t pair = (int64_t)blockIdx.x * kPairsPerBlock + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  const int64_t npairs = (int64_t)M * G;
-  const bool live = pair < npairs;
-  const int64_t m = live ? pair / G : 0;
-  const int g = live ? (int)(pair - m * G) : 0;
-
-  uint4 raw = make_uint4(0, 0, 0, 0);
-  if (live) raw = *reinterpret_cast<const uint4 *>(a + m * lda + (int64_t)g * MIXLLM_GROUP + sub * 8);
+// One (token, group) pair per 16-lane quarter: load, reduce, quantize, store.
+__device__ __forceinline__ void quant_pair(uint4 raw, bool live, int64_t m, int g, int sub, int32_t M, int32_t K,
+                                           int8_t *__restrict__ aq, float *__restrict__ sa,
+                                           int32_t *__restrict__ asum, uint4 *__restrict__ rowop) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   float x[8];
 #pragma unroll
@@ -108,8 +106,41 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__r
     if (asum) asum[(int64_t)g * M + m] = qsum;
   }
   if (rowop && sub < 2) {
-    const float v = sub == 0 ? s : (float)qsum * s;
-    rowop[((int64_t)g * 2 + sub) * M + m] = row_operand(v);
+    uint32_t ws[3], wu[3];
+    split3(s, ws);
+    split3((float)qsum * s, wu);
+    rowop[((int64_t)g * M + m) * 2 + sub] =
+        sub == 0 ? make_uint4(wu[0], wu[1], ws[0], ws[1]) : make_uint4(wu[2], 0u, ws[2], 0u);
+  }
+}
+
+// Each quarter handles pairs pair0, pair0 + stride, ... with PPL of them in flight.
+template <int PPL>
+__global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__restrict__ a, int64_t lda,
+                                                             int32_t M, int32_t K, int8_t *__restrict__ aq,
+                                                             float *__restrict__ sa, int32_t *__restrict__ asum,
+                                                             uint4 *__restrict__ rowop) {
+  const int G = K / MIXLLM_GROUP;
+  const int sub = threadIdx.x & 15;
+  const int64_t npairs = (int64_t)M * G;
+  const int64_t stride = (int64_t)gridDim.x * kPairsPerBlock;
+  for (int64_t base = (int64_t)blockIdx.x * kPairsPerBlock + (threadIdx.x >> 4); base < npairs;
+       base += stride * PPL) {
+    uint4 raw[PPL];
+    int64_t m[PPL];
+    int g[PPL];
+    bool live[PPL];
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int64_t pair = base + i * stride;
+      live[i] = pair < npairs;
+      m[i] = live[i] ? pair / G : 0;
+      g[i] = live[i] ? (int)(pair - m[i] * G) : 0;
+      raw[i] = make_uint4(0, 0, 0, 0);
+      if (live[i]) raw[i] = *reinterpret_cast<const uint4 *>(a + m[i] * lda + (int64_t)g[i] * MIXLLM_GROUP + sub * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) quant_pair(raw[i], live[i], m[i], g[i], sub, M, K, aq, sa, asum, rowop);
   }
 }
 
@@ -125,9 +156,10 @@ extern "C" int mixllm_quant_act(const uint16_t *a, int64_t lda, int32_t M, int32
       (asum && !mixllm::is_aligned16(asum)) || (rowop && !mixllm::is_aligned16(rowop)))
     return MIXLLM_E_SHAPE;
   const int64_t npairs = (int64_t)M * (K / MIXLLM_GROUP);
-  const int64_t blocks = (npairs + kPairsPerBlock - 1) / kPairsPerBlock;
-  if (blocks > 0x7FFFFFFF) return MIXLLM_E_SHAPE;
-  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a,
+  constexpr int kPPL = MIXLLM_QA_PPL;
+  int64_t blocks = (npairs + kPairsPerBlock * kPPL - 1) / (kPairsPerBlock * kPPL);
+  if (blocks > MIXLLM_QA_MAXBLOCKS) blocks = MIXLLM_QA_MAXBLOCKS;
+  hipLaunchKernelGGL(quant_act_kernel<kPPL>, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a,
                      lda, M, K, aq, sa, asum, reinterpret_cast<uint4 *>(rowop));
   return hipGetLastError() == hipSuccess ? MIXLLM_OK : MIXLLM_E_HIP;
 }

@@ -167,7 +167,7 @@ def _ptr(t):
 
 def mixllm_quant_act(a, aq, sa, asum=None, rowop=None, stream=None):
     """a: fp16 [M, K] CUDA tensor (rows may be strided); aq: int8 [M, K];
-    sa: fp32 [G, M]; asum: int32 [G, M] or None; rowop: 32-bit [G, 2, M, 4] or None."""
+    sa: fp32 [G, M]; asum: int32 [G, M] or None; rowop: 32-bit [G, M, 8] or None."""
     m, k = a.shape
     if a.dtype != torch.float16 or a.stride(1) != 1:
         raise ValueError("a must be fp16 with unit column stride")
@@ -199,8 +199,8 @@ def mixllm_gemm_w4w8a8_partials(aq, sa, asum, rowop, m: int, n: int, k: int, n8:
 
 
 def rowop_buffer(m: int, k: int, device="cuda"):
-    """Storage for mixllm_quant_act's row operands: 32-bit words [G, 2, M, 4]."""
-    return torch.empty((k // GROUP, 2, m, 4), dtype=torch.int32, device=device)
+    """Storage for mixllm_quant_act's row operands: 32-bit words [G, M, 8]."""
+    return torch.empty((k // GROUP, m, 8), dtype=torch.int32, device=device)
 
 
 # ---------------------------------------------------------------------------- convenience
