@@ -123,6 +123,35 @@ int mixllm_unpack_weights(const void *blob_host, size_t blob_bytes, uint8_t *q, 
                           uint16_t *s_fp16, uint8_t *is8);
 
 /* ------------------------------------------------------------------------------------
+ * Global output-channel precision search (host): the step before packing that decides
+ * which channels get 8 bits (talk notes, グローバル混合精度探索; summary page, 核心方法).
+ *
+ * mixllm_channel_salience: for every output channel n of one layer,
+ *   S_n = (1/D) sum_d | t_dn + t_dn^2 / 2 |,  t_dn = sum_k grads[d][n][k] * delta_n[k],
+ * the loss change of quantizing only channel n by a second-order Taylor expansion with the
+ * Fisher approximation of the Hessian (first-order term kept), where delta_n = c_q - c_0
+ * is the channel dequantized from this library's 4-bit asymmetric group-128 quantizer
+ * minus its fp16 weights.  Computed in fp64.
+ * w_fp16: [N][K] fp16 weights (host).  grads: [D][N][K] fp32 per-sample gradients of the
+ * loss with respect to those weights (host; the caller computes them on a model and
+ * calibration data).  s_out: [N] fp64.  Errors: E_NULL, E_SHAPE (N, K or D <= 0,
+ * K % 128 != 0), E_GROUP.
+ *
+ * mixllm_assign_channels: the pages' Algorithm 1.  scores: the salience of every channel
+ * of L layers, concatenated layer by layer (layer l has layer_n[l] channels).  The T
+ * highest scores over all layers get 8 bits; equal scores go to the lower layer, then the
+ * lower channel, first.  idx8_out: [T] the chosen channels, layer by layer, ascending
+ * within a layer (each layer's run is the idx8 argument of mixllm_pack_weights);
+ * layer_n8_out: [L] how many each layer got.  idx8_out may be NULL when T == 0.  Errors:
+ * E_NULL, E_SHAPE (L <= 0, a layer_n <= 0, T < 0 or above the total, a non-finite score).
+ * ------------------------------------------------------------------------------------ */
+int mixllm_channel_salience(const uint16_t *w_fp16, const float *grads, int32_t N, int32_t K, int32_t group,
+                            int32_t D, double *s_out);
+
+int mixllm_assign_channels(const double *scores, const int32_t *layer_n, int32_t L, int64_t T, int32_t *idx8_out,
+                           int32_t *layer_n8_out);
+
+/* ------------------------------------------------------------------------------------
  * Activation quantization (device).
  *
  * Per token m and group g (talk notes, 設計判断の概要: 8-bit symmetric group-wise RTN

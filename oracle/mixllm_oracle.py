@@ -302,6 +302,53 @@ def partials_python(aq, q, z, group: int = GROUP):
 
 
 # --------------------------------------------------------------------------------------
+# Global output-channel precision search (MixLLM talk notes, グローバル混合精度探索;
+# summary page, 核心方法)
+# --------------------------------------------------------------------------------------
+
+def w4_perturbation(w16: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """c_q - c_0 for every output channel: the channel as the 4-bit asymmetric path stores
+    it, dequantized ((q - z) * s16), minus the original fp16 weights.  fp64, exact."""
+    q, z, s16 = quant_w4_asym(w16, group)
+    n, k = q.shape
+    g = k // group
+    deq = (q.reshape(n, g, group).astype(np.float64) - z[:, :, None].astype(np.float64)) \
+        * s16[:, :, None].astype(np.float64)
+    return deq.reshape(n, k) - np.asarray(w16, np.float16).astype(np.float64)
+
+
+def channel_salience(w16: np.ndarray, grads: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """Salience of each output channel c of one layer: the loss change if only c is
+    quantized, from a second-order Taylor expansion with the Hessian replaced by the
+    empirical Fisher matrix (1/|D|) sum_d g_d g_d^T, which leaves one dot product per
+    calibration sample d and keeps the first-order term:
+
+        S_c = (1/|D|) sum_d | t_d + t_d^2 / 2 |,   t_d = g_d . (c_q - c_0)
+
+    grads: [D, N, K] per-sample gradients of the loss w.r.t. the layer's weights.
+    Returns fp64 [N]."""
+    grads = np.asarray(grads, dtype=np.float32)
+    delta = w4_perturbation(w16, group)
+    t = np.einsum("dnk,nk->dn", grads.astype(np.float64), delta)
+    return np.mean(np.abs(t + 0.5 * t * t), axis=0)
+
+
+def assign_channels(scores, total_8bit: int):
+    """The global assignment: every channel of every layer in one list, ranked by
+    salience descending (ties: lower layer index, then lower channel index, first -- a
+    reading; the pages do not order ties), the first ``total_8bit`` get 8 bits.
+    scores: list of per-layer fp64 arrays.  Returns the per-layer sorted idx8 arrays."""
+    layer = np.concatenate([np.full(len(s), i, np.int64) for i, s in enumerate(scores)])
+    chan = np.concatenate([np.arange(len(s), dtype=np.int64) for s in scores])
+    val = np.concatenate([np.asarray(s, np.float64) for s in scores])
+    if total_8bit < 0 or total_8bit > len(val):
+        raise ValueError("total_8bit out of range")
+    order = np.lexsort((chan, layer, -val))  # last key is the primary one
+    top = order[:total_8bit]
+    return [np.sort(chan[top][layer[top] == i]).astype(np.int32) for i in range(len(scores))]
+
+
+# --------------------------------------------------------------------------------------
 # Fast int-to-float (MixLLM talk notes, 高速 I2F 変換)
 # --------------------------------------------------------------------------------------
 

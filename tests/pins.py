@@ -290,6 +290,72 @@ def pin_fp16_rounding(O):
         assert float(O.to_fp16(np.array([x]))[0]) == want, (x, want)
 
 
+# ------------------------------------------------------------------ global precision search
+
+def _salience_channels():
+    """Three hand-built channels (K = 128) whose 4-bit perturbation is known exactly:
+    channel 0: w[1] = 15/16 sets the scale 1/16 (range [0, 15/16], zero point 0), w[2] =
+    7.25/16 rounds to code 7, so c_q - c_0 is -1/64 at k = 2 and 0 elsewhere;
+    channel 1: all zeros (no perturbation); channel 2: like channel 0."""
+    w = np.zeros((3, G), np.float64)
+    w[0, 1] = w[2, 1] = 15 / 16
+    w[0, 2] = w[2, 2] = 7.25 / 16
+    return w.astype(np.float16)
+
+
+def pin_salience_hand(O):
+    """Salience S_c = (1/|D|) sum_d |t_d + t_d^2 / 2|, t_d = g_d . (c_q - c_0) (talk notes,
+    グローバル混合精度探索), on hand-derived cases.  With c_q - c_0 = -1/64 at one input:
+    gradients 64 and -128 there give t = (-1, 2) and S = (0.5 + 4) / 2 = 2.25; a lone
+    gradient 128 gives t = -2, where the first- and second-order terms cancel: S = 0;
+    inputs where the channel is exactly representable do not matter."""
+    w = _salience_channels()
+    rng = np.random.default_rng(3)
+    g = rng.normal(0, 5, size=(2, 3, G)).astype(np.float32)
+    g[:, 0, 2] = [64.0, -128.0]
+    g[:, 2, 2] = [128.0, 128.0]
+    s = O.channel_salience(w, g)
+    assert s.shape == (3,)
+    assert s[0] == 2.25, s
+    assert s[1] == 0.0, s
+    assert s[2] == 0.0, s
+    # the calibration set enters as a mean: duplicating it changes nothing
+    assert np.array_equal(O.channel_salience(w, np.concatenate([g, g[::-1]])), s)
+
+
+def _best_subset_bruteforce(vals, t):
+    import itertools
+    best, arg = None, None
+    for comb in itertools.combinations(range(len(vals)), t):
+        tot = sum(vals[i] for i in comb)
+        if best is None or tot > best:
+            best, arg = tot, comb
+    return set(arg)
+
+
+def pin_assignment_bruteforce(O):
+    """Algorithm 1 ranks every channel of every layer in one list: for distinct scores the
+    8-bit set of size T is the size-T subset with the largest total salience (brute force
+    over all subsets), whatever the layer sizes; ties go to the lower layer, then the lower
+    channel (the reading taken)."""
+    rng = np.random.default_rng(11)
+    sizes = [2, 3, 4]
+    scores = [rng.permutation(20)[:n].astype(np.float64) * 0.37 + rng.random() for n in sizes]
+    flat = np.concatenate(scores)
+    owner = [(li, c) for li, n in enumerate(sizes) for c in range(n)]
+    for t in range(len(flat) + 1):
+        idx8 = O.assign_channels(scores, t)
+        assert [len(x) for x in idx8] and sum(len(x) for x in idx8) == t
+        got = {owner.index((li, int(c))) for li, x in enumerate(idx8) for c in x}
+        assert got == _best_subset_bruteforce(list(flat), t), t
+        for x in idx8:
+            assert np.all(np.diff(x) > 0)
+    tie = O.assign_channels([np.array([1.0, 2.0]), np.array([2.0, 0.5])], 1)
+    assert [list(x) for x in tie] == [[1], []]
+    tie2 = O.assign_channels([np.array([3.0, 3.0, 1.0])], 1)
+    assert [list(x) for x in tie2] == [[0]]
+
+
 ALL_PINS = [pin_golden_quant_examples, pin_tiny_gemm_golden, pin_fp16_rounding, pin_quant_error_bounds,
             pin_partials_bruteforce, pin_y_vs_dequant, pin_p0_p100_and_disjoint, pin_i2f,
-            pin_byte_model, pin_layer_fractions]
+            pin_byte_model, pin_layer_fractions, pin_salience_hand, pin_assignment_bruteforce]

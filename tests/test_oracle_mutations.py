@@ -156,6 +156,28 @@ def _mixed_with(w4=None, w8=None):
     return quant_weights_mixed
 
 
+def _sal_with(form):
+    def channel_salience(w16, grads, group=128):
+        d = core.w4_perturbation(w16, group)
+        t = np.einsum("dnk,nk->dn", np.asarray(grads, np.float64), d)
+        return form(t)
+    return channel_salience
+
+
+def _assign_ascending(scores, total):
+    return core.assign_channels([-np.asarray(s, np.float64) for s in scores], total)
+
+
+def _assign_per_layer(scores, total):
+    n = sum(len(s) for s in scores)
+    out = []
+    for s in scores:
+        k = int(round(total * len(s) / n))
+        out.append(np.sort(np.argsort(-np.asarray(s))[:k]).astype(np.int32))
+    return out
+
+
+
 MUTANTS = {
     "act_round_half_up": _layer_with(quant_act=_act_round_half_up),
     "act_per_token_scale": _layer_with(quant_act=_act_per_token),
@@ -175,6 +197,13 @@ MUTANTS = {
     "effective_bits_wrong": _ns(effective_bits=_eff_bits_wrong),
     "w4_zero_as_fp16": _ns(weight_footprint=_footprint_fp16_zero),
     "fp16_truncation": _layer_with(to_fp16=_to_fp16_trunc),
+    "salience_first_order_dropped": _ns(channel_salience=_sal_with(lambda t: np.mean(np.abs(0.5 * t * t), axis=0))),
+    "salience_abs_outside": _ns(channel_salience=_sal_with(lambda t: np.mean(np.abs(t) + 0.5 * t * t, axis=0))),
+    "salience_no_half": _ns(channel_salience=_sal_with(lambda t: np.mean(np.abs(t + t * t), axis=0))),
+    "salience_sum_not_mean": _ns(channel_salience=_sal_with(lambda t: np.sum(np.abs(t + 0.5 * t * t), axis=0))),
+    "salience_perturbation_sign": _ns(channel_salience=_sal_with(lambda t: np.mean(np.abs(-t + 0.5 * t * t), axis=0))),
+    "assign_lowest": _ns(assign_channels=_assign_ascending),
+    "assign_per_layer": _ns(assign_channels=_assign_per_layer),
 }
 
 

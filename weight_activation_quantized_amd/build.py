@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmixllm.so")
 
-SOURCES = ["mixllm_pack.cpp", "mixllm_quant_act.hip", "mixllm_gemm.hip"]
+SOURCES = ["mixllm_pack.cpp", "mixllm_assign.cpp", "mixllm_quant_act.hip", "mixllm_gemm.hip"]
 ARCH = os.environ.get("MIXLLM_ARCH", "gfx950")
 
 

@@ -17,12 +17,10 @@
 #include <vector>
 
 #include "mixllm.h"
+#include "mixllm_hostquant.h"
 #include "mixllm_layout.h"
 
-namespace {
-
-using mixllm::kBlock;
-using mixllm::kGroup;
+namespace mixllm {
 
 float f16_to_f32(uint16_t h) {
   const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
@@ -67,7 +65,7 @@ uint16_t f32_to_f16_rne(float f) {
   return sign | (uint16_t)q;
 }
 
-float clampf(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
+static inline float clampf(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // One group of an 8-bit symmetric channel.
 void quant_group_w8(const uint16_t *w, int8_t *q, uint16_t *s16_out) {
@@ -115,6 +113,17 @@ void quant_group_w4(const uint16_t *w, uint8_t *q, uint8_t *z_out, uint16_t *s16
   *z_out = (uint8_t)z;
   *s16_out = s16;
 }
+
+}  // namespace mixllm
+
+namespace {
+
+using mixllm::f16_to_f32;
+using mixllm::f32_to_f16_rne;
+using mixllm::kBlock;
+using mixllm::kGroup;
+using mixllm::quant_group_w4;
+using mixllm::quant_group_w8;
 
 // Position of the byte holding the code of group input k inside a 4-bit unit:
 // returns byte offset within the (block, group) chunk and whether it is the high nibble.

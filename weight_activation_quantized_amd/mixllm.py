@@ -67,6 +67,8 @@ _SIGS = {
     "mixllm_pack_weights": ([_vp, _i32, _i32, _i32, _vp, _i32, _vp, _sz], ctypes.c_int),
     "mixllm_blob_get_info": ([_vp, _sz, ctypes.POINTER(BlobInfo)], ctypes.c_int),
     "mixllm_unpack_weights": ([_vp, _sz, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mixllm_channel_salience": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
+    "mixllm_assign_channels": ([_vp, _vp, _i32, _i64, _vp, _vp], ctypes.c_int),
     "mixllm_quant_act": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mixllm_gemm_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "mixllm_gemm_w4w8a8": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _i64, _vp, _sz, _vp],
@@ -149,6 +151,35 @@ def mixllm_unpack_weights(blob: np.ndarray):
     _check(_lib.mixllm_unpack_weights(b.ctypes.data, b.size, q.ctypes.data, z.ctypes.data,
                                       s.ctypes.data, is8.ctypes.data))
     return q, z, s.view(np.float16), is8.astype(bool)
+
+
+def mixllm_channel_salience(w_fp16: np.ndarray, grads: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """w_fp16: [N, K] fp16; grads: [D, N, K] fp32.  Returns the fp64 salience of each channel."""
+    w = np.ascontiguousarray(w_fp16, dtype=np.float16)
+    g = np.ascontiguousarray(grads, dtype=np.float32)
+    n, k = w.shape
+    if g.ndim != 3 or g.shape[1:] != (n, k):
+        raise ValueError("grads must be [D, N, K]")
+    out = np.zeros(n, np.float64)
+    _check(_lib.mixllm_channel_salience(w.ctypes.data, g.ctypes.data, n, k, group, g.shape[0], out.ctypes.data))
+    return out
+
+
+def mixllm_assign_channels(scores, total_8bit: int):
+    """scores: list of per-layer fp64 arrays.  Returns the per-layer idx8 arrays (int32,
+    ascending) of the global top-``total_8bit`` channels."""
+    per = [np.ascontiguousarray(s, dtype=np.float64).reshape(-1) for s in scores]
+    flat = np.ascontiguousarray(np.concatenate(per)) if per else np.zeros(0)
+    sizes = np.array([len(s) for s in per], np.int32)
+    idx = np.zeros(max(int(total_8bit), 1), np.int32)
+    n8 = np.zeros(max(len(per), 1), np.int32)
+    _check(_lib.mixllm_assign_channels(flat.ctypes.data, sizes.ctypes.data, len(per), int(total_8bit),
+                                       idx.ctypes.data, n8.ctypes.data))
+    out, o = [], 0
+    for c in n8[:len(per)]:
+        out.append(idx[o:o + c].copy())
+        o += int(c)
+    return out
 
 
 # ---------------------------------------------------------------------------- device calls
