@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--k", type=int, default=4096)
     ap.add_argument("--p8", type=float, default=0.10)
+    ap.add_argument("--variant", default="",
+                    help="time a measured variant of the tile GEMM (libmixllm_<name>.so: fold_bias, zero_pre) "
+                         "instead of the library")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB before the steps, as the "
                          "known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
@@ -114,6 +117,9 @@ def main():
 
     import numpy as np
     import torch
+    if args.variant:
+        os.environ["MIXLLM_LIB"] = os.path.join(HERE, "weight_activation_quantized_amd",
+                                                f"libmixllm_{args.variant}.so")
     from weight_activation_quantized_amd import mixllm as L
     from weight_activation_quantized_amd import workloads as WL
 
@@ -208,7 +214,7 @@ def main():
     gemm_tops = ops / (gemm_us * 1e-6) / 1e12
     alg_bytes = algorithmic_bytes(m, n, k, n8)
     gemm_hash = src_hash(GEMM_SRC)
-    traffic = traffic_for(gemm_hash)
+    traffic = None if args.variant else traffic_for(gemm_hash)  # counters were taken on the library
     out = {
         "metric": "W4.4A8 GEMM TOPS at M=512,N=K=4096; % of int8 MFMA peak / HBM BW",
         "value": round(value, 2),
@@ -224,7 +230,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"W4.4A8 mixed linear layer M={m} N={n} K={k} group=128 n8={n8} "
                                f"(p{round(100 * n8 / n)}); step = quant_act + mixed GEMM",
-                   "M": m, "N": n, "K": k, "n8": n8, "group": 128, "rotating_sets": sets},
+                   "M": m, "N": n, "K": k, "n8": n8, "group": 128, "rotating_sets": sets,
+                   "variant": args.variant or None},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": traffic, "kernel": "mixllm_gemm_w4w8a8",

@@ -1,6 +1,15 @@
 """Builds libmixllm.so (HIP kernels for gfx950 + host packer) in-tree.
 
-    python -m weight_activation_quantized_amd.build
+    python -m weight_activation_quantized_amd.build [--variants]
+
+``--variants`` also builds the measured alternatives of the tile GEMM (same C ABI, one
+compile-time switch each) as libmixllm_<name>.so next to the library:
+
+    fold_bias  the float-bits int-to-float conversion with its bias moved onto the matrix
+               cores (one VALU op per folded element instead of two; not exact enough to
+               be the default)
+    zero_pre   4-bit zero points subtracted from the codes before the matrix cores with
+               byte-wise integer ops, instead of the per-group matrix-core correction
 
 Every source is compiled with hipcc for --offload-arch=gfx950 with packed-FP32
 instructions disabled and floating-point contraction off (the kernels write their
@@ -19,6 +28,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmixllm.so")
+
+VARIANTS = {"fold_bias": ("MIXLLM_FOLD_BIAS=1",), "zero_pre": ("MIXLLM_ZERO_PRE=1",)}
 
 SOURCES = ["mixllm_pack.cpp", "mixllm_assign.cpp", "mixllm_quant_act.hip", "mixllm_gemm.hip"]
 ARCH = os.environ.get("MIXLLM_ARCH", "gfx950")
@@ -60,6 +71,14 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+def variant_path(name: str) -> str:
+    return os.path.join(HERE, f"libmixllm_{name}.so")
+
+
+def build_variants(verbose: bool = False):
+    return [build(verbose, variant_path(name), defs) for name, defs in VARIANTS.items()]
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -74,3 +93,6 @@ def _run(cmd, verbose):
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    if "--variants" in sys.argv:
+        for path in build_variants(verbose="-v" in sys.argv):
+            print(path)

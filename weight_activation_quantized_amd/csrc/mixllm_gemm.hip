@@ -175,6 +175,12 @@ static_assert(kWR == 2 || kWR == 4, "weight ring");
 #ifndef MIXLLM_TILE_PHASE
 #define MIXLLM_TILE_PHASE 1
 #endif
+#ifndef MIXLLM_ZERO_PRE
+#define MIXLLM_ZERO_PRE 0
+#endif
+// Variant: subtract 4-bit zero points from the codes (byte-wise) before the matrix cores
+// instead of the matrix-core correction per group and block (a measured ablation).
+constexpr bool kZeroPre = MIXLLM_ZERO_PRE != 0;
 #ifndef MIXLLM_FOLD_BIAS
 #define MIXLLM_FOLD_BIAS 0
 #endif
@@ -255,7 +261,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
                                           int lane) {
   constexpr bool HASW = KIND != kNone;
   constexpr int NW = KIND == kW8 ? 4 : (KIND == kW4 ? 2 : 0);     // 16-byte weight loads per step
-  constexpr int NZ = (PARTIALS && KIND == kW4) ? 1 : 0;           // zero-point word (partials)
+  // Zero-point word: partials mode, and the variant that subtracts the zero point from
+  // the codes before the matrix cores.
+  constexpr bool ZPRE = kZeroPre && !PARTIALS && KIND == kW4;
+  constexpr int NZ = ((PARTIALS && KIND == kW4) || ZPRE) ? 1 : 0;
   constexpr int LD = RDMA ? 3 : 2;                                // direct-to-LDS loads per step
   constexpr int LW = HASW ? NW + 1 + NZ : 0;                      // weight-ring loads per step
   // Loads that may still be outstanding when a step's loads have landed.  Ring of four:
@@ -263,7 +272,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   // two later steps.  Ring of two: the weights are issued one step ahead, so the stage
   // batch of the previous step (or, for a wave without weights, of the two previous).
   constexpr int WAIT = kWR == 4 ? 2 * (LW + LD) : (HASW ? LD : 2 * LD);
-  constexpr bool CORR = KIND == kW4 || (kFoldBias && KIND == kW8);
+  constexpr bool CORR = (KIND == kW4 && !ZPRE) || (kFoldBias && KIND != kNone);
   const int ch32 = lane & 31, h = lane >> 5;
   const int G = p.G;
   const int nsteps = (G + kKS - 1) / kKS;                          // same for every wave
@@ -328,7 +337,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   };
 
   v16f acc0 = v16f{0}, acc1 = v16f{0};  // folded products
-  v16f cr0 = v16f{0}, cr1 = v16f{0};    // corrections (matrix cores only)
+  // Corrections: a separate accumulator that only the matrix cores touch, except in the
+  // bias fold, which is short of registers and adds them to the folded sums directly.
+  constexpr bool SEPCORR = !kFoldBias;
+  v16f cr0 = v16f{0}, cr1 = v16f{0};
   v16i P1 = v16i{0};                    // block 1 partials of the previous step
   v16f sc1 = v16f{0};                   // and their scale products
   v16i pinit;
@@ -400,8 +412,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const uint32_t x0 = (uint32_t)bR[W][e][2 * u], x1 = (uint32_t)bR[W][e][2 * u + 1];
-            bw[2 * e + u] = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
-                                (int)((x1 >> 4) & 0x0F0F0F0Fu)};
+            if constexpr (ZPRE) {
+              // (q - z) per byte before the matrix cores (the pages' vsub4 role)
+              const uint32_t zz = ((zR[W] >> ((ch32 & 7) * 4)) & 15u) * 0x01010101u;
+              bw[2 * e + u] = w4_operand(x0, x1, zz);
+            } else {
+              bw[2 * e + u] = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
+                                  (int)((x1 >> 4) & 0x0F0F0F0Fu)};
+            }
           }
       } else {
 #pragma unroll
@@ -416,7 +434,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
         if (g < G) emit(1, Pb, g, zR[W]);
       } else {
         const v4i r0 = load_rows(j_c, 0), r1 = load_rows(j_c, 1);
-        const int sw = (int)pwR[W].x, zw = (int)pwR[W].y, cw = kFoldBias ? (int)pwR[W].z : 0;
+        const int sw = (int)pwR[W].x, zw = ZPRE ? 0 : (int)pwR[W].y, cw = kFoldBias ? (int)pwR[W].z : 0;
         const v4i bs = v4i{0, 0, sw, sw}, bc = v4i{zw, zw, cw, cw};
         if constexpr (PHASE == 0) {
           // the previous step's block 1 folds while this step's operands arrive
@@ -425,23 +443,27 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
           const v16i P0 = chain(av0, bw);
           load_a(j_c, 1, av1);
           const v16f sc0 = mfma_bf16(r0, bs, v16f{0});
-          if constexpr (CORR) cr0 = mfma_bf16(r0, bc, cr0);
+          if constexpr (CORR && SEPCORR) cr0 = mfma_bf16(r0, bc, cr0);
+          if constexpr (CORR && !SEPCORR) acc0 = mfma_bf16(r0, bc, acc0);
           P1 = chain(av1, bw);
           fold(acc0, P0, sc0);
           sc1 = mfma_bf16(r1, bs, v16f{0});
-          if constexpr (CORR) cr1 = mfma_bf16(r1, bc, cr1);
+          if constexpr (CORR && SEPCORR) cr1 = mfma_bf16(r1, bc, cr1);
+          if constexpr (CORR && !SEPCORR) acc1 = mfma_bf16(r1, bc, acc1);
         } else {
           // block 0 runs on the matrix cores while the previous block 1 folds
           const v16i P0 = chain(av0, bw);
           load_a(j_c, 1, av1);
           fold(acc1, P1, sc1);
           const v16f sc0 = mfma_bf16(r0, bs, v16f{0});
-          if constexpr (CORR) cr0 = mfma_bf16(r0, bc, cr0);
+          if constexpr (CORR && SEPCORR) cr0 = mfma_bf16(r0, bc, cr0);
+          if constexpr (CORR && !SEPCORR) acc0 = mfma_bf16(r0, bc, acc0);
           fence();
           P1 = chain(av1, bw);
           fold(acc0, P0, sc0);
           sc1 = mfma_bf16(r1, bs, v16f{0});
-          if constexpr (CORR) cr1 = mfma_bf16(r1, bc, cr1);
+          if constexpr (CORR && SEPCORR) cr1 = mfma_bf16(r1, bc, cr1);
+          if constexpr (CORR && !SEPCORR) acc1 = mfma_bf16(r1, bc, acc1);
         }
       }
     }
@@ -471,7 +493,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   }
   if constexpr (!PARTIALS && HASW) {
     fold(acc1, P1, sc1);
-    if constexpr (CORR) {
+    if constexpr (CORR && SEPCORR) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         acc0[r] += cr0[r];

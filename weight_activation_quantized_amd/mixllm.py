@@ -28,6 +28,7 @@ if not os.path.exists(LIB_PATH):
         "(there is no fallback implementation)")
 
 _lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+_variants = {}
 
 
 def hip_runtimes_loaded():
@@ -76,10 +77,28 @@ _SIGS = {
     "mixllm_gemm_w4w8a8_partials": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp,
                                      _vp], ctypes.c_int),
 }
-for _name, (_args, _res) in _SIGS.items():
-    _fn = getattr(_lib, _name)
-    _fn.argtypes = _args
-    _fn.restype = _res
+def _bind(lib):
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_bind(_lib)
+
+
+def load_variant(name: str):
+    """A measured variant of the library (libmixllm_<name>.so, built by
+    ``python -m weight_activation_quantized_amd.build --variants``), loaded beside the
+    main one with its symbols kept local.  Pass it as ``lib=`` to the device calls."""
+    if name not in _variants:
+        path = os.path.join(HERE, f"libmixllm_{name}.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
+                              "`python -m weight_activation_quantized_amd.build --variants`")
+        _variants[name] = _bind(ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL))
+    return _variants[name]
 
 STATUS = {0: "MIXLLM_OK", -1: "MIXLLM_E_NULL", -2: "MIXLLM_E_SHAPE", -3: "MIXLLM_E_GROUP",
           -4: "MIXLLM_E_INDEX", -5: "MIXLLM_E_SPACE", -6: "MIXLLM_E_FORMAT", -7: "MIXLLM_E_HIP"}
@@ -196,15 +215,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def mixllm_quant_act(a, aq, sa, asum=None, rowop=None, stream=None):
+def mixllm_quant_act(a, aq, sa, asum=None, rowop=None, stream=None, lib=None):
     """a: fp16 [M, K] CUDA tensor (rows may be strided); aq: int8 [M, K];
     sa: fp32 [G, M]; asum: int32 [G, M] or None; rowop: 32-bit [G, M, 8] or None."""
     m, k = a.shape
     if a.dtype != torch.float16 or a.stride(1) != 1:
         raise ValueError("a must be fp16 with unit column stride")
     lda = a.stride(0) if m > 1 else k
-    _check(_lib.mixllm_quant_act(_ptr(a), lda, m, k, GROUP, _ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop),
-                                 _stream(stream)))
+    _check((lib or _lib).mixllm_quant_act(_ptr(a), lda, m, k, GROUP, _ptr(aq), _ptr(sa), _ptr(asum),
+                                          _ptr(rowop), _stream(stream)))
 
 
 def mixllm_gemm_workspace_bytes(m: int, n: int, k: int, n8: int) -> int:
@@ -212,21 +231,22 @@ def mixllm_gemm_workspace_bytes(m: int, n: int, k: int, n8: int) -> int:
 
 
 def mixllm_gemm_w4w8a8(aq, sa, asum, rowop, m: int, n: int, k: int, n8: int, blob_dev, y, workspace=None,
-                       stream=None):
+                       stream=None, lib=None):
     """aq, sa, asum, rowop: outputs of mixllm_quant_act; y: fp16 [M, ldy] CUDA tensor;
     blob_dev: uint8 CUDA tensor holding the packed blob."""
     ldy = y.stride(0) if y.dim() == 2 and m > 1 else n
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.mixllm_gemm_w4w8a8(_ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop), m, n, k, n8, _ptr(blob_dev),
-                                   blob_dev.numel(), _ptr(y), ldy, _ptr(workspace), ws, _stream(stream)))
+    _check((lib or _lib).mixllm_gemm_w4w8a8(_ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop), m, n, k, n8,
+                                            _ptr(blob_dev), blob_dev.numel(), _ptr(y), ldy, _ptr(workspace), ws,
+                                            _stream(stream)))
 
 
 def mixllm_gemm_w4w8a8_partials(aq, sa, asum, rowop, m: int, n: int, k: int, n8: int, blob_dev, n_begin: int,
-                                n_count: int, part, stream=None):
+                                n_count: int, part, stream=None, lib=None):
     """part: int32 [M, n_count, G] CUDA tensor."""
-    _check(_lib.mixllm_gemm_w4w8a8_partials(_ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop), m, n, k, n8,
-                                            _ptr(blob_dev), blob_dev.numel(), n_begin, n_count, _ptr(part),
-                                            _stream(stream)))
+    _check((lib or _lib).mixllm_gemm_w4w8a8_partials(_ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop), m, n, k, n8,
+                                                     _ptr(blob_dev), blob_dev.numel(), n_begin, n_count,
+                                                     _ptr(part), _stream(stream)))
 
 
 def rowop_buffer(m: int, k: int, device="cuda"):
