@@ -153,6 +153,23 @@ def test_gemm_full_compare(L, m, n, k, n8):
     assert np.array_equal(part.cpu().numpy().astype(np.int64), U.partials_at(ref))
 
 
+@pytest.mark.parametrize("m,n,k,n8,ldy_pad", [(130, 96, 256, 0, 0), (100, 200, 384, 200, 0), (65, 4100, 256, 0, 4),
+                                              (129, 136, 512, 136, 8), (70, 100, 128, 0, 4), (80, 64, 256, 64, 3)])
+def test_gemm_pure_paths(L, m, n, k, n8, ldy_pad):
+    """All channels 4-bit (p0) or all 8-bit (p100): no scatter, 16-byte output stores when
+    the output rows allow them (row stride a multiple of 8), including a partial last run
+    of channels; a row stride that does not allow them takes the scatter path."""
+    sh = WL.Shape(0, "edge", m, n, k, n8)
+    a16, w16, idx8 = WL.make_layer_inputs(sh)
+    U.say("gemm pure", sh.name, "ldy", n + ldy_pad)
+    blob, qa, y = _run_gemm(L, a16, w16, idx8, ldy_pad=ldy_pad)
+    torch.cuda.synchronize()
+    ref = U.oracle_at(a16, w16, idx8)
+    yg = y.cpu().numpy()
+    assert np.all(np.isnan(yg[:, n:].astype(np.float32))), "wrote outside [0, N)"
+    U.assert_y_close(yg[:, :n], ref["y16"], sh.name)
+
+
 @pytest.mark.parametrize("m,n,k,n8", [(128, 256, 1024, 26), (512, 4096, 4096, 410), (65, 4100, 256, 500),
                                     (192, 384, 128, 40)])
 def test_gemm_repeat_deterministic(L, m, n, k, n8):

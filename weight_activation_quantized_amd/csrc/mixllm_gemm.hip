@@ -72,6 +72,8 @@ struct GemmArgs {
   int32_t *part;  // partials mode output [M][n_count][G]
   int n_begin, n_count;
   int tiles_m, tiles_n;
+  int spread;  // tile kernel: the grid fits the device at once (one workgroup per CU)
+  int ident;   // tile kernel: packed channel j is original channel j, and y takes 16-byte stores
 };
 
 __device__ __forceinline__ float h2f(uint16_t bits) { return (float)__builtin_bit_cast(_Float16, bits); }
@@ -200,7 +202,8 @@ constexpr int kAStage = kKS * kTileBM * 128;        // bytes per activation stag
 constexpr int kRBase = kSA * kAStage;               // offset of the row operand stages
 constexpr int kRStage = kKS * kTileBM * 32;
 static_assert(offsetof(TileSmem, r) == kRBase, "LDS layout");
-static_assert(kKS * kTileNB * 16 * 64 * 4 <= (int)sizeof(TileSmem::a), "reduction space");
+static_assert(kKS * kTileNB * 16 * 64 * 4 + kKS * kTileNB * 32 * 32 * 2 <= (int)sizeof(TileSmem::a),
+              "reduction and output staging space");
 
 __device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
@@ -523,6 +526,31 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     const float other = red[((q * kTileNB + bi) * 16 + r) * 64 + lane];
     mine[r] = q == 0 ? mine[r] + other : other + mine[r];
   }
+  if (p.ident) {
+    // Channels in original order (all 4-bit or all 8-bit): no scatter.  The wave's
+    // 32 x 32 block goes through LDS row-major, then out as 16-byte runs of 8 channels.
+    uint16_t *st = reinterpret_cast<uint16_t *>(&sm.a[0][0][0] + kKS * kTileNB * 16 * 64 * 4) +
+                   (q * kTileNB + bi) * 32 * 32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[(8 * (r >> 2) + 4 * h + (r & 3)) * 32 + ch32] = f2h(mine[r]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = i * 16 + (lane >> 2), c8 = (lane & 3) * 8;
+      const uint4 v = *reinterpret_cast<const uint4 *>(st + row * 32 + c8);
+      const int grow = m0 + q * 32 + row, col = blk * 32 + c8;
+      if (grow >= p.M) continue;
+      uint16_t *dst = p.y + (int64_t)grow * p.ldy + col;
+      if (col + 8 <= p.N) {
+        *reinterpret_cast<uint4 *>(dst) = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < p.N) dst[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+      }
+    }
+    return;
+  }
   const int orig = p.idx[jp];
   if (orig < 0) return;
 #pragma unroll
@@ -549,7 +577,12 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
   const int t = xcd * per + (xcd < rem ? xcd : rem) + i;
   const int band = t / (kBandM * p.tiles_n), in_band = t - band * (kBandM * p.tiles_n);
   const int bm = min(kBandM, p.tiles_m - band * kBandM);  // M tiles in this band
-  const int tm = band * kBandM + in_band % bm, tn = in_band / bm;
+  const int tm = band * kBandM + in_band % bm, tr = in_band / bm;
+  // When the whole grid runs at once, N tiles go in a stride-8 order so that the XCDs
+  // sharing a band each get some of the 8-bit blocks (the last N tiles) instead of one
+  // XCD getting all of them; in longer grids the contiguous order streams the weights
+  // better.
+  const int tn = (!p.spread || (p.tiles_n & 7)) ? tr : (tr & 7) * (p.tiles_n >> 3) + (tr >> 3);
   const int m0 = tm * kTileBM;
   const int blk = tn * kTileNB + bi;
   const int kind = blk >= p.nb ? kNone : (blk < p.nb4 ? kW4 : kW8);
@@ -709,6 +742,21 @@ void fill_args(GemmArgs &a, const int8_t *aq, const float *sa, const int32_t *as
   a.n_begin = 0;
   a.n_count = 0;
   a.tiles_m = a.tiles_n = 0;
+  a.spread = 0;
+  a.ident = 0;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = v;
+  }
+  return cus[dev];
 }
 
 // Launch plan of one GEMM call, a pure function of the shape.
@@ -760,6 +808,7 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
     a.tiles_n = pl.tiles_n;
     const int64_t T = (int64_t)a.tiles_m * a.tiles_n;
     if (T > 0x7FFFFFFF) return MIXLLM_E_SHAPE;
+    a.spread = T <= device_cus() ? 1 : 0;
     hipLaunchKernelGGL((gemm_tile_kernel<PARTIALS>), dim3((unsigned)T), dim3(kTileThreads), 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? MIXLLM_OK : MIXLLM_E_HIP;
@@ -792,6 +841,8 @@ extern "C" int mixllm_gemm_w4w8a8(const int8_t *aq, const float *sa, const int32
   fill_args(a, aq, sa, asum, rowop, M, blob, L);
   a.y = y;
   a.ldy = ldy;
+  // All channels of one kind: the packed order is the original order.
+  a.ident = (L.n8 == 0 || L.n8 == L.N) && ldy % 8 == 0 && is_aligned16(y) ? 1 : 0;
   return launch<false>(a, pl, (hipStream_t)stream);
 }
 
