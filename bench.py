@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--k", type=int, default=4096)
     ap.add_argument("--p8", type=float, default=0.10)
+    ap.add_argument("--workload", default="layer", choices=["layer", "mlp"],
+                    help="layer: the W4.4A8 layer step (default); mlp: the Llama-3.1-8B MLP block "
+                         "(quantize, gate/up GEMM, SiLU*up + quantize, down GEMM) replayed as a HIP graph")
     ap.add_argument("--variant", default="",
                     help="time a measured variant of the tile GEMM (libmixllm_<name>.so: fold_bias, zero_pre) "
                          "instead of the library")
@@ -108,12 +111,81 @@ def cpu_baseline(m, n, k, n8):
                       f"two-step GEMM), M={m} N={n} K={k} n8={n8}, {dt:.2f} s"}
 
 
+def mlp_main(args):
+    """The Llama-3.1-8B MLP block at M tokens as a second workload: four launches per
+    block captured in one HIP graph per rotating set; a step is one graph replay."""
+    import numpy as np
+    import torch
+    from weight_activation_quantized_amd import mixllm as L
+    from weight_activation_quantized_amd import workloads as WL
+
+    m = args.m
+    hidden, inter = WL.MLP8B["hidden"], WL.MLP8B["inter"]
+    n8 = WL.llama8b_n8()
+    torch.cuda.set_device(0)
+    x16, wg, wu, wd, ig, iu, idn = WL.mlp_block_inputs(m, hidden, inter, n8)
+    blk0 = L.MLPBlock(wg, wu, wd, ig, iu, idn)
+    set_bytes = blk0.gu.blob.numel() + blk0.down.blob.numel() + m * (hidden + 2 * inter) * 6
+    sets = args.sets or max(2, int(np.ceil(512e6 / set_bytes)))
+    blocks = [blk0] + [L.MLPBlock(wg, wu, wd, ig, iu, idn) for _ in range(sets - 1)]
+    xs = [torch.from_numpy(x16).cuda() for _ in range(sets)]
+    bufs = [b.buffers(m) for b in blocks]
+    graphs = [b.capture(x, bb) for b, x, bb in zip(blocks, xs, bufs)]
+    for i in range(args.warmup):
+        graphs[i % sets].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(SPIN_CYCLES)
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % sets].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / args.steps
+    # the same blocks launched eagerly, for comparison
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        blocks[i % sets].forward(xs[i % sets], bufs[i % sets], stream)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)
+    e0.record()
+    for i in range(args.steps):
+        blocks[i % sets].forward(xs[i % sets], bufs[i % sets], stream)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    ops = 2.0 * m * 3 * inter * hidden
+    out = {
+        "metric": "Llama-3.1-8B MLP block TOPS (W4.4A8, HIP graph)",
+        "value": round(ops / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"Llama-3.1-8B MLP block M={m} hidden={hidden} inter={inter}: quant_act, "
+                               f"gate/up GEMM (N={2 * inter}), SiLU*up + quant, down GEMM; 8-bit channels "
+                               f"gate {n8['gate']}, up {n8['up']}, down {n8['down']}",
+                   "M": m, "hidden": hidden, "inter": inter, "rotating_sets": sets},
+        "eager_ms_per_step": round(eager_ms, 5),
+        "eager_tops": round(ops / (eager_ms * 1e-3) / 1e12, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                           "(the sharding design is described in DESIGN.md)"}))
         sys.exit(2)
+    if args.workload == "mlp":
+        return mlp_main(args)
 
     import numpy as np
     import torch

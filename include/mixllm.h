@@ -176,6 +176,26 @@ int mixllm_quant_act(const uint16_t *a_fp16_dev, int64_t lda, int32_t M, int32_t
                      int8_t *aq_dev, float *sa_dev, int32_t *asum_dev, uint32_t *rowop_dev, void *stream);
 
 /* ------------------------------------------------------------------------------------
+ * Llama MLP activation fused with the down projection's activation quantization (device).
+ *
+ * The step between the gate/up and down projections of the Llama MLP blocks whose layer
+ * shapes the pages time (talk notes, A100 GPU でのシステム性能; the activation itself is
+ * the standard Llama one, not described on the pages): h = SiLU(gate) * up with
+ * SiLU(x) = x / (1 + e^-x), computed in fp32 and rounded once to fp16 (nearest even), then
+ * quantized for the down projection exactly as mixllm_quant_act quantizes an fp16 input
+ * (the outputs equal mixllm_quant_act applied to h).
+ *
+ * gate_dev, up_dev: fp16 [M][ld] each (for one GEMM over the packed gate ∪ up channels,
+ *                   up_dev = gate_dev + I and ld = 2 I); ld >= I, ld % 8 == 0.
+ * aq_dev, sa_dev, asum_dev, rowop_dev: as mixllm_quant_act with K = I.
+ * h_dev:            fp16 [M][I] copy of h, or NULL to skip.
+ * Errors: E_NULL, E_SHAPE, E_GROUP, E_HIP.
+ * ------------------------------------------------------------------------------------ */
+int mixllm_silu_mul_quant(const uint16_t *gate_dev, const uint16_t *up_dev, int64_t ld, int32_t M, int32_t I,
+                          int32_t group, int8_t *aq_dev, float *sa_dev, int32_t *asum_dev, uint32_t *rowop_dev,
+                          uint16_t *h_dev, void *stream);
+
+/* ------------------------------------------------------------------------------------
  * Mixed W4/W8 x A8 GEMM with scatter epilogue (device).
  *
  * Two-step dequantization (talk notes, 二段階逆量子化): for each group, the exact

@@ -239,6 +239,39 @@ def layer_forward(a16: np.ndarray, w16: np.ndarray, idx8, group: int = GROUP):
 
 
 # --------------------------------------------------------------------------------------
+# The Llama MLP block around the layer (the gate/up and down projections whose shapes
+# the talk notes time, A100 GPU でのシステム性能; the activation between them is the
+# standard Llama one, SiLU(gate) * up, which the pages do not describe)
+# --------------------------------------------------------------------------------------
+
+def silu(x64: np.ndarray) -> np.ndarray:
+    """SiLU(x) = x / (1 + e^-x) in fp64."""
+    x = np.asarray(x64, np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def silu_mul_fp16(g16: np.ndarray, u16: np.ndarray) -> np.ndarray:
+    """h = SiLU(gate) * up from fp16 inputs, in fp64, rounded once to fp16."""
+    return to_fp16(silu(np.asarray(g16, np.float16).astype(np.float64))
+                   * np.asarray(u16, np.float16).astype(np.float64))
+
+
+def mlp_block_forward(x16, w_gate, w_up, w_down, idx8_gate, idx8_up, idx8_down, group: int = GROUP):
+    """quantize x -> gate and up projections (one layer over the gate and up channels;
+    columns are independent, so this equals the two layers) -> h = SiLU(gate) * up in
+    fp16 -> quantize h -> down projection.  Returns a dict with the fp16 gate/up output,
+    h and the block output."""
+    inter = np.asarray(w_gate).shape[0]
+    w_gu = np.concatenate([np.asarray(w_gate, np.float16), np.asarray(w_up, np.float16)])
+    idx_gu = np.concatenate([np.asarray(idx8_gate, np.int64), np.asarray(idx8_up, np.int64) + inter])
+    gu = layer_forward(x16, w_gu, idx_gu, group)
+    h16 = silu_mul_fp16(gu["y16"][:, :inter], gu["y16"][:, inter:])
+    dn = layer_forward(h16, w_down, idx8_down, group)
+    return dict(gu16=gu["y16"], h16=h16, y16=dn["y16"], y64=dn["y64"], down=dn)
+
+
+# --------------------------------------------------------------------------------------
 # Uniform-precision layers, written separately (p0 = pure W4A8, p100 = pure W8A8)
 # --------------------------------------------------------------------------------------
 

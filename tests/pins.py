@@ -356,6 +356,32 @@ def pin_assignment_bruteforce(O):
     assert [list(x) for x in tie2] == [[0]]
 
 
+# ------------------------------------------------------------------ the MLP block around the layer
+
+def pin_silu_mul(O):
+    """SiLU(x) = x / (1 + e^-x): SiLU(x) - SiLU(-x) = x for every x (an identity of the
+    definition, independent of how it is evaluated); SiLU(0) = 0; the hand value
+    SiLU(2) * 3 = 6 / (1 + e^-2) = 5.2847824..., which rounds to the fp16 5.28515625
+    (spacing 2^-8 in [4, 8): 5.2847824 / 2^-8 = 1352.9 -> 1353); saturation for large |x|."""
+    x = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, rtol=0, atol=1e-12)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    e_minus_2 = 0.1353352832366127  # e^-2
+    assert abs(O.silu(np.array([2.0]))[0] - 2.0 / (1.0 + e_minus_2)) < 1e-14
+    assert abs(O.silu(np.array([-2.0]))[0] + 2.0 * e_minus_2 / (1.0 + e_minus_2)) < 1e-14
+    h = O.silu_mul_fp16(np.array([2.0, 30.0, -30.0, 0.0], np.float16), np.array([3.0, 1.0, 1.0, 5.0], np.float16))
+    assert list(h.astype(np.float64)) == [5.28515625, 30.0, 0.0, 0.0], h
+    # the block's down projection consumes h quantized like any fp16 activation
+    rng = np.random.default_rng(4)
+    g = rng.normal(0, 3, size=(3, 256)).astype(np.float16)
+    u = rng.normal(0, 3, size=(3, 256)).astype(np.float16)
+    h = O.silu_mul_fp16(g, u)
+    assert h.dtype == np.float16
+    want = (g.astype(np.float64) * u.astype(np.float64)) / (1 + np.exp(-g.astype(np.float64)))
+    assert np.all(np.abs(h.astype(np.float64) - want) <= O.ulp_fp16(h) / 2 + 1e-300)
+
+
 ALL_PINS = [pin_golden_quant_examples, pin_tiny_gemm_golden, pin_fp16_rounding, pin_quant_error_bounds,
             pin_partials_bruteforce, pin_y_vs_dequant, pin_p0_p100_and_disjoint, pin_i2f,
-            pin_byte_model, pin_layer_fractions, pin_salience_hand, pin_assignment_bruteforce]
+            pin_byte_model, pin_layer_fractions, pin_salience_hand, pin_assignment_bruteforce,
+            pin_silu_mul]

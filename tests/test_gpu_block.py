@@ -1,0 +1,117 @@
+"""The Llama MLP block around the layer on the GPU, through the C ABI: the fused
+SiLU(gate) * up + quantization kernel, the block's four launches, and its HIP-graph replay.
+
+Each step is compared with the oracle applied to the GPU's own input of that step (the
+steps round to fp16 in between, so this is how a pipeline's parity is checked):
+* mixllm_silu_mul_quant: h within 1 fp16 ulp of the fp64 definition (the GPU evaluates
+  SiLU in fp32 with the library exp), and the int8 codes, scales, code sums and row
+  operands bit-exact to quantizing that h;
+* the gate/up GEMM and the down GEMM: within the layer tolerance;
+* graph replays: bit-identical to the eager forward pass, with other work between replays.
+"""
+import numpy as np
+import pytest
+
+from tests import gpu_util as U
+from weight_activation_quantized_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from weight_activation_quantized_amd import mixllm
+    return mixllm
+
+
+def _check_h_and_codes(h_gpu, ref_h, aq, sa, asum, ro):
+    import oracle as O
+    d = np.abs(h_gpu.astype(np.float64) - ref_h.astype(np.float64))
+    assert np.all(d <= O.ulp_fp16(ref_h)), "h off by more than one fp16 ulp"
+    assert (d == 0).mean() >= 0.999, "h differs from the definition too often"
+    oq, osa, osum = O.quant_act(h_gpu)
+    assert np.array_equal(aq, oq)
+    assert np.array_equal(sa.T.view(np.uint32), osa.view(np.uint32))
+    assert np.array_equal(asum.T, osum)
+    assert np.array_equal(ro, U.rowop_records(osa.T, osum.T.astype(np.float32) * osa.T))
+
+
+@pytest.mark.parametrize("m,inter,ld_extra", [(16, 512, 0), (33, 1408, 8), (130, 384, 384), (1, 128, 0)])
+def test_silu_mul_quant(L, m, inter, ld_extra):
+    import oracle as O
+    g16 = WL.make_acts(m, inter, (21, m, inter))
+    u16 = WL.make_acts(m, inter, (22, m, inter))
+    U.say("silu_mul_quant", m, inter, ld_extra)
+    buf = torch.zeros((m, 2 * inter + ld_extra), dtype=torch.float16, device="cuda")
+    buf[:, :inter] = torch.from_numpy(g16).cuda()
+    buf[:, inter:2 * inter] = torch.from_numpy(u16).cuda()
+    gi = inter // 128
+    aq = torch.empty((m, inter), dtype=torch.int8, device="cuda")
+    sa = torch.empty((gi, m), dtype=torch.float32, device="cuda")
+    asum = torch.empty((gi, m), dtype=torch.int32, device="cuda")
+    ro = L.rowop_buffer(m, inter)
+    h = torch.empty((m, inter), dtype=torch.float16, device="cuda")
+    L.mixllm_silu_mul_quant(buf[:, :inter], buf[:, inter:2 * inter], aq, sa, asum, ro, h)
+    torch.cuda.synchronize()
+    _check_h_and_codes(h.cpu().numpy(), O.silu_mul_fp16(g16, u16), aq.cpu().numpy(), sa.cpu().numpy(),
+                       asum.cpu().numpy(), ro.cpu().numpy().view(np.uint32))
+
+
+def _block(L, m, hidden, inter, n8, seed):
+    x16, wg, wu, wd, ig, iu, idn = WL.mlp_block_inputs(m, hidden, inter, n8, seed)
+    blk = L.MLPBlock(wg, wu, wd, ig, iu, idn)
+    return (x16, wg, wu, wd, ig, iu, idn), blk
+
+
+@pytest.mark.parametrize("m,hidden,inter,n8,rows", [
+    (65, 256, 384, dict(gate=3, up=40, down=130), None),
+    (130, 512, 1408, dict(gate=10, up=141, down=276), None),
+    (512, 4096, 14336, WL.llama8b_n8(), 12),
+])
+def test_mlp_block_chain(L, m, hidden, inter, n8, rows):
+    import oracle as O
+    (x16, wg, wu, wd, ig, iu, idn), blk = _block(L, m, hidden, inter, n8, (31,))
+    U.say("mlp block", m, hidden, inter)
+    x = torch.from_numpy(x16).cuda()
+    bufs = blk.buffers(m)
+    y = blk.forward(x, bufs, keep_h=True)
+    torch.cuda.synchronize()
+    rs = np.arange(m) if rows is None else U.sample_rows(m, np.random.default_rng(5), rows)
+    gu = bufs["x"]["y"].cpu().numpy()[rs]
+    h = bufs["h16"].cpu().numpy()[rs]
+    yg = y.cpu().numpy()[rs]
+    w_gu = np.concatenate([wg, wu])
+    idx_gu = np.concatenate([ig, iu + inter])
+    ref_gu = U.oracle_at(x16[rs], w_gu, idx_gu)
+    U.assert_y_close(gu, ref_gu["y16"], "gate/up")
+    bh = bufs["h"]
+    _check_h_and_codes(h, O.silu_mul_fp16(gu[:, :inter], gu[:, inter:]), bh["aq"].cpu().numpy()[rs],
+                       bh["sa"].cpu().numpy()[:, rs], bh["asum"].cpu().numpy()[:, rs],
+                       bh["rowop"].cpu().numpy().view(np.uint32)[:, rs])
+    ref_dn = U.oracle_at(h, wd, idn)
+    U.assert_y_close(yg, ref_dn["y16"], "down")
+
+
+def test_mlp_block_graph_replays(L):
+    (x16, *_), blk = _block(L, 130, 512, 1408, dict(gate=10, up=141, down=276), (32,))
+    x = torch.from_numpy(x16).cuda()
+    U.say("mlp block graph")
+    eager_bufs = blk.buffers(130)
+    want = blk.forward(x, eager_bufs).clone()
+    torch.cuda.synchronize()
+    bufs = blk.buffers(130)
+    graph = blk.capture(x, bufs)
+    other = torch.randn(1 << 20, device="cuda")
+    for i in range(4):
+        bufs["h"]["y"].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["h"]["y"], want), f"replay {i}"
+        other.mul_(1.0001).add_(1.0)              # eager work between replays
+        blk.forward(x, eager_bufs)                # and an eager pass on other buffers
+        torch.cuda.synchronize()
+        assert torch.equal(eager_bufs["h"]["y"], want)

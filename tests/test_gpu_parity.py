@@ -47,29 +47,6 @@ def _quant(L, a16, lda_pad=0, with_sum=True):
     return aq, sa, asum, rowop
 
 
-def _split3(x32):
-    """Host-side exact three-way bf16 split of fp32 values: the words p | p << 16 of the
-    pieces p0, p1, p2 (uint32), checked to sum to x exactly."""
-    x32 = np.asarray(x32, np.float32)
-    b0 = x32.view(np.uint32) & np.uint32(0xFFFF0000)
-    r1 = (x32 - b0.view(np.float32)).astype(np.float32)
-    b1 = r1.view(np.uint32) & np.uint32(0xFFFF0000)
-    r2 = (r1 - b1.view(np.float32)).astype(np.float32)
-    b2 = r2.view(np.uint32) & np.uint32(0xFFFF0000)
-    tot = b0.view(np.float32).astype(np.float64) + b1.view(np.float32) + b2.view(np.float32)
-    assert np.array_equal(tot, x32.astype(np.float64))
-    return [b | (b >> np.uint32(16)) for b in (b0, b1, b2)]
-
-
-def _rowop_records(sa_gm, u_gm):
-    """The row operand records [G][M][8] of s_a and u = fp32(S_A s_a):
-    {w(u0), w(u1), w(s0), w(s1), w(u2), 0, w(s2), 0}."""
-    s0, s1, s2 = _split3(sa_gm)
-    u0, u1, u2 = _split3(u_gm)
-    z = np.zeros_like(s0)
-    return np.stack([u0, u1, s0, s1, u2, z, s2, z], axis=-1)
-
-
 # --------------------------------------------------------------------------- quant_act
 
 QA_SHAPES = [(16, 1024, "normal"), (1, 128, "normal"), (17, 384, "normal"), (512, 4096, "normal"),
@@ -91,7 +68,7 @@ def test_quant_act_bitexact(L, m, k, dist):
     assert np.array_equal(asum.cpu().numpy().T, osum)
     # row operand records of s_a and fp32(S_A * s_a)
     ro = rowop.cpu().numpy().view(np.uint32)
-    assert np.array_equal(ro, _rowop_records(osa.T, osum.T.astype(np.float32) * osa.T))
+    assert np.array_equal(ro, U.rowop_records(osa.T, osum.T.astype(np.float32) * osa.T))
 
 
 def test_quant_act_golden_ties(L):

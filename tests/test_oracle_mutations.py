@@ -204,6 +204,8 @@ MUTANTS = {
     "salience_perturbation_sign": _ns(channel_salience=_sal_with(lambda t: np.mean(np.abs(-t + 0.5 * t * t), axis=0))),
     "assign_lowest": _ns(assign_channels=_assign_ascending),
     "assign_per_layer": _ns(assign_channels=_assign_per_layer),
+    "silu_sign": _ns(silu=lambda x: np.asarray(x, np.float64) / (1.0 + np.exp(np.asarray(x, np.float64)))),
+    "silu_sigmoid_only": _ns(silu=lambda x: 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64)))),
 }
 
 

@@ -144,6 +144,48 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__r
   }
 }
 
+// The Llama MLP activation between the gate/up and down projections, fused with the
+// down projection's activation quantization: h = SiLU(gate) * up, computed in fp32
+// (SiLU(x) = x / (1 + e^-x), IEEE division, the library exp) and rounded once to fp16,
+// then quantized exactly as quant_act quantizes an fp16 input (same code path), so the
+// outputs equal quant_act applied to h.  Optionally writes h.
+__global__ __launch_bounds__(kThreads) void silu_mul_quant_kernel(const uint16_t *__restrict__ gate,
+                                                                  const uint16_t *__restrict__ up, int64_t ld,
+                                                                  int32_t M, int32_t I, int8_t *__restrict__ aq,
+                                                                  float *__restrict__ sa, int32_t *__restrict__ asum,
+                                                                  uint4 *__restrict__ rowop, uint16_t *__restrict__ h) {
+  const int G = I / MIXLLM_GROUP;
+  const int sub = threadIdx.x & 15;
+  const int64_t npairs = (int64_t)M * G;
+  const int64_t pair = (int64_t)blockIdx.x * kPairsPerBlock + (threadIdx.x >> 4);
+  const bool live = pair < npairs;
+  const int64_t m = live ? pair / G : 0;
+  const int g = live ? (int)(pair - m * G) : 0;
+  uint4 gr = make_uint4(0, 0, 0, 0), ur = make_uint4(0, 0, 0, 0);
+  if (live) {
+    const int64_t off = m * ld + (int64_t)g * MIXLLM_GROUP + sub * 8;
+    gr = *reinterpret_cast<const uint4 *>(gate + off);
+    ur = *reinterpret_cast<const uint4 *>(up + off);
+  }
+  const uint32_t gw[4] = {gr.x, gr.y, gr.z, gr.w}, uw[4] = {ur.x, ur.y, ur.z, ur.w};
+  uint32_t hw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const float gv = h2f((gw[i] >> (16 * half)) & 0xFFFFu), uv = h2f((uw[i] >> (16 * half)) & 0xFFFFu);
+      const float silu = gv / (1.0f + expf(-gv));
+      const float hv = silu * uv;
+      out |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hv) << (16 * half);
+    }
+    hw[i] = out;
+  }
+  const uint4 raw = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  if (live && h) *reinterpret_cast<uint4 *>(h + m * I + (int64_t)g * MIXLLM_GROUP + sub * 8) = raw;
+  quant_pair(raw, live, m, g, sub, M, I, aq, sa, asum, rowop);
+}
+
 }  // namespace
 
 extern "C" int mixllm_quant_act(const uint16_t *a, int64_t lda, int32_t M, int32_t K, int32_t group,
@@ -161,5 +203,24 @@ extern "C" int mixllm_quant_act(const uint16_t *a, int64_t lda, int32_t M, int32
   if (blocks > MIXLLM_QA_MAXBLOCKS) blocks = MIXLLM_QA_MAXBLOCKS;
   hipLaunchKernelGGL(quant_act_kernel<kPPL>, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a,
                      lda, M, K, aq, sa, asum, reinterpret_cast<uint4 *>(rowop));
+  return hipGetLastError() == hipSuccess ? MIXLLM_OK : MIXLLM_E_HIP;
+}
+
+extern "C" int mixllm_silu_mul_quant(const uint16_t *gate, const uint16_t *up, int64_t ld, int32_t M, int32_t I,
+                                     int32_t group, int8_t *aq, float *sa, int32_t *asum, uint32_t *rowop, uint16_t *h,
+                                     void *stream) {
+  if (group != MIXLLM_GROUP) return MIXLLM_E_GROUP;
+  if (M < 0 || I <= 0 || I % MIXLLM_GROUP != 0 || ld < I || ld % 8 != 0) return MIXLLM_E_SHAPE;
+  if (M == 0) return MIXLLM_OK;
+  if (!gate || !up || !aq || !sa) return MIXLLM_E_NULL;
+  if (!mixllm::is_aligned16(gate) || !mixllm::is_aligned16(up) || !mixllm::is_aligned16(aq) ||
+      !mixllm::is_aligned16(sa) || (asum && !mixllm::is_aligned16(asum)) ||
+      (rowop && !mixllm::is_aligned16(rowop)) || (h && !mixllm::is_aligned16(h)))
+    return MIXLLM_E_SHAPE;
+  const int64_t npairs = (int64_t)M * (I / MIXLLM_GROUP);
+  const int64_t blocks = (npairs + kPairsPerBlock - 1) / kPairsPerBlock;
+  if (blocks > 0x7FFFFFFF) return MIXLLM_E_SHAPE;
+  hipLaunchKernelGGL(silu_mul_quant_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, gate,
+                     up, ld, M, I, aq, sa, asum, reinterpret_cast<uint4 *>(rowop), h);
   return hipGetLastError() == hipSuccess ? MIXLLM_OK : MIXLLM_E_HIP;
 }

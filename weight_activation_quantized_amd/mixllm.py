@@ -71,6 +71,7 @@ _SIGS = {
     "mixllm_channel_salience": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
     "mixllm_assign_channels": ([_vp, _vp, _i32, _i64, _vp, _vp], ctypes.c_int),
     "mixllm_quant_act": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mixllm_silu_mul_quant": ([_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mixllm_gemm_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "mixllm_gemm_w4w8a8": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _i64, _vp, _sz, _vp],
                            ctypes.c_int),
@@ -226,6 +227,19 @@ def mixllm_quant_act(a, aq, sa, asum=None, rowop=None, stream=None, lib=None):
                                           _ptr(rowop), _stream(stream)))
 
 
+def mixllm_silu_mul_quant(gate, up, aq, sa, asum=None, rowop=None, h=None, stream=None, lib=None):
+    """gate, up: fp16 [M, I] CUDA views with the same row stride (e.g. the two halves of a
+    [M, 2I] GEMM output); outputs as mixllm_quant_act with K = I; h: fp16 [M, I] or None."""
+    m, inter = gate.shape
+    if gate.dtype != torch.float16 or up.dtype != torch.float16 or gate.stride(1) != 1 or up.stride(1) != 1:
+        raise ValueError("gate and up must be fp16 with unit column stride")
+    if up.shape != gate.shape or (m > 1 and up.stride(0) != gate.stride(0)):
+        raise ValueError("gate and up must have the same shape and row stride")
+    ld = gate.stride(0) if m > 1 else inter
+    _check((lib or _lib).mixllm_silu_mul_quant(_ptr(gate), _ptr(up), ld, m, inter, GROUP, _ptr(aq), _ptr(sa),
+                                               _ptr(asum), _ptr(rowop), _ptr(h), _stream(stream)))
+
+
 def mixllm_gemm_workspace_bytes(m: int, n: int, k: int, n8: int) -> int:
     return int(_lib.mixllm_gemm_workspace_bytes(m, n, k, n8))
 
@@ -290,3 +304,47 @@ class PackedLinear:
         mixllm_gemm_w4w8a8(bufs["aq"], bufs["sa"], bufs["asum"], bufs["rowop"], m, self.n, self.k, self.n8,
                            self.blob, bufs["y"], bufs["ws"], stream)
         return bufs["y"]
+
+
+class MLPBlock:
+    """The Llama MLP block on the packed layers: one activation quantization feeds one GEMM
+    over the gate and up channels (packed together as one layer of 2I channels), the fused
+    SiLU(gate) * up + quantization feeds the down projection.  Four launches on one stream;
+    ``capture`` records them in a HIP graph.  Argument marshalling only."""
+
+    def __init__(self, w_gate, w_up, w_down, idx8_gate, idx8_up, idx8_down, device="cuda"):
+        self.inter, self.hidden = np.asarray(w_gate).shape
+        w_gu = np.concatenate([np.asarray(w_gate, np.float16), np.asarray(w_up, np.float16)])
+        idx_gu = np.concatenate([np.asarray(idx8_gate, np.int32), np.asarray(idx8_up, np.int32) + self.inter])
+        self.gu = PackedLinear(w_gu, idx_gu, device)
+        self.down = PackedLinear(np.asarray(w_down, np.float16), idx8_down, device)
+        self.device = device
+
+    def buffers(self, m: int):
+        dev = self.device
+        return dict(x=self.gu.buffers(m), h=self.down.buffers(m),
+                    h16=torch.empty((m, self.inter), dtype=torch.float16, device=dev))
+
+    def forward(self, x, bufs, stream=None, keep_h=False):
+        m = x.shape[0]
+        bx, bh = bufs["x"], bufs["h"]
+        self.gu.forward(x, bx, stream)
+        gu = bx["y"]
+        mixllm_silu_mul_quant(gu[:, :self.inter], gu[:, self.inter:], bh["aq"], bh["sa"], bh["asum"], bh["rowop"],
+                              bufs["h16"] if keep_h else None, stream)
+        mixllm_gemm_w4w8a8(bh["aq"], bh["sa"], bh["asum"], bh["rowop"], m, self.down.n, self.down.k,
+                           self.down.n8, self.down.blob, bh["y"], bh["ws"], stream)
+        return bh["y"]
+
+    def capture(self, x, bufs, keep_h=False):
+        """A HIP graph of one forward pass on these buffers (torch.cuda.CUDAGraph)."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.forward(x, bufs, s, keep_h)  # warm-up outside the capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self.forward(x, bufs, s, keep_h)
+        return g

@@ -162,3 +162,19 @@ def make_layer_inputs(shape: Shape):
 def make_layer_weights(shape: Shape):
     """(W fp16 [N, K], idx8 int32 [n8]) for a shape; independent of the token count."""
     return make_weights(shape.n, shape.k, shape.wseed), make_idx8(shape.n, shape.n8, shape.wseed)
+
+
+# Llama-3.1-8B MLP block (hidden 4096, intermediate 14336), 8-bit counts as in llama8b_n8().
+MLP8B = dict(hidden=4096, inter=14336)
+
+
+def mlp_block_inputs(m: int, hidden: int, inter: int, n8: dict, seed=(9,), dist: str = "normal"):
+    """(x fp16 [M, hidden], w_gate, w_up [inter, hidden], w_down [hidden, inter] fp16,
+    idx8_gate, idx8_up, idx8_down) for an MLP block."""
+    key = tuple(seed) + (hidden, inter)
+    x = make_acts(m, hidden, key + (m,), dist)
+    wg = make_weights(inter, hidden, key + (1,))
+    wu = make_weights(inter, hidden, key + (2,))
+    wd = make_weights(hidden, inter, key + (3,))
+    return (x, wg, wu, wd, make_idx8(inter, n8["gate"], key + (1,)), make_idx8(inter, n8["up"], key + (2,)),
+            make_idx8(hidden, n8["down"], key + (3,)))
