@@ -96,6 +96,8 @@ SMALL = [
     (1, 1, 128, 0), (3, 1, 128, 1), (256, 520, 640, 52), (200, 33, 256, 32),
     # tile kernel: slices with an odd step count, the LDS stage ring wrapping several times
     (160, 288, 1920, 40), (96, 130, 2688, 13),
+    # M <= 64 on layers wide enough (on a 256-CU part) for the tile kernel's cost rule
+    (48, 12800, 256, 1280), (20, 16448, 128, 100), (1, 29000, 128, 290),
 ]
 
 

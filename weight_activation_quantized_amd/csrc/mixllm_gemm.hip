@@ -125,7 +125,7 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 // ------------------------------------------------------------------------------------
-// Tile kernel (M > 64).  A workgroup of 8 waves owns 64 rows x 128 channels (4 blocks of
+// Tile kernel.  A workgroup of 8 waves owns 64 rows x 128 channels (4 blocks of
 // 32 channels).  Wave (b, q) computes block 4 tn + b for all 64 rows over the groups
 // g = q, q + 2, q + 4, ... (two interleaved group slices, two waves per SIMD); the
 // slices' accumulators are summed through LDS at the end in slice order.
@@ -605,80 +605,175 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
 
 // ------------------------------------------------------------------------------------
 // Skinny kernel (small M): one workgroup per 16-channel half block; its KS waves split
-// the groups, each wave computes all M <= 16 RB rows for its groups with
-// v_mfma_i32_16x16x64_i8, and the partial sums are reduced through LDS.
+// the groups into contiguous ranges, each wave computes all M <= 16 RB rows for its
+// groups with v_mfma_i32_16x16x64_i8, and the partial sums are reduced through LDS.
+// The kernel is bound by the weight stream from HBM: every wave keeps the loads of the
+// next D - 1 groups in flight (a register ring, unrolled so the slot indices are
+// constants; the compiler places the waits), then finishes the last cnt % D groups in an
+// unrolled tail.  Loads issued ahead past a wave's last group re-read that group (the
+// group index is clamped) and are never consumed.
 // ------------------------------------------------------------------------------------
-template <int RB, bool PARTIALS>
-__global__ __launch_bounds__(1024) void gemm_skinny_kernel(const GemmArgs p, int ks) {
-  __shared__ float red[16][RB * 4][64];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int sub = blockIdx.x;
-  const int blk = sub >> 1, half = sub & 1;
+// A per-lane buffer offset beyond any skinny-kernel descriptor, even with the largest
+// scalar offset added (the host checks M * K and G * M * 4 stay below it).
+constexpr int kSkinnyOob = 0x7FFFFF00;
+
+#ifndef MIXLLM_SK_WR2
+#define MIXLLM_SK_WR2 4
+#endif
+#ifndef MIXLLM_SK_AR34
+#define MIXLLM_SK_AR34 2
+#endif
+#ifndef MIXLLM_SK_AR2
+#define MIXLLM_SK_AR2 4
+#endif
+constexpr int skinny_wring(int rb, int kind) {
+  return rb == 1 && kind == kW4 ? 8 : (rb == 2 && kind == kW4 ? MIXLLM_SK_WR2 : 4);
+}
+constexpr int skinny_aring(int rb) { return rb == 1 ? 8 : (rb == 2 ? MIXLLM_SK_AR2 : MIXLLM_SK_AR34); }
+
+template <int RB, int KIND, bool PARTIALS>
+__device__ __forceinline__ void skinny_body(const GemmArgs &p, int blk, int half, int lane, int g0, int cnt,
+                                            float (&acc)[RB][4]) {
+  constexpr int DW = skinny_wring(RB, KIND);         // weight ring: loads DW - 1 groups ahead
+  constexpr int DA = skinny_aring(RB) < DW ? skinny_aring(RB) : DW;  // activation ring: DA - 1 ahead
+  constexpr int NWL = KIND == kW8 ? 2 : 1;           // 16-byte weight loads per group
   const int ch = lane & 15, qd = lane >> 4, ch32 = half * 16 + ch;
   const int G = p.G;
-  const int g0 = (int)((int64_t)G * wave / ks), g1 = (int)((int64_t)G * (wave + 1) / ks);
-  const bool has4 = blk < p.nb4;
-  const bool has8 = !has4;
   const int jp = blk * 32 + ch32;
+  const int bq = KIND == kW8 ? blk - p.nb4 : blk;
+  constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
+  const Rsrc rw = make_rsrc((KIND == kW8 ? p.w8 : p.w4) + (size_t)bq * G * kWChunk, (int64_t)G * kWChunk);
+  const Rsrc rs = make_rsrc((KIND == kW8 ? p.s8 : p.s4) + (size_t)bq * G * 32, (int64_t)G * 64);
+  const Rsrc rz = make_rsrc(p.z4 + (size_t)bq * G * kZ4Chunk, KIND == kW4 ? (int64_t)G * kZ4Chunk : 0);
+  const Rsrc ra = make_rsrc(p.aq, (int64_t)p.M * p.K);
+  const Rsrc rsa = make_rsrc(p.sa, (int64_t)G * p.M * 4);
+  // Per-lane offsets.  Lanes of rows past M take an offset past the end of every
+  // descriptor (kSkinnyOob), so their loads return zeros without touching memory.
+  const int vw = KIND == kW8 ? half * 2048 + lane * 16 : half * 1024 + lane * 16;
+  int va[RB][2], vsa[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = rb * 16 + ch;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) va[rb][c] = row < p.M ? row * p.K + (qd + 4 * c) * 16 : kSkinnyOob;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vsa[rb][r] = rb * 16 + 4 * qd + r < p.M ? (rb * 16 + 4 * qd + r) * 4 : kSkinnyOob;
+  }
+
+  v4i wR[DW][NWL];
+  uint32_t zR[DW], sR[DW];
+  v4i aR[DA][RB][2], saR[DA][RB];
+  auto grp = [&](int s) { return g0 + min(s, cnt - 1); };
+  // The activation loads of step s go first in a step's batch: waiting for them then
+  // leaves the deeper weight loads issued after them in flight.
+  auto issue_a = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    const int g = grp(s);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) aR[J][rb][c] = bload16(ra, va[rb][c], g * 128);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) saR[J][rb][r] = (int)bload4(rsa, vsa[rb][r], g * p.M * 4);
+    }
+  };
+  auto issue_w = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    const int g = grp(s);
+#pragma unroll
+    for (int t = 0; t < NWL; ++t) wR[J][t] = bload16(rw, vw + t * 1024, g * kWChunk);
+    sR[J] = bload4(rs, (ch32 >> 1) * 4, g * 64);
+    if constexpr (KIND == kW4) zR[J] = bload4(rz, (ch32 >> 3) * 4, g * (int)kZ4Chunk);
+  };
+  auto compute = [&](auto jw_c, auto ja_c, int s) {
+    constexpr int JW = decltype(jw_c)::value, JA = decltype(ja_c)::value;
+    const int g = grp(s);
+    const float sw = h2f((uint16_t)(sR[JW] >> ((ch32 & 1) * 16)));
+    v4i b0, b1;
+    if constexpr (KIND == kW4) {
+      const uint32_t zz = ((zR[JW] >> ((ch32 & 7) * 4)) & 15u) * 0x01010101u;
+      const v4i x = wR[JW][0];
+      b0 = w4_operand((uint32_t)x[0], (uint32_t)x[1], zz);
+      b1 = w4_operand((uint32_t)x[2], (uint32_t)x[3], zz);
+    } else {
+      b0 = wR[JW][0];
+      b1 = wR[JW][1];
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      v4i P = __builtin_amdgcn_mfma_i32_16x16x64_i8(aR[JA][rb][0], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+      P = __builtin_amdgcn_mfma_i32_16x16x64_i8(aR[JA][rb][1], b1, P, 0, 0, 0);
+      if constexpr (PARTIALS) {
+        const int orig = p.idx[jp];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rb * 16 + 4 * qd + r;
+          if (row < p.M && orig >= p.n_begin && orig < p.n_begin + p.n_count)
+            p.part[((int64_t)row * p.n_count + (orig - p.n_begin)) * G + g] = P[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[rb][r] = fmaf((float)P[r], sw * __int_as_float(saR[JA][rb][r]), acc[rb][r]);
+      }
+    }
+  };
+
+  // Prologue in the order the steps issue: step t issues activations for t + DA - 1, then
+  // weights for t + DW - 1 (DA <= DW).
+  static_assert(DW % DA == 0, "ring depths");
+  static_for<0, DW - 1>([&](auto t_c) {
+    constexpr int T = decltype(t_c)::value;  // "step" T - (DW - 1) of the prologue
+    constexpr int SA = T - (DW - 1) + (DA - 1);
+    if constexpr (SA >= 0) issue_a(IntC<SA % DA>{}, SA);
+    issue_w(t_c, T);
+  });
+  const int nfull = cnt / DW * DW;
+  for (int s = 0; s < nfull; s += DW) {
+    static_for<0, DW>([&](auto j_c) {
+      constexpr int J = decltype(j_c)::value;
+      issue_a(IntC<(J + DA - 1) % DA>{}, s + J + DA - 1);
+      issue_w(IntC<(J + DW - 1) % DW>{}, s + J + DW - 1);
+      compute(j_c, IntC<J % DA>{}, s + J);
+    });
+  }
+  // The last cnt % DW steps: their weights are already in flight; the activations of the
+  // later ones still have to be issued.  (Wave-uniform branches.)
+  const int rem = cnt - nfull;
+  static_for<0, DW - 1>([&](auto j_c) {
+    constexpr int J = decltype(j_c)::value;
+    if (J < rem) {
+      issue_a(IntC<(J + DA - 1) % DA>{}, nfull + J + DA - 1);
+      compute(j_c, IntC<J % DA>{}, nfull + J);
+    }
+  });
+}
+
+#ifndef MIXLLM_SK_MAXW2
+#define MIXLLM_SK_MAXW2 8
+#endif
+constexpr int skinny_max_waves(int rb) { return rb == 2 ? MIXLLM_SK_MAXW2 : 8; }
+
+template <int RB, bool PARTIALS>
+__global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(const GemmArgs p, int ks) {
+  extern __shared__ float red_dyn[];  // [ks][RB * 4][64]
+  float(*red)[RB * 4][64] = reinterpret_cast<float(*)[RB * 4][64]>(red_dyn);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int sub = blockIdx.x;
+  const int blk = sub >> 1, half = sub & 1;
+  const int G = p.G;
+  const int g0 = (int)((int64_t)G * wave / ks), g1 = (int)((int64_t)G * (wave + 1) / ks);
 
   float acc[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[rb][r] = 0.0f;
-
-  auto a_load = [&](int rb, int g, int chunk) {
-    const int row = rb * 16 + ch;
-    return row < p.M ? ldg16(p.aq + (int64_t)row * p.K + g * 128 + chunk * 16) : v4i{0, 0, 0, 0};
-  };
-  auto fold_or_emit = [&](const v4i (&P)[RB], int g, float sw) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rb * 16 + 4 * qd + r;
-        if (PARTIALS) {
-          const int orig = p.idx[jp];
-          if (row < p.M && orig >= p.n_begin && orig < p.n_begin + p.n_count)
-            p.part[((int64_t)row * p.n_count + (orig - p.n_begin)) * G + g] = P[rb][r];
-        } else {
-          const float s_a = row < p.M ? p.sa[(int64_t)g * p.M + row] : 0.0f;
-          acc[rb][r] = fmaf((float)P[rb][r], sw * s_a, acc[rb][r]);
-        }
-      }
-  };
-
-  for (int g = g0; g < g1; ++g) {
-    if (has4) {
-      const size_t cidx = (size_t)blk * G + g;
-      const v4i x = ldg16(p.w4 + cidx * kW4Chunk + half * 1024 + lane * 16);
-      const uint32_t zz = zero_point_x4(p.z4[cidx * 16 + (ch32 >> 1)], ch32 & 1);
-      const float sw = h2f(p.s4[cidx * 32 + ch32]);
-      const v4i b0 = w4_operand((uint32_t)x[0], (uint32_t)x[1], zz);
-      const v4i b1 = w4_operand((uint32_t)x[2], (uint32_t)x[3], zz);
-      v4i P[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        P[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_load(rb, g, qd), b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-        P[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_load(rb, g, qd + 4), b1, P[rb], 0, 0, 0);
-      }
-      fold_or_emit(P, g, sw);
-    }
-    if (has8) {
-      const size_t cidx = (size_t)(blk - p.nb4) * G + g;
-      const uint8_t *chunk = p.w8 + cidx * kW8Chunk + half * 2048;
-      const v4i b0 = ldg16(chunk + lane * 16);
-      const v4i b1 = ldg16(chunk + 1024 + lane * 16);
-      const float sw = h2f(p.s8[cidx * 32 + ch32]);
-      v4i P[RB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        P[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_load(rb, g, qd), b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-        P[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_load(rb, g, qd + 4), b1, P[rb], 0, 0, 0);
-      }
-      fold_or_emit(P, g, sw);
-    }
+  if (g1 > g0) {
+    if (blk < p.nb4)
+      skinny_body<RB, kW4, PARTIALS>(p, blk, half, lane, g0, g1 - g0, acc);
+    else
+      skinny_body<RB, kW8, PARTIALS>(p, blk, half, lane, g0, g1 - g0, acc);
   }
   if (PARTIALS) return;
 
@@ -767,15 +862,60 @@ struct Plan {
   int tiles_m, tiles_n;        // tile kernel grid
 };
 
+// Waves of the skinny kernel that fit a SIMD at once (its register count, read once).
+template <int RB>
+int skinny_waves_per_simd() {
+  static int cached = 0;
+  if (cached == 0) {
+    hipFuncAttributes at;
+    int regs = 128;
+    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(gemm_skinny_kernel<RB, false>)) == hipSuccess &&
+        at.numRegs > 0)
+      regs = at.numRegs;
+    regs = (regs + 7) / 8 * 8;
+    const int w = 512 / regs;
+    cached = w < 1 ? 1 : (w > 8 ? 8 : w);
+  }
+  return cached;
+}
+
+int skinny_waves_per_simd_rb(int rb) {
+  switch (rb) {
+    case 1: return skinny_waves_per_simd<1>();
+    case 2: return skinny_waves_per_simd<2>();
+    case 3: return skinny_waves_per_simd<3>();
+    default: return skinny_waves_per_simd<4>();
+  }
+}
+
+// Relative cost per weight byte of the skinny kernel against a full round of the tile
+// kernel, in thousandths, for M rows (measured on the Llama-3.1 8B and 70B layers: it grows
+// with the 16-row blocks the skinny kernel computes).
+int skinny_cost_pm(int M) {
+  const int rb = (M + 15) / 16;
+  return rb == 1 ? 1000 + 1000 * M / 48 : (rb == 2 ? 2100 : (rb == 3 ? 3900 : 4400));
+}
+
+// M <= 64 rows: the tile kernel runs one 64-row tile per 128 channels, so a layer with
+// fewer tiles than CUs leaves CUs idle (a round of tiles takes about as long as the skinny
+// kernel takes to stream the same weights at M = 1); the skinny kernel keeps every CU busy
+// but costs more per weight byte as M grows.  The tile kernel is taken when
+// tiles * cost > 0.9 * CUs.
 Plan make_plan(int M, const mixllm_blob_info &L) {
   Plan pl{};
-  if (M <= 64) {
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const int64_t tiles_n = (L.nb + kTileNB - 1) / kTileNB;
+  if (M <= 64 && tiles_n * skinny_cost_pm(M) <= (int64_t)900 * cus) {
     pl.skinny = true;
     pl.rb = (M + 15) / 16;
+    // Split each half block's groups over as many waves as keep the whole grid resident at
+    // once (one round of workgroups), within the workgroup size limit.
     const int subs = 2 * L.nb;
-    int ks = (4096 + subs - 1) / subs;
-    ks = ks < 1 ? 1 : (ks > 16 ? 16 : ks);
-    pl.ks = ks > L.G ? L.G : ks;
+    const int64_t slots = (int64_t)cus * 4 * skinny_waves_per_simd_rb(pl.rb);
+    int64_t ks = slots / subs;
+    const int kmax = skinny_max_waves(pl.rb);
+    ks = ks < 1 ? 1 : (ks > kmax ? kmax : ks);
+    pl.ks = (int)(ks > L.G ? L.G : ks);
     return pl;
   }
   pl.tiles_m = (M + kTileBM - 1) / kTileBM;
@@ -791,17 +931,26 @@ bool tile_offsets_fit(int M, const mixllm_blob_info &L) {
          (int64_t)kTileBM * L.K + (int64_t)L.G * 128 <= 0x7FFFFFFF;
 }
 
+// The skinny kernel addresses an activation row set (M * K bytes), a group's scales
+// (G * M * 4) and a block's weights (G * 4096) with 32-bit offsets.
+bool skinny_offsets_fit(int M, const mixllm_blob_info &L) {
+  return (int64_t)M * L.K + 256 <= kSkinnyOob && (int64_t)L.G * M * 4 + 256 <= kSkinnyOob &&
+         (int64_t)L.G * (int64_t)kW8Chunk <= 0x7FFFFFFF &&
+         (int64_t)kSkinnyOob + (int64_t)L.G * 128 + (int64_t)L.G * M * 4 < ((int64_t)1 << 32);
+}
+
 template <bool PARTIALS>
 int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
   (void)hipGetLastError();
   if (pl.skinny) {
     const int ks = pl.ks;
     const dim3 grid((unsigned)(2 * a.nb)), block((unsigned)(64 * ks));
+    const size_t lds = (size_t)ks * pl.rb * 4 * 64 * sizeof(float);
     switch (pl.rb) {
-      case 1: hipLaunchKernelGGL((gemm_skinny_kernel<1, PARTIALS>), grid, block, 0, stream, a, ks); break;
-      case 2: hipLaunchKernelGGL((gemm_skinny_kernel<2, PARTIALS>), grid, block, 0, stream, a, ks); break;
-      case 3: hipLaunchKernelGGL((gemm_skinny_kernel<3, PARTIALS>), grid, block, 0, stream, a, ks); break;
-      default: hipLaunchKernelGGL((gemm_skinny_kernel<4, PARTIALS>), grid, block, 0, stream, a, ks); break;
+      case 1: hipLaunchKernelGGL((gemm_skinny_kernel<1, PARTIALS>), grid, block, lds, stream, a, ks); break;
+      case 2: hipLaunchKernelGGL((gemm_skinny_kernel<2, PARTIALS>), grid, block, lds, stream, a, ks); break;
+      case 3: hipLaunchKernelGGL((gemm_skinny_kernel<3, PARTIALS>), grid, block, lds, stream, a, ks); break;
+      default: hipLaunchKernelGGL((gemm_skinny_kernel<4, PARTIALS>), grid, block, lds, stream, a, ks); break;
     }
   } else {
     a.tiles_m = pl.tiles_m;
@@ -836,7 +985,7 @@ extern "C" int mixllm_gemm_w4w8a8(const int8_t *aq, const float *sa, const int32
   (void)workspace;
   (void)workspace_bytes;
   const Plan pl = make_plan(M, L);
-  if (!pl.skinny && !tile_offsets_fit(M, L)) return MIXLLM_E_SHAPE;
+  if (pl.skinny ? !skinny_offsets_fit(M, L) : !tile_offsets_fit(M, L)) return MIXLLM_E_SHAPE;
   GemmArgs a;
   fill_args(a, aq, sa, asum, rowop, M, blob, L);
   a.y = y;
@@ -857,7 +1006,7 @@ extern "C" int mixllm_gemm_w4w8a8_partials(const int8_t *aq, const float *sa, co
   if (M == 0 || n_count == 0) return MIXLLM_OK;
   if (!part) return MIXLLM_E_NULL;
   const Plan pl = make_plan(M, L);
-  if (!pl.skinny && !tile_offsets_fit(M, L)) return MIXLLM_E_SHAPE;
+  if (pl.skinny ? !skinny_offsets_fit(M, L) : !tile_offsets_fit(M, L)) return MIXLLM_E_SHAPE;
   GemmArgs a;
   fill_args(a, aq, sa, asum, rowop, M, blob, L);
   a.part = part;
