@@ -11,8 +11,9 @@
 // groups of the same token, so a wave reads 1 KB of contiguous fp16 input.
 //
 // Arithmetic matches the definition bit for bit: the maximum of |x| is exact, the scale
-// is an IEEE fp32 division amax / 127, each code is rne(x / s) with an IEEE division
-// (hipcc's default correctly rounded division; no fast-math), clamped to [-127, 127].
+// is an IEEE fp32 division amax / 127, each code is rne(x / s) of the correctly rounded
+// quotient (a reciprocal product where that provably rounds the same way, else hipcc's
+// default correctly rounded division; no fast-math), clamped to [-127, 127].
 //
 // Optionally the kernel also writes the row operands of the GEMM's scale products: s and
 // u = fp32(S_A * s) each as an exact sum of three bf16 values (truncate to bf16, the
@@ -30,6 +31,9 @@ bool is_aligned16(const void *p);
 
 namespace {
 
+#ifndef MIXLLM_QA_DIV
+#define MIXLLM_QA_DIV 0
+#endif
 #ifndef MIXLLM_QA_PPL
 #define MIXLLM_QA_PPL 1
 #endif
@@ -85,6 +89,7 @@ __device__ __forceinline__ void quant_pair(uint4 raw, bool live, int64_t m, int 
 
   int q[8];
   int qsum = 0;
+#if MIXLLM_QA_DIV
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float v = amax > 0.0f ? __builtin_rintf(x[i] / s) : 0.0f;
@@ -92,6 +97,22 @@ __device__ __forceinline__ void quant_pair(uint4 raw, bool live, int64_t m, int 
     q[i] = (int)v;
     qsum += q[i];
   }
+#else
+  // rne(x / s) without a division per code: t = x * rcp(s) differs from the correctly
+  // rounded quotient by less than 6e-5 (|x / s| <= 127, v_rcp_f32 within 1 ulp, one more
+  // rounding in the product), so rne(t) is rne(x / s) unless t lies within 2^-12 of a
+  // half-integer; those codes take the IEEE division.
+  const float r = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = x[i] * r;
+    float v = __builtin_rintf(t);
+    if (fabsf(t - v) > 0.5f - 0x1p-12f) v = __builtin_rintf(x[i] / s);
+    v = amax > 0.0f ? fminf(fmaxf(v, -127.0f), 127.0f) : 0.0f;
+    q[i] = (int)v;
+    qsum += q[i];
+  }
+#endif
   qsum = quarter_sum(qsum);
   if (!live) return;
 
