@@ -168,12 +168,16 @@ constexpr int kTileNB = 4;                          // channel blocks per workgr
 constexpr int kKS = 2;                              // interleaved group slices
 constexpr int kTileWaves = kTileNB * kKS;
 constexpr int kTileThreads = 64 * kTileWaves;
-constexpr int kSA = 4;                              // LDS stages = ring slots = unroll
+#ifndef MIXLLM_STAGES
+#define MIXLLM_STAGES 4
+#endif
+constexpr int kSA = MIXLLM_STAGES;                  // LDS stages
 #ifndef MIXLLM_WRING
 #define MIXLLM_WRING 4
 #endif
 constexpr int kWR = MIXLLM_WRING;                   // weight ring slots (2 or 4)
 static_assert(kWR == 2 || kWR == 4, "weight ring");
+static_assert(kSA % kWR == 0 && kSA >= 2, "the step loop is unrolled by the number of stages");
 #ifndef MIXLLM_TILE_PHASE
 #define MIXLLM_TILE_PHASE 1
 #endif
@@ -270,11 +274,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   constexpr int NZ = ((PARTIALS && KIND == kW4) || ZPRE) ? 1 : 0;
   constexpr int LD = RDMA ? 3 : 2;                                // direct-to-LDS loads per step
   constexpr int LW = HASW ? NW + 1 + NZ : 0;                      // weight-ring loads per step
-  // Loads that may still be outstanding when a step's loads have landed.  Ring of four:
-  // a step's weights and stage are both issued kSA - 1 steps ahead, so the batches of the
-  // two later steps.  Ring of two: the weights are issued one step ahead, so the stage
-  // batch of the previous step (or, for a wave without weights, of the two previous).
-  constexpr int WAIT = kWR == 4 ? 2 * (LW + LD) : (HASW ? LD : 2 * LD);
+  // Loads that may still be outstanding when a step's loads have landed.  A step issues
+  // its weight batch, then its stage batch; step s's weights come kWR - 1 steps ahead and
+  // its stage kSA - 1 >= kWR - 1 steps ahead.  With weights, the last of step s's loads is
+  // its weight batch (or, when kWR == kSA, the stage batch right after it), followed by
+  // the stage batch of that step (if kWR < kSA) and the kWR - 2 full batches of the steps
+  // in between; without weights, the kSA - 2 stage batches after step s's stage.
+  constexpr int WAIT = !HASW ? (kSA - 2) * LD : (kWR < kSA ? LD : 0) + (kWR - 2) * (LW + LD);
+  static_assert(WAIT < 64, "vmcnt range");
   constexpr bool CORR = (KIND == kW4 && !ZPRE) || (kFoldBias && KIND != kNone);
   const int ch32 = lane & 31, h = lane >> 5;
   const int G = p.G;
@@ -391,7 +398,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     }
   };
 
-  // One step s: stage J = s % kSA, weight slot J % 2.
+  // One step s: stage J = s % kSA, weight slot W = s % kWR.
   auto step = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
     constexpr int W = J % kWR;
@@ -472,27 +479,16 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     }
   };
 
-  // Prologue: the loads of steps 0 .. kSA - 2 in the order the steps issue them.
-  static_assert(kSA == 4, "prologue and loop are written for four stages");
-  if constexpr (kWR == 4) {
-    issue_w(IntC<0>{}, 0);
-    issue_a(IntC<0>{}, 0);
-    issue_w(IntC<1>{}, 1);
-    issue_a(IntC<1>{}, 1);
-    issue_w(IntC<2>{}, 2);
-    issue_a(IntC<2>{}, 2);
-  } else {
-    issue_a(IntC<0>{}, 0);
-    issue_a(IntC<1>{}, 1);
-    issue_w(IntC<0>{}, 0);
-    issue_a(IntC<2>{}, 2);
-  }
+  // Prologue: the loads of the first kSA - 1 stages and kWR - 1 weight slots, in the order
+  // the steps before step 0 would issue them (weights, then stage, per step).
+  static_for<0, kSA - 1>([&](auto t_c) {
+    constexpr int T = decltype(t_c)::value - (kSA - 1);  // steps -(kSA - 1) .. -1
+    if constexpr (T + kWR - 1 >= 0) issue_w(IntC<(T + kWR - 1) % kWR>{}, T + kWR - 1);
+    issue_a(IntC<T + kSA - 1>{}, T + kSA - 1);
+  });
   for (int it = 0; it < niter; ++it) {
     const int s = it * kSA;
-    step(IntC<0>{}, s);
-    step(IntC<1>{}, s + 1);
-    step(IntC<2>{}, s + 2);
-    step(IntC<3>{}, s + 3);
+    static_for<0, kSA>([&](auto j_c) { step(j_c, s + decltype(j_c)::value); });
   }
   if constexpr (!PARTIALS && HASW) {
     fold(acc1, P1, sc1);
