@@ -98,6 +98,9 @@ SMALL = [
     (160, 288, 1920, 40), (96, 130, 2688, 13),
     # M <= 64 on layers wide enough (on a 256-CU part) for the tile kernel's cost rule
     (48, 12800, 256, 1280), (20, 16448, 128, 100), (1, 29000, 128, 290),
+    # M = 1 on a layer wide enough for the one-lane-per-channel kernel: an odd number of
+    # 4-bit blocks, promoted 4-bit channels, several groups per wave and a ragged tail
+    (1, 16448, 8960, 1608),
 ]
 
 

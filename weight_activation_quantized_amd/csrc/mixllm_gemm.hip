@@ -790,6 +790,176 @@ __global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(
 }
 
 // ------------------------------------------------------------------------------------
+// GEMV kernel (M = 1, one token: the decode case).  Every lane streams 64 bytes of one
+// channel's codes per group and forms its part of the group partial with v_dot4_i32_i8
+// against the token's activation codes, which all lanes share and which therefore come
+// through scalar loads into SGPRs.  A 4-bit wave owns two blocks (64 channels, one per
+// lane; the 64 bytes are the channel's 128 codes); an 8-bit wave owns one block, lanes c
+// and c + 32 holding the first and second 64 inputs of channel c.  The zero point enters
+// as - z * S_A.  A workgroup's waves split the groups into contiguous ranges and reduce
+// through LDS in a fixed order.  The vector memory path carries only weights and their
+// scale and zero-point words, so the kernel is bound by the weight stream.
+// ------------------------------------------------------------------------------------
+#ifndef MIXLLM_GV_WAVES
+#define MIXLLM_GV_WAVES 16
+#endif
+constexpr int kGvWaves = MIXLLM_GV_WAVES;  // waves per workgroup at most
+constexpr int kGvRing = 4;   // weight ring: loads 3 groups ahead
+
+typedef const __attribute__((address_space(4))) v16i *ConstV16;
+typedef const __attribute__((address_space(4))) float *ConstF;
+typedef const __attribute__((address_space(4))) int32_t *ConstI;
+
+// 4-bit: lane c (c = lane & 31) computes packed channel 32 blk + c, blk being the strip's
+// first block for lanes 0-31 and its second for lanes 32-63 (`second`; with `dup` the
+// first block again, results unused).  8-bit: blk0 is the block and kh = lane >> 5 the
+// half of the group's inputs.
+template <int KIND, bool PARTIALS>
+__device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
+                                          int cnt, float &acc) {
+  constexpr int D = kGvRing;
+  constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
+  const int c = lane & 31, half = c >> 4, ch = c & 15, kh = lane >> 5;
+  const int G = p.G;
+  const int bq = KIND == kW8 ? blk0 - p.nb4 : blk0;
+  const Rsrc rw = make_rsrc((KIND == kW8 ? p.w8 : p.w4) + (size_t)bq * G * kWChunk, (int64_t)2 * G * kWChunk);
+  const Rsrc rs = make_rsrc((KIND == kW8 ? p.s8 : p.s4) + (size_t)bq * G * 32, (int64_t)2 * G * 64);
+  const Rsrc rz = make_rsrc(p.z4 + (size_t)bq * G * kZ4Chunk, KIND == kW4 ? (int64_t)2 * G * kZ4Chunk : 0);
+  // 4-bit: unit (half * 4 + a) * 16 + ch holds k-chunks a and a + 4 of the channel;
+  // 8-bit: unit (half * 8 + t) * 16 + ch holds k-chunk t (this lane: t = 4 kh + a).
+  const int vw = KIND == kW8 ? ((half * 8 + 4 * kh) * 16 + ch) * 16
+                             : second * G * kWChunk + ((half * 4) * 16 + ch) * 16;
+  const int vs = (KIND == kW8 ? 0 : second * G * 64) + (c >> 1) * 4;
+  const int vz = second * G * (int)kZ4Chunk + (c >> 3) * 4;
+  const int jp = (blk0 + second) * 32 + c;
+
+  v4i wR[D][4];
+  uint32_t sR[D], zR[D];
+  v16i aR[2][2];
+  float saR[2];
+  int asR[2];
+  auto grp = [&](int s) { return g0 + min(s, cnt - 1); };
+  auto issue_a = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    const int g = grp(s);
+    aR[J][0] = *(ConstV16)(p.aq + (int64_t)g * 128);
+    aR[J][1] = *(ConstV16)(p.aq + (int64_t)g * 128 + 64);
+    saR[J] = *(ConstF)(p.sa + g);
+    if constexpr (KIND == kW4) asR[J] = *(ConstI)(p.asum + g);
+  };
+  auto issue_w = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    const int g = grp(s);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wR[J][t] = bload16(rw, vw + t * 256, g * kWChunk);
+    sR[J] = bload4(rs, vs, g * 64);
+    if constexpr (KIND == kW4) zR[J] = bload4(rz, vz, g * (int)kZ4Chunk);
+  };
+  auto compute = [&](auto jw_c, auto ja_c, int s) {
+    constexpr int JW = decltype(jw_c)::value, JA = decltype(ja_c)::value;
+    int P = 0;
+    if constexpr (KIND == kW4) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const v4i x = wR[JW][a];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          // words 2w, 2w + 1: the codes of inputs 64 w + 16 a + [0, 16)
+          const uint32_t x0 = (uint32_t)x[2 * w], x1 = (uint32_t)x[2 * w + 1];
+          const v16i &av = aR[JA][w];
+          P = __builtin_amdgcn_sdot4(av[4 * a + 0], (int)(x0 & 0x0F0F0F0Fu), P, false);
+          P = __builtin_amdgcn_sdot4(av[4 * a + 1], (int)((x0 >> 4) & 0x0F0F0F0Fu), P, false);
+          P = __builtin_amdgcn_sdot4(av[4 * a + 2], (int)(x1 & 0x0F0F0F0Fu), P, false);
+          P = __builtin_amdgcn_sdot4(av[4 * a + 3], (int)((x1 >> 4) & 0x0F0F0F0Fu), P, false);
+        }
+      }
+      const int z = (int)((zR[JW] >> ((c & 7) * 4)) & 15u);
+      P -= z * asR[JA];
+    } else {
+      // Both halves of the activation codes against this lane's codes (scalar operands
+      // cannot differ between lanes), then keep the half this lane's inputs belong to.
+      int P0 = 0, P1 = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        P0 = __builtin_amdgcn_sdot4(aR[JA][0][i], wR[JW][i >> 2][i & 3], P0, false);
+        P1 = __builtin_amdgcn_sdot4(aR[JA][1][i], wR[JW][i >> 2][i & 3], P1, false);
+      }
+      P = kh ? P1 : P0;
+    }
+    if constexpr (PARTIALS) {
+      if constexpr (KIND == kW8) P += __shfl_xor(P, 32);  // both halves of the inputs
+      const int orig = p.idx[jp];
+      if (!dup && (KIND == kW4 || kh == 0) && orig >= p.n_begin && orig < p.n_begin + p.n_count)
+        p.part[(int64_t)(orig - p.n_begin) * G + grp(s)] = P;
+    } else {
+      const float sw = h2f((uint16_t)(sR[JW] >> ((c & 1) * 16)));
+      acc = fmaf((float)P, sw * saR[JA], acc);
+    }
+  };
+
+  // Prologue: weights of steps 0 .. D - 2, activations of step 0.  The loop is unrolled by
+  // D (a multiple of the activation ring's 2) so every slot index is a constant; the last
+  // cnt % D groups run in an unrolled tail (wave-uniform branches).
+  static_assert(D % 2 == 0, "ring sizes");
+  issue_a(IntC<0>{}, 0);
+  static_for<0, D - 1>([&](auto t_c) { issue_w(t_c, decltype(t_c)::value); });
+  const int nfull = cnt / D * D;
+  for (int s = 0; s < nfull; s += D) {
+    static_for<0, D>([&](auto j_c) {
+      constexpr int J = decltype(j_c)::value;
+      issue_a(IntC<(J + 1) % 2>{}, s + J + 1);
+      issue_w(IntC<(J + D - 1) % D>{}, s + J + D - 1);
+      compute(j_c, IntC<J % 2>{}, s + J);
+    });
+  }
+  const int rem = cnt - nfull;
+  static_for<0, D - 1>([&](auto j_c) {
+    constexpr int J = decltype(j_c)::value;
+    if (J < rem) {
+      issue_a(IntC<(J + 1) % 2>{}, nfull + J + 1);
+      compute(j_c, IntC<J % 2>{}, nfull + J);
+    }
+  });
+}
+
+template <bool PARTIALS>
+__global__ __launch_bounds__(64 * kGvWaves) void gemm_gemv_kernel(const GemmArgs p, int ks, int nstrip4) {
+  __shared__ float red[kGvWaves][64];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int strip = blockIdx.x;
+  // Strips [0, nstrip4) pair the 4-bit blocks (with an odd count the last strip has one
+  // block, and its lanes 32-63 repeat lanes 0-31); the others hold one 8-bit block each.
+  const bool w4 = strip < nstrip4;
+  const int blk0 = w4 ? 2 * strip : p.nb4 + (strip - nstrip4);
+  const bool dup = w4 && (lane >> 5) >= min(2, p.nb4 - blk0);
+  const int second = w4 && !dup ? (lane >> 5) : 0;
+  const int G = p.G;
+  // (wave-uniform; read back into scalar registers for the loads' scalar offsets)
+  const int g0 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * wave / ks));
+  const int g1 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * (wave + 1) / ks));
+  float acc = 0.0f;
+  if (g1 > g0) {
+    if (w4)
+      gemv_body<kW4, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, acc);
+    else
+      gemv_body<kW8, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
+  }
+  if (PARTIALS) return;
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || dup || (!w4 && lane >= 32)) return;
+  float v = 0.0f;
+  if (w4) {
+    for (int w = 0; w < ks; ++w) v += red[w][lane];
+  } else {
+    for (int w = 0; w < ks; ++w) v += red[w][lane] + red[w][lane + 32];
+  }
+  const int orig = p.idx[(blk0 + second) * 32 + (lane & 31)];
+  if (orig >= 0) p.y[orig] = f2h(v);
+}
+
+// ------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------
 
@@ -852,6 +1022,8 @@ int device_cus() {
 
 // Launch plan of one GEMM call, a pure function of the shape.
 struct Plan {
+  bool gemv;                   // M = 1: the one-lane-per-channel kernel
+  int nstrip4, nstrip;         // gemv: strips of 4-bit blocks, all strips
   bool skinny;
   int rb;                      // skinny: 16-row blocks
   int ks;                      // skinny: waves per workgroup
@@ -884,6 +1056,22 @@ int skinny_waves_per_simd_rb(int rb) {
   }
 }
 
+// Waves of the gemv kernel that fit a SIMD at once (its register count, read once).
+int gemv_waves_per_simd() {
+  static int cached = 0;
+  if (cached == 0) {
+    hipFuncAttributes at;
+    int regs = 128;
+    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(gemm_gemv_kernel<false>)) == hipSuccess &&
+        at.numRegs > 0)
+      regs = at.numRegs;
+    regs = (regs + 7) / 8 * 8;
+    const int w = 512 / regs;
+    cached = w < 1 ? 1 : (w > 8 ? 8 : w);
+  }
+  return cached;
+}
+
 // Relative cost per weight byte of the skinny kernel against a full round of the tile
 // kernel, in thousandths, for M rows (measured on the Llama-3.1 8B and 70B layers: it grows
 // with the 16-row blocks the skinny kernel computes).
@@ -900,6 +1088,21 @@ int skinny_cost_pm(int M) {
 Plan make_plan(int M, const mixllm_blob_info &L) {
   Plan pl{};
   const int cus = device_cus() > 0 ? device_cus() : 256;
+  // One token: the gemv kernel, when the layer has enough strips (one workgroup each) to
+  // occupy at least half the CUs; narrower layers run the skinny kernel, whose grid is
+  // twice as fine.
+  const int nstrip4 = (L.nb4 + 1) / 2, nstrip = nstrip4 + L.nb8;
+  if (M == 1 && 2 * nstrip >= cus) {
+    pl.gemv = true;
+    pl.nstrip4 = nstrip4;
+    pl.nstrip = nstrip;
+    // Waves per workgroup: as many as keep the whole grid resident in one round.
+    const int64_t slots = (int64_t)cus * 4 * gemv_waves_per_simd();
+    int64_t ks = slots / pl.nstrip;
+    ks = ks < 1 ? 1 : (ks > kGvWaves ? kGvWaves : ks);
+    pl.ks = (int)(ks > L.G ? L.G : ks);
+    return pl;
+  }
   const int64_t tiles_n = (L.nb + kTileNB - 1) / kTileNB;
   if (M <= 64 && tiles_n * skinny_cost_pm(M) <= (int64_t)900 * cus) {
     pl.skinny = true;
@@ -935,10 +1138,20 @@ bool skinny_offsets_fit(int M, const mixllm_blob_info &L) {
          (int64_t)kSkinnyOob + (int64_t)L.G * 128 + (int64_t)L.G * M * 4 < ((int64_t)1 << 32);
 }
 
+// The gemv kernel addresses two blocks' weights of all groups with 32-bit offsets.
+bool gemv_offsets_fit(const mixllm_blob_info &L) { return (int64_t)(2 * L.G + 1) * (int64_t)kW8Chunk <= 0x7FFFFFFF; }
+
+bool offsets_fit(const Plan &pl, int M, const mixllm_blob_info &L) {
+  return pl.gemv ? gemv_offsets_fit(L) : (pl.skinny ? skinny_offsets_fit(M, L) : tile_offsets_fit(M, L));
+}
+
 template <bool PARTIALS>
 int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
   (void)hipGetLastError();
-  if (pl.skinny) {
+  if (pl.gemv) {
+    hipLaunchKernelGGL((gemm_gemv_kernel<PARTIALS>), dim3((unsigned)pl.nstrip), dim3((unsigned)(64 * pl.ks)), 0, stream,
+                       a, pl.ks, pl.nstrip4);
+  } else if (pl.skinny) {
     const int ks = pl.ks;
     const dim3 grid((unsigned)(2 * a.nb)), block((unsigned)(64 * ks));
     const size_t lds = (size_t)ks * pl.rb * 4 * 64 * sizeof(float);
@@ -981,7 +1194,7 @@ extern "C" int mixllm_gemm_w4w8a8(const int8_t *aq, const float *sa, const int32
   (void)workspace;
   (void)workspace_bytes;
   const Plan pl = make_plan(M, L);
-  if (pl.skinny ? !skinny_offsets_fit(M, L) : !tile_offsets_fit(M, L)) return MIXLLM_E_SHAPE;
+  if (!offsets_fit(pl, M, L)) return MIXLLM_E_SHAPE;
   GemmArgs a;
   fill_args(a, aq, sa, asum, rowop, M, blob, L);
   a.y = y;
@@ -1002,7 +1215,7 @@ extern "C" int mixllm_gemm_w4w8a8_partials(const int8_t *aq, const float *sa, co
   if (M == 0 || n_count == 0) return MIXLLM_OK;
   if (!part) return MIXLLM_E_NULL;
   const Plan pl = make_plan(M, L);
-  if (pl.skinny ? !skinny_offsets_fit(M, L) : !tile_offsets_fit(M, L)) return MIXLLM_E_SHAPE;
+  if (!offsets_fit(pl, M, L)) return MIXLLM_E_SHAPE;
   GemmArgs a;
   fill_args(a, aq, sa, asum, rowop, M, blob, L);
   a.part = part;
