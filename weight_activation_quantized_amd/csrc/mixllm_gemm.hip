@@ -805,6 +805,8 @@ __global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(
 #endif
 constexpr int kGvWaves = MIXLLM_GV_WAVES;  // waves per workgroup at most
 constexpr int kGvRing = 4;   // weight ring: loads 3 groups ahead
+constexpr int kNonTemporal = 2;  // cache-policy bit nt: the weights are read once
+constexpr int kGvMaxRows = 3;  // tokens the gemv kernel takes
 
 typedef const __attribute__((address_space(4))) v16i *ConstV16;
 typedef const __attribute__((address_space(4))) float *ConstF;
@@ -813,10 +815,12 @@ typedef const __attribute__((address_space(4))) int32_t *ConstI;
 // 4-bit: lane c (c = lane & 31) computes packed channel 32 blk + c, blk being the strip's
 // first block for lanes 0-31 and its second for lanes 32-63 (`second`; with `dup` the
 // first block again, results unused).  8-bit: blk0 is the block and kh = lane >> 5 the
-// half of the group's inputs.
-template <int KIND, bool PARTIALS>
+// half of the group's inputs.  MT tokens (rows): a lane decodes its codes of a group once
+// and runs them against each row's activation codes; the rows' operands pass through a
+// two-slot SGPR ring in (group, row) order, one item ahead.
+template <int KIND, int MT, bool PARTIALS>
 __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
-                                          int cnt, float &acc) {
+                                          int cnt, float (&acc)[MT]) {
   constexpr int D = kGvRing;
   constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
   const int c = lane & 31, half = c >> 4, ch = c & 15, kh = lane >> 5;
@@ -832,6 +836,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
   const int vs = (KIND == kW8 ? 0 : second * G * 64) + (c >> 1) * 4;
   const int vz = second * G * (int)kZ4Chunk + (c >> 3) * 4;
   const int jp = (blk0 + second) * 32 + c;
+  const int64_t K = p.K;
 
   v4i wR[D][4];
   uint32_t sR[D], zR[D];
@@ -839,25 +844,30 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
   float saR[2];
   int asR[2];
   auto grp = [&](int s) { return g0 + min(s, cnt - 1); };
-  auto issue_a = [&](auto j_c, int s) {
-    constexpr int J = decltype(j_c)::value;
+  // Item (s, m): row m's operands of step s's group into slot Q.
+  auto issue_a = [&](auto q_c, int s, int m) {
+    constexpr int Q = decltype(q_c)::value;
     const int g = grp(s);
-    aR[J][0] = *(ConstV16)(p.aq + (int64_t)g * 128);
-    aR[J][1] = *(ConstV16)(p.aq + (int64_t)g * 128 + 64);
-    saR[J] = *(ConstF)(p.sa + g);
-    if constexpr (KIND == kW4) asR[J] = *(ConstI)(p.asum + g);
+    const int8_t *ap = p.aq + (int64_t)m * K + (int64_t)g * 128;
+    aR[Q][0] = *(ConstV16)ap;
+    aR[Q][1] = *(ConstV16)(ap + 64);
+    saR[Q] = *(ConstF)(p.sa + (int64_t)g * MT + m);
+    if constexpr (KIND == kW4) asR[Q] = *(ConstI)(p.asum + (int64_t)g * MT + m);
   };
   auto issue_w = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
     const int g = grp(s);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) wR[J][t] = bload16(rw, vw + t * 256, g * kWChunk);
+    for (int t = 0; t < 4; ++t)
+      wR[J][t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, vw + t * 256, g * kWChunk, kNonTemporal));
     sR[J] = bload4(rs, vs, g * 64);
     if constexpr (KIND == kW4) zR[J] = bload4(rz, vz, g * (int)kZ4Chunk);
   };
-  auto compute = [&](auto jw_c, auto ja_c, int s) {
-    constexpr int JW = decltype(jw_c)::value, JA = decltype(ja_c)::value;
-    int P = 0;
+  // Step s (ring slot J of the weights; U = its position in the unrolled loop, which
+  // fixes the activation slots): decode once, then every row, prefetching the next item.
+  auto compute = [&](auto jw_c, auto u_c, int s, bool last) {
+    constexpr int JW = decltype(jw_c)::value, U = decltype(u_c)::value;
+    int wd[32];  // the lane's codes as 32 words of 4 consecutive inputs
     if constexpr (KIND == kW4) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
@@ -866,65 +876,80 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
         for (int w = 0; w < 2; ++w) {
           // words 2w, 2w + 1: the codes of inputs 64 w + 16 a + [0, 16)
           const uint32_t x0 = (uint32_t)x[2 * w], x1 = (uint32_t)x[2 * w + 1];
-          const v16i &av = aR[JA][w];
-          P = __builtin_amdgcn_sdot4(av[4 * a + 0], (int)(x0 & 0x0F0F0F0Fu), P, false);
-          P = __builtin_amdgcn_sdot4(av[4 * a + 1], (int)((x0 >> 4) & 0x0F0F0F0Fu), P, false);
-          P = __builtin_amdgcn_sdot4(av[4 * a + 2], (int)(x1 & 0x0F0F0F0Fu), P, false);
-          P = __builtin_amdgcn_sdot4(av[4 * a + 3], (int)((x1 >> 4) & 0x0F0F0F0Fu), P, false);
+          wd[16 * w + 4 * a + 0] = (int)(x0 & 0x0F0F0F0Fu);
+          wd[16 * w + 4 * a + 1] = (int)((x0 >> 4) & 0x0F0F0F0Fu);
+          wd[16 * w + 4 * a + 2] = (int)(x1 & 0x0F0F0F0Fu);
+          wd[16 * w + 4 * a + 3] = (int)((x1 >> 4) & 0x0F0F0F0Fu);
         }
       }
-      const int z = (int)((zR[JW] >> ((c & 7) * 4)) & 15u);
-      P -= z * asR[JA];
     } else {
-      // Both halves of the activation codes against this lane's codes (scalar operands
-      // cannot differ between lanes), then keep the half this lane's inputs belong to.
-      int P0 = 0, P1 = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        P0 = __builtin_amdgcn_sdot4(aR[JA][0][i], wR[JW][i >> 2][i & 3], P0, false);
-        P1 = __builtin_amdgcn_sdot4(aR[JA][1][i], wR[JW][i >> 2][i & 3], P1, false);
+      for (int i = 0; i < 16; ++i) wd[i] = wR[JW][i >> 2][i & 3];
+    }
+    const int z = KIND == kW4 ? (int)((zR[JW] >> ((c & 7) * 4)) & 15u) : 0;
+    const float sw = h2f((uint16_t)(sR[JW] >> ((c & 1) * 16)));
+    static_for<0, MT>([&](auto m_c) {
+      constexpr int m = decltype(m_c)::value;
+      constexpr int Q = (U * MT + m) % 2;
+      // the next item: row m + 1 of this step, or row 0 of the next step
+      if constexpr (m + 1 < MT)
+        issue_a(IntC<(Q + 1) % 2>{}, s, m + 1);
+      else if (!last)
+        issue_a(IntC<(Q + 1) % 2>{}, s + 1, 0);
+      int P = 0;
+      if constexpr (KIND == kW4) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) P = __builtin_amdgcn_sdot4(aR[Q][i >> 4][i & 15], wd[i], P, false);
+        P -= z * asR[Q];
+      } else {
+        // Both halves of the activation codes against this lane's codes (scalar operands
+        // cannot differ between lanes), then keep the half this lane's inputs belong to.
+        int P0 = 0, P1 = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          P0 = __builtin_amdgcn_sdot4(aR[Q][0][i], wd[i], P0, false);
+          P1 = __builtin_amdgcn_sdot4(aR[Q][1][i], wd[i], P1, false);
+        }
+        P = kh ? P1 : P0;
       }
-      P = kh ? P1 : P0;
-    }
-    if constexpr (PARTIALS) {
-      if constexpr (KIND == kW8) P += __shfl_xor(P, 32);  // both halves of the inputs
-      const int orig = p.idx[jp];
-      if (!dup && (KIND == kW4 || kh == 0) && orig >= p.n_begin && orig < p.n_begin + p.n_count)
-        p.part[(int64_t)(orig - p.n_begin) * G + grp(s)] = P;
-    } else {
-      const float sw = h2f((uint16_t)(sR[JW] >> ((c & 1) * 16)));
-      acc = fmaf((float)P, sw * saR[JA], acc);
-    }
+      if constexpr (PARTIALS) {
+        if constexpr (KIND == kW8) P += __shfl_xor(P, 32);  // both halves of the inputs
+        const int orig = p.idx[jp];
+        if (!dup && (KIND == kW4 || kh == 0) && orig >= p.n_begin && orig < p.n_begin + p.n_count)
+          p.part[((int64_t)m * p.n_count + (orig - p.n_begin)) * G + grp(s)] = P;
+      } else {
+        acc[m] = fmaf((float)P, sw * saR[Q], acc[m]);
+      }
+    });
   };
 
-  // Prologue: weights of steps 0 .. D - 2, activations of step 0.  The loop is unrolled by
-  // D (a multiple of the activation ring's 2) so every slot index is a constant; the last
-  // cnt % D groups run in an unrolled tail (wave-uniform branches).
+  // Prologue: weights of steps 0 .. D - 2, the first item.  The loop is unrolled by D (even)
+  // so every slot index is a constant; the last cnt % D steps run in an unrolled tail
+  // (wave-uniform branches).
   static_assert(D % 2 == 0, "ring sizes");
-  issue_a(IntC<0>{}, 0);
+  issue_a(IntC<0>{}, 0, 0);
   static_for<0, D - 1>([&](auto t_c) { issue_w(t_c, decltype(t_c)::value); });
   const int nfull = cnt / D * D;
   for (int s = 0; s < nfull; s += D) {
     static_for<0, D>([&](auto j_c) {
       constexpr int J = decltype(j_c)::value;
-      issue_a(IntC<(J + 1) % 2>{}, s + J + 1);
       issue_w(IntC<(J + D - 1) % D>{}, s + J + D - 1);
-      compute(j_c, IntC<J % 2>{}, s + J);
+      compute(j_c, j_c, s + J, false);
     });
   }
   const int rem = cnt - nfull;
   static_for<0, D - 1>([&](auto j_c) {
     constexpr int J = decltype(j_c)::value;
-    if (J < rem) {
-      issue_a(IntC<(J + 1) % 2>{}, nfull + J + 1);
-      compute(j_c, IntC<J % 2>{}, nfull + J);
-    }
+    if (J < rem) compute(j_c, j_c, nfull + J, J + 1 == rem);
   });
 }
 
-template <bool PARTIALS>
-__global__ __launch_bounds__(64 * kGvWaves) void gemm_gemv_kernel(const GemmArgs p, int ks, int nstrip4) {
-  __shared__ float red[kGvWaves][64];
+// Waves per workgroup at most: 16 for one row, 8 (more registers per wave) for more.
+constexpr int gv_max_waves(int mt) { return mt == 1 ? kGvWaves : kGvWaves / 2; }
+
+template <int MT, bool PARTIALS>
+__global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const GemmArgs p, int ks, int nstrip4) {
+  __shared__ float red[gv_max_waves(MT)][MT][64];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int strip = blockIdx.x;
@@ -938,25 +963,32 @@ __global__ __launch_bounds__(64 * kGvWaves) void gemm_gemv_kernel(const GemmArgs
   // (wave-uniform; read back into scalar registers for the loads' scalar offsets)
   const int g0 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * wave / ks));
   const int g1 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * (wave + 1) / ks));
-  float acc = 0.0f;
+  float acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
   if (g1 > g0) {
     if (w4)
-      gemv_body<kW4, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, acc);
+      gemv_body<kW4, MT, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, acc);
     else
-      gemv_body<kW8, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
+      gemv_body<kW8, MT, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
   }
   if (PARTIALS) return;
-  red[wave][lane] = acc;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
   __syncthreads();
   if (wave != 0 || dup || (!w4 && lane >= 32)) return;
-  float v = 0.0f;
-  if (w4) {
-    for (int w = 0; w < ks; ++w) v += red[w][lane];
-  } else {
-    for (int w = 0; w < ks; ++w) v += red[w][lane] + red[w][lane + 32];
-  }
   const int orig = p.idx[(blk0 + second) * 32 + (lane & 31)];
-  if (orig >= 0) p.y[orig] = f2h(v);
+  if (orig < 0) return;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    float v = 0.0f;
+    if (w4) {
+      for (int w = 0; w < ks; ++w) v += red[w][m][lane];
+    } else {
+      for (int w = 0; w < ks; ++w) v += red[w][m][lane] + red[w][m][lane + 32];
+    }
+    p.y[(int64_t)m * p.ldy + orig] = f2h(v);
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -1056,13 +1088,14 @@ int skinny_waves_per_simd_rb(int rb) {
   }
 }
 
-// Waves of the gemv kernel that fit a SIMD at once (its register count, read once).
+// Waves of the gemv kernel for MT rows that fit a SIMD at once (its register count, read once).
+template <int MT>
 int gemv_waves_per_simd() {
   static int cached = 0;
   if (cached == 0) {
     hipFuncAttributes at;
     int regs = 128;
-    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(gemm_gemv_kernel<false>)) == hipSuccess &&
+    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(gemm_gemv_kernel<MT, false>)) == hipSuccess &&
         at.numRegs > 0)
       regs = at.numRegs;
     regs = (regs + 7) / 8 * 8;
@@ -1070,6 +1103,35 @@ int gemv_waves_per_simd() {
     cached = w < 1 ? 1 : (w > 8 ? 8 : w);
   }
   return cached;
+}
+
+int gemv_waves_per_simd_m(int m) {
+  static_assert(kGvMaxRows == 3, "one case per row count");
+  switch (m) {
+    case 1: return gemv_waves_per_simd<1>();
+    case 2: return gemv_waves_per_simd<2>();
+    default: return gemv_waves_per_simd<3>();
+  }
+}
+
+// Waves per workgroup for a grid of nwg workgroups whose waves split G groups into
+// contiguous ranges: the count that minimizes (rounds of workgroups) x (groups per wave),
+// a CU holding floor(wpc / k) workgroups of k waves (wpc: waves per CU the kernel's
+// registers allow).  Ties keep the smaller count (fewer rounds, longer loops).
+int pick_waves(int64_t nwg, int G, int wpc, int kmax, int cus) {
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int k = 1; k <= kmax && k <= G; ++k) {
+    const int per_cu = wpc / k;
+    if (per_cu < 1) break;
+    const int64_t fit = (int64_t)cus * per_cu;
+    const int64_t cost = (nwg + fit - 1) / fit * ((G + k - 1) / k);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = k;
+    }
+  }
+  return best;
 }
 
 // Relative cost per weight byte of the skinny kernel against a full round of the tile
@@ -1088,33 +1150,23 @@ int skinny_cost_pm(int M) {
 Plan make_plan(int M, const mixllm_blob_info &L) {
   Plan pl{};
   const int cus = device_cus() > 0 ? device_cus() : 256;
-  // One token: the gemv kernel, when the layer has enough strips (one workgroup each) to
-  // occupy at least half the CUs; narrower layers run the skinny kernel, whose grid is
-  // twice as fine.
+  // One to three tokens: the gemv kernel, when the layer has enough strips (one workgroup
+  // each) to occupy at least half the CUs; narrower layers run the skinny kernel, whose
+  // grid is twice as fine.  (At four tokens the gemv kernel lost to the tile kernel on
+  // the 70B layers.)
   const int nstrip4 = (L.nb4 + 1) / 2, nstrip = nstrip4 + L.nb8;
-  if (M == 1 && 2 * nstrip >= cus) {
+  if (M <= kGvMaxRows && 2 * nstrip >= cus) {
     pl.gemv = true;
     pl.nstrip4 = nstrip4;
     pl.nstrip = nstrip;
-    // Waves per workgroup: as many as keep the whole grid resident in one round.
-    const int64_t slots = (int64_t)cus * 4 * gemv_waves_per_simd();
-    int64_t ks = slots / pl.nstrip;
-    ks = ks < 1 ? 1 : (ks > kGvWaves ? kGvWaves : ks);
-    pl.ks = (int)(ks > L.G ? L.G : ks);
+    pl.ks = pick_waves(nstrip, L.G, 4 * gemv_waves_per_simd_m(M), gv_max_waves(M), cus);
     return pl;
   }
   const int64_t tiles_n = (L.nb + kTileNB - 1) / kTileNB;
   if (M <= 64 && tiles_n * skinny_cost_pm(M) <= (int64_t)900 * cus) {
     pl.skinny = true;
     pl.rb = (M + 15) / 16;
-    // Split each half block's groups over as many waves as keep the whole grid resident at
-    // once (one round of workgroups), within the workgroup size limit.
-    const int subs = 2 * L.nb;
-    const int64_t slots = (int64_t)cus * 4 * skinny_waves_per_simd_rb(pl.rb);
-    int64_t ks = slots / subs;
-    const int kmax = skinny_max_waves(pl.rb);
-    ks = ks < 1 ? 1 : (ks > kmax ? kmax : ks);
-    pl.ks = (int)(ks > L.G ? L.G : ks);
+    pl.ks = pick_waves(2 * (int64_t)L.nb, L.G, 4 * skinny_waves_per_simd_rb(pl.rb), skinny_max_waves(pl.rb), cus);
     return pl;
   }
   pl.tiles_m = (M + kTileBM - 1) / kTileBM;
@@ -1149,8 +1201,12 @@ template <bool PARTIALS>
 int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
   (void)hipGetLastError();
   if (pl.gemv) {
-    hipLaunchKernelGGL((gemm_gemv_kernel<PARTIALS>), dim3((unsigned)pl.nstrip), dim3((unsigned)(64 * pl.ks)), 0, stream,
-                       a, pl.ks, pl.nstrip4);
+    const dim3 grid((unsigned)pl.nstrip), block((unsigned)(64 * pl.ks));
+    switch (a.M) {
+      case 1: hipLaunchKernelGGL((gemm_gemv_kernel<1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4); break;
+      case 2: hipLaunchKernelGGL((gemm_gemv_kernel<2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4); break;
+      default: hipLaunchKernelGGL((gemm_gemv_kernel<3, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4); break;
+    }
   } else if (pl.skinny) {
     const int ks = pl.ks;
     const dim3 grid((unsigned)(2 * a.nb)), block((unsigned)(64 * ks));
