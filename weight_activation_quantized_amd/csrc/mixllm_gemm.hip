@@ -804,7 +804,10 @@ __global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(
 #define MIXLLM_GV_WAVES 16
 #endif
 constexpr int kGvWaves = MIXLLM_GV_WAVES;  // waves per workgroup at most
-constexpr int kGvRing = 4;   // weight ring: loads 3 groups ahead
+#ifndef MIXLLM_GV_RING
+#define MIXLLM_GV_RING 4
+#endif
+constexpr int kGvRing = MIXLLM_GV_RING;  // weight ring: loads kGvRing - 1 groups ahead
 constexpr int kNonTemporal = 2;  // cache-policy bit nt: the weights are read once
 constexpr int kGvMaxRows = 3;  // tokens the gemv kernel takes
 
