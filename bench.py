@@ -184,8 +184,8 @@ def mlp_main(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the sharding design is described in DESIGN.md)"}))
+        print(json.dumps({"error": "the path runs on one GPU: --gpus must be 1 (a multi-GPU run would "
+                          "shard the output channels; it is not implemented)"}))
         sys.exit(2)
     if args.workload == "mlp":
         return mlp_main(args)
