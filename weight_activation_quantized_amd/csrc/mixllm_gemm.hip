@@ -357,6 +357,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
 #pragma unroll
   for (int r = 0; r < 16; ++r) pinit[r] = (kFoldBias && !PARTIALS) ? kBiasBits : 0;
   const int jp = blk * 32 + ch32;
+  // The channel's original index for the scatter epilogue, loaded now so its latency
+  // overlaps the main loop instead of delaying the final stores.
+  const int orig_out = (!PARTIALS && HASW) ? p.idx[jp] : -1;
 
   auto load_a = [&](auto j_c, int rb, v4i (&av)[4]) {
     constexpr int J = decltype(j_c)::value;
@@ -547,12 +550,11 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     }
     return;
   }
-  const int orig = p.idx[jp];
-  if (orig < 0) return;
+  if (orig_out < 0) return;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = m0 + q * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (row < p.M) p.y[(int64_t)row * p.ldy + orig] = f2h(mine[r]);
+    if (row < p.M) p.y[(int64_t)row * p.ldy + orig_out] = f2h(mine[r]);
   }
 }
 
