@@ -615,19 +615,11 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
 // scalar offset added (the host checks M * K and G * M * 4 stay below it).
 constexpr int kSkinnyOob = 0x7FFFFF00;
 
-#ifndef MIXLLM_SK_WR2
-#define MIXLLM_SK_WR2 4
-#endif
-#ifndef MIXLLM_SK_AR34
-#define MIXLLM_SK_AR34 2
-#endif
-#ifndef MIXLLM_SK_AR2
-#define MIXLLM_SK_AR2 4
-#endif
-constexpr int skinny_wring(int rb, int kind) {
-  return rb == 1 && kind == kW4 ? 8 : (rb == 2 && kind == kW4 ? MIXLLM_SK_WR2 : 4);
-}
-constexpr int skinny_aring(int rb) { return rb == 1 ? 8 : (rb == 2 ? MIXLLM_SK_AR2 : MIXLLM_SK_AR34); }
+// Ring depths (measured on the Llama-3.1 8B and 70B layers): weights 8 groups for one
+// 16-row block of 4-bit codes, else 4; activations 8 for one block, 4 for two, 2 for three
+// or four (deeper rings spill there).
+constexpr int skinny_wring(int rb, int kind) { return rb == 1 && kind == kW4 ? 8 : 4; }
+constexpr int skinny_aring(int rb) { return rb == 1 ? 8 : (rb == 2 ? 4 : 2); }
 
 template <int RB, int KIND, bool PARTIALS>
 __device__ __forceinline__ void skinny_body(const GemmArgs &p, int blk, int half, int lane, int g0, int cnt,
@@ -746,10 +738,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs &p, int blk, int half
   });
 }
 
-#ifndef MIXLLM_SK_MAXW2
-#define MIXLLM_SK_MAXW2 8
-#endif
-constexpr int skinny_max_waves(int rb) { return rb == 2 ? MIXLLM_SK_MAXW2 : 8; }
+constexpr int skinny_max_waves(int) { return 8; }  // waves per workgroup (up to 256 VGPRs each)
 
 template <int RB, bool PARTIALS>
 __global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(const GemmArgs p, int ks) {
@@ -802,14 +791,8 @@ __global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(
 // through LDS in a fixed order.  The vector memory path carries only weights and their
 // scale and zero-point words, so the kernel is bound by the weight stream.
 // ------------------------------------------------------------------------------------
-#ifndef MIXLLM_GV_WAVES
-#define MIXLLM_GV_WAVES 16
-#endif
-constexpr int kGvWaves = MIXLLM_GV_WAVES;  // waves per workgroup at most
-#ifndef MIXLLM_GV_RING
-#define MIXLLM_GV_RING 4
-#endif
-constexpr int kGvRing = MIXLLM_GV_RING;  // weight ring: loads kGvRing - 1 groups ahead
+constexpr int kGvWaves = 16;  // waves per workgroup at most
+constexpr int kGvRing = 4;    // weight ring: loads 3 groups ahead
 constexpr int kNonTemporal = 2;  // cache-policy bit nt: the weights are read once
 constexpr int kGvMaxRows = 3;  // tokens the gemv kernel takes
 
