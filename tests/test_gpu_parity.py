@@ -98,10 +98,11 @@ SMALL = [
     (160, 288, 1920, 40), (96, 130, 2688, 13),
     # M <= 64 on layers wide enough (on a 256-CU part) for the tile kernel's cost rule
     (48, 12800, 256, 1280), (20, 16448, 128, 100), (1, 29000, 128, 290),
-    # M = 1 .. 3 on layers wide enough for the one-lane-per-channel kernel: an odd or even
-    # number of 4-bit blocks, promoted 4-bit channels, several groups per wave and a
-    # ragged tail, or only the tail (and M = 4 on the same layer, the next kernel)
+    # M = 1 .. 3 on layers wide enough for the one-lane-per-channel kernel, and 4 .. 16 for
+    # the strip kernel: an odd or even number of 4-bit blocks, promoted 4-bit channels,
+    # several groups per wave and a ragged tail, or only the tail; ragged M
     (1, 16448, 8960, 1608), (2, 16448, 8960, 1608), (3, 16448, 2688, 1640), (4, 16448, 8960, 1608),
+    (9, 16448, 4480, 1608), (16, 16448, 1152, 1640),
 ]
 
 

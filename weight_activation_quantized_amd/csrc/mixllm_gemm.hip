@@ -980,6 +980,200 @@ __global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const 
 }
 
 // ------------------------------------------------------------------------------------
+// Strip kernel (4 <= M <= 16 on wide layers).  A wave owns a strip of channels (two
+// 4-bit blocks, or one 8-bit block) and all M rows, as 16 x 16 tiles of
+// v_mfma_i32_16x16x64_i8: it loads a group's activation operands once and reuses them for
+// its four (4-bit) or two (8-bit) 16-channel column tiles, so the activation reads per
+// channel are a quarter of the skinny kernel's.  The 4-bit codes go to the matrix cores
+// raw and the zero point enters as - z * S_A on the exact integer partial.  Weights pass
+// through a register ring 3 groups ahead, activations, s_a and S_A one group ahead; the
+// workgroup's waves split the groups and reduce through LDS in a fixed order.
+// ------------------------------------------------------------------------------------
+constexpr int kStWaves = 8;  // waves per workgroup at most
+constexpr int kStRing = 4;   // weight ring: loads 3 groups ahead
+constexpr int kStARing = 2;  // activation ring: one group ahead (a deeper one spills)
+
+// NT column tiles: 4-bit strips hold blocks blk0 and blk0 + second (tiles 2 and 3 repeat
+// tiles 0 and 1 when the strip has one block: dup); 8-bit strips hold block blk0.
+template <int KIND, bool PARTIALS>
+__device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
+                                           int cnt, float (&acc)[4][4]) {
+  constexpr int NT = KIND == kW8 ? 2 : 4;
+  constexpr int D = kStRing;
+  constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
+  const int ch = lane & 15, qd = lane >> 4;
+  const int G = p.G, M = p.M;
+  const int bq = KIND == kW8 ? blk0 - p.nb4 : blk0;
+  const Rsrc rw = make_rsrc((KIND == kW8 ? p.w8 : p.w4) + (size_t)bq * G * kWChunk, (int64_t)2 * G * kWChunk);
+  const Rsrc rs = make_rsrc((KIND == kW8 ? p.s8 : p.s4) + (size_t)bq * G * 32, (int64_t)2 * G * 64);
+  const Rsrc rz = make_rsrc(p.z4 + (size_t)bq * G * kZ4Chunk, KIND == kW4 ? (int64_t)2 * G * kZ4Chunk : 0);
+  const Rsrc ra = make_rsrc(p.aq, (int64_t)M * p.K);
+  const Rsrc rsa = make_rsrc(p.sa, (int64_t)G * M * 4);
+  const Rsrc ras = make_rsrc(p.asum, KIND == kW4 ? (int64_t)G * M * 4 : 0);
+  // Column tile t: block offset bo(t) (in blocks from blk0) and half ht(t) of it.
+  auto bo = [&](int t) { return KIND == kW8 ? 0 : (t >> 1) * second; };
+  auto ht = [&](int t) { return KIND == kW8 ? t : (t & 1); };
+  // Per-lane offsets.  Rows past M load from past every descriptor (zeros, no traffic).
+  const int row = ch;
+  int va[2], vsa[4];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) va[c] = row < M ? row * p.K + (qd + 4 * c) * 16 : kSkinnyOob;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vsa[r] = 4 * qd + r < M ? (4 * qd + r) * 4 : kSkinnyOob;
+
+  v4i wR[D][NT][KIND == kW8 ? 2 : 1];
+  uint32_t sR[D][NT], zR[D][NT];
+  constexpr int DA = kStARing;
+  static_assert(D % DA == 0, "ring sizes");
+  v4i aR[DA][2];
+  float saR[DA][4];
+  int asR[DA][4];
+  auto grp = [&](int s) { return g0 + min(s, cnt - 1); };
+  auto issue_a = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    const int g = grp(s);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) aR[J][c] = bload16(ra, va[c], g * 128);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      saR[J][r] = __uint_as_float(bload4(rsa, vsa[r], g * M * 4));
+      if constexpr (KIND == kW4) asR[J][r] = (int)bload4(ras, vsa[r], g * M * 4);
+    }
+  };
+  auto issue_w = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    const int g = grp(s);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int cw = ht(t) * 16 + ch;  // the lane's channel within its block
+      if constexpr (KIND == kW8) {
+#pragma unroll
+        for (int mf = 0; mf < 2; ++mf)
+          wR[J][t][mf] = bload16(rw, ht(t) * 2048 + mf * 1024 + lane * 16, g * kWChunk);
+      } else {
+        wR[J][t][0] = bload16(rw, bo(t) * G * kWChunk + ht(t) * 1024 + lane * 16, g * kWChunk);
+        zR[J][t] = bload4(rz, bo(t) * G * (int)kZ4Chunk + (cw >> 3) * 4, g * (int)kZ4Chunk);
+      }
+      sR[J][t] = bload4(rs, bo(t) * G * 64 + (cw >> 1) * 4, g * 64);
+    }
+  };
+  auto compute = [&](auto jw_c, auto ja_c, int s) {
+    constexpr int JW = decltype(jw_c)::value, JA = decltype(ja_c)::value;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int cw = ht(t) * 16 + ch;
+      v4i b0, b1;
+      if constexpr (KIND == kW4) {
+        const v4i x = wR[JW][t][0];
+        const uint32_t x0 = (uint32_t)x[0], x1 = (uint32_t)x[1], x2 = (uint32_t)x[2], x3 = (uint32_t)x[3];
+        b0 = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
+                 (int)((x1 >> 4) & 0x0F0F0F0Fu)};
+        b1 = v4i{(int)(x2 & 0x0F0F0F0Fu), (int)((x2 >> 4) & 0x0F0F0F0Fu), (int)(x3 & 0x0F0F0F0Fu),
+                 (int)((x3 >> 4) & 0x0F0F0F0Fu)};
+      } else {
+        b0 = wR[JW][t][0];
+        b1 = wR[JW][t][1];
+      }
+      v4i P = __builtin_amdgcn_mfma_i32_16x16x64_i8(aR[JA][0], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+      P = __builtin_amdgcn_mfma_i32_16x16x64_i8(aR[JA][1], b1, P, 0, 0, 0);
+      if constexpr (KIND == kW4) {
+        const int z = (int)((zR[JW][t] >> ((cw & 7) * 4)) & 15u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[r] -= z * asR[JA][r];
+      }
+      if constexpr (PARTIALS) {
+        const int orig = p.idx[(blk0 + bo(t)) * 32 + cw];
+        if (!(dup && t >= 2) && orig >= p.n_begin && orig < p.n_begin + p.n_count) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * qd + r < M) p.part[((int64_t)(4 * qd + r) * p.n_count + (orig - p.n_begin)) * G + grp(s)] = P[r];
+        }
+      } else {
+        const float sw = h2f((uint16_t)(sR[JW][t] >> ((cw & 1) * 16)));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)P[r], sw * saR[JA][r], acc[t][r]);
+      }
+    }
+  };
+
+  // Prologue: the loads of the steps before step 0 in the order they issue them
+  // (activations DA - 1 steps ahead, then weights D - 1 ahead).  The loop is unrolled by D
+  // so every slot index is a constant; the last cnt % D steps run in an unrolled tail
+  // (wave-uniform branches).
+  static_for<0, D - 1>([&](auto t_c) {
+    constexpr int T = decltype(t_c)::value - (D - 1);  // steps -(D - 1) .. -1
+    if constexpr (T + DA - 1 >= 0) issue_a(IntC<(T + DA - 1) % DA>{}, T + DA - 1);
+    issue_w(IntC<T + D - 1>{}, T + D - 1);
+  });
+  const int nfull = cnt / D * D;
+  for (int s = 0; s < nfull; s += D) {
+    static_for<0, D>([&](auto j_c) {
+      constexpr int J = decltype(j_c)::value;
+      issue_a(IntC<(J + DA - 1) % DA>{}, s + J + DA - 1);
+      issue_w(IntC<(J + D - 1) % D>{}, s + J + D - 1);
+      compute(j_c, IntC<J % DA>{}, s + J);
+    });
+  }
+  const int rem = cnt - nfull;
+  static_for<0, D - 1>([&](auto j_c) {
+    constexpr int J = decltype(j_c)::value;
+    if (J < rem) {
+      if constexpr (DA < D) issue_a(IntC<(J + DA - 1) % DA>{}, nfull + J + DA - 1);
+      compute(j_c, IntC<J % DA>{}, nfull + J);
+    }
+  });
+}
+
+template <bool PARTIALS>
+__global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArgs p, int ks, int nstrip4) {
+  __shared__ float red[kStWaves][16][64];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int strip = blockIdx.x;
+  // Strips [0, nstrip4) pair the 4-bit blocks (an odd count leaves the last strip one
+  // block, repeated in tiles 2 and 3); the others hold one 8-bit block each.
+  const bool w4 = strip < nstrip4;
+  const int blk0 = w4 ? 2 * strip : p.nb4 + (strip - nstrip4);
+  const bool dup = w4 && p.nb4 - blk0 < 2;
+  const int second = w4 && !dup ? 1 : 0;
+  const int G = p.G;
+  // (wave-uniform; read back into scalar registers for the loads' scalar offsets)
+  const int g0 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * wave / ks));
+  const int g1 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * (wave + 1) / ks));
+  float acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+  if (g1 > g0) {
+    if (w4)
+      strip_body<kW4, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, acc);
+    else
+      strip_body<kW8, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
+  }
+  if (PARTIALS) return;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][t * 4 + r][lane] = acc[t][r];
+  __syncthreads();
+  // Output: the workgroup's waves share the 16 (tile, row) slots; each sums its slot over
+  // the waves in order and writes the row's channel.
+  const int nt = w4 ? (dup ? 2 : 4) : 2;
+  const int ch = lane & 15, qd = lane >> 4;
+  for (int e = wave; e < 16; e += ks) {
+    const int t = e >> 2, r = e & 3;
+    const int rowo = 4 * qd + r;
+    if (t >= nt || rowo >= p.M) continue;
+    float v = 0.0f;
+    for (int w = 0; w < ks; ++w) v += red[w][e][lane];
+    const int cw = (w4 ? (t & 1) : t) * 16 + ch;
+    const int orig = p.idx[(blk0 + (w4 ? (t >> 1) : 0)) * 32 + cw];
+    if (orig >= 0) p.y[(int64_t)rowo * p.ldy + orig] = f2h(v);
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------
 
@@ -1042,7 +1236,8 @@ int device_cus() {
 
 // Launch plan of one GEMM call, a pure function of the shape.
 struct Plan {
-  bool gemv;                   // M = 1: the one-lane-per-channel kernel
+  bool gemv;                   // M <= 3: the one-lane-per-channel kernel
+  bool strip;                  // 4 <= M <= 16 on wide layers: the 64-channel strip kernel
   int nstrip4, nstrip;         // gemv: strips of 4-bit blocks, all strips
   bool skinny;
   int rb;                      // skinny: 16-row blocks
@@ -1074,6 +1269,22 @@ int skinny_waves_per_simd_rb(int rb) {
     case 3: return skinny_waves_per_simd<3>();
     default: return skinny_waves_per_simd<4>();
   }
+}
+
+// Waves of the strip kernel that fit a SIMD at once (its register count, read once).
+int strip_waves_per_simd() {
+  static int cached = 0;
+  if (cached == 0) {
+    hipFuncAttributes at;
+    int regs = 128;
+    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(gemm_strip_kernel<false>)) == hipSuccess &&
+        at.numRegs > 0)
+      regs = at.numRegs;
+    regs = (regs + 7) / 8 * 8;
+    const int w = 512 / regs;
+    cached = w < 1 ? 1 : (w > 8 ? 8 : w);
+  }
+  return cached;
 }
 
 // Waves of the gemv kernel for MT rows that fit a SIMD at once (its register count, read once).
@@ -1150,6 +1361,16 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
     pl.ks = pick_waves(nstrip, L.G, 4 * gemv_waves_per_simd_m(M), gv_max_waves(M), cus);
     return pl;
   }
+  // Up to 16 tokens on layers with a strip (one workgroup) for at least 3/4 of the CUs:
+  // the strip kernel (its registers allow one 8-wave workgroup per CU, so a narrower
+  // layer would leave CUs idle; the skinny kernel's grid is finer).
+  if (M <= 16 && 4 * (int64_t)nstrip >= 3 * (int64_t)cus) {
+    pl.strip = true;
+    pl.nstrip4 = nstrip4;
+    pl.nstrip = nstrip;
+    pl.ks = pick_waves(nstrip, L.G, 4 * strip_waves_per_simd(), kStWaves, cus);
+    return pl;
+  }
   const int64_t tiles_n = (L.nb + kTileNB - 1) / kTileNB;
   if (M <= 64 && tiles_n * skinny_cost_pm(M) <= (int64_t)900 * cus) {
     pl.skinny = true;
@@ -1182,7 +1403,9 @@ bool skinny_offsets_fit(int M, const mixllm_blob_info &L) {
 bool gemv_offsets_fit(const mixllm_blob_info &L) { return (int64_t)(2 * L.G + 1) * (int64_t)kW8Chunk <= 0x7FFFFFFF; }
 
 bool offsets_fit(const Plan &pl, int M, const mixllm_blob_info &L) {
-  return pl.gemv ? gemv_offsets_fit(L) : (pl.skinny ? skinny_offsets_fit(M, L) : tile_offsets_fit(M, L));
+  if (pl.gemv) return gemv_offsets_fit(L);
+  if (pl.strip) return gemv_offsets_fit(L) && skinny_offsets_fit(M, L);
+  return pl.skinny ? skinny_offsets_fit(M, L) : tile_offsets_fit(M, L);
 }
 
 template <bool PARTIALS>
@@ -1195,6 +1418,9 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
       case 2: hipLaunchKernelGGL((gemm_gemv_kernel<2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4); break;
       default: hipLaunchKernelGGL((gemm_gemv_kernel<3, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4); break;
     }
+  } else if (pl.strip) {
+    hipLaunchKernelGGL((gemm_strip_kernel<PARTIALS>), dim3((unsigned)pl.nstrip), dim3((unsigned)(64 * pl.ks)), 0,
+                       stream, a, pl.ks, pl.nstrip4);
   } else if (pl.skinny) {
     const int ks = pl.ks;
     const dim3 grid((unsigned)(2 * a.nb)), block((unsigned)(64 * ks));
