@@ -986,21 +986,41 @@ __global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const 
 // its four (4-bit) or two (8-bit) 16-channel column tiles, so the activation reads per
 // channel are a quarter of the skinny kernel's.  The 4-bit codes go to the matrix cores
 // raw and the zero point enters as - z * S_A on the exact integer partial.  Weights pass
-// through a register ring 3 groups ahead, activations, s_a and S_A one group ahead; the
+// through a register ring and the activation codes, s_a and S_A through an LDS ring (its
+// own stages per wave, filled by direct-to-LDS loads), both 3 groups ahead; the
 // workgroup's waves split the groups and reduce through LDS in a fixed order.
 // ------------------------------------------------------------------------------------
 constexpr int kStWaves = 8;  // waves per workgroup at most
-constexpr int kStRing = 4;   // weight ring: loads 3 groups ahead
-constexpr int kStARing = 2;  // activation ring: one group ahead (a deeper one spills)
+constexpr int kStRing = 4;   // weight ring (registers) and activation ring (LDS): 3 groups ahead
+// LDS stage of a wave: the group's activation codes [16 rows][128 B] (chunk c of row r at
+// position c ^ (r & 7)), then s_a and S_A of the 16 rows (4 B each, 256 B areas).
+constexpr int kStStage = 2048 + 256 + 256;
+constexpr int kStLds = kStWaves * kStRing * kStStage;
+static_assert(kStLds >= kStWaves * 16 * 64 * 4, "the reduction reuses the stage space");
+
+__device__ __forceinline__ void bload4_lds(Rsrc r, void *dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)dst, 4, voff, soff, 0, 0);
+}
 
 // NT column tiles: 4-bit strips hold blocks blk0 and blk0 + second (tiles 2 and 3 repeat
-// tiles 0 and 1 when the strip has one block: dup); 8-bit strips hold block blk0.
+// tiles 0 and 1 when the strip has one block: dup); 8-bit strips hold block blk0.  `lds`
+// is this wave's ring of kStRing stages.
 template <int KIND, bool PARTIALS>
 __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
-                                           int cnt, float (&acc)[4][4]) {
+                                           int cnt, uint8_t *lds, float (&acc)[4][4]) {
   constexpr int NT = KIND == kW8 ? 2 : 4;
   constexpr int D = kStRing;
   constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
+  // Vector-memory operations per step: the stage's direct-to-LDS loads, then the weight
+  // ring's loads.  When step s computes, the loads issued after step s's stage are the
+  // weight batch of the step that issued it and D - 1 full batches; a wait for at most
+  // that many outstanding proves the stage has landed (the compiler does not track LDS
+  // written by these loads).
+  constexpr int LA = KIND == kW4 ? 4 : 3;
+  constexpr int LW = 3 * NT;  // per column tile: codes (or two loads of 8-bit codes) and scale
+                              // word, plus the zero-point word for 4-bit
+  constexpr int WAIT = LW + (D - 1) * (LA + LW);
+  static_assert(WAIT < 64, "vmcnt range");
   const int ch = lane & 15, qd = lane >> 4;
   const int G = p.G, M = p.M;
   const int bq = KIND == kW8 ? blk0 - p.nb4 : blk0;
@@ -1013,32 +1033,32 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
   // Column tile t: block offset bo(t) (in blocks from blk0) and half ht(t) of it.
   auto bo = [&](int t) { return KIND == kW8 ? 0 : (t >> 1) * second; };
   auto ht = [&](int t) { return KIND == kW8 ? t : (t & 1); };
-  // Per-lane offsets.  Rows past M load from past every descriptor (zeros, no traffic).
-  const int row = ch;
-  int va[2], vsa[4];
+  // Direct-to-LDS offsets: load i of a stage fills rows 8i .. 8i + 7 (lane l: row
+  // 8i + l / 8, position l % 8, which holds chunk (l % 8) ^ (row & 7)); the scale loads
+  // fill row l's word.  Rows past M load from past every descriptor (zeros, no traffic).
+  int vdma[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) va[c] = row < M ? row * p.K + (qd + 4 * c) * 16 : kSkinnyOob;
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    vdma[i] = r < M ? r * p.K + (((lane & 7) ^ (r & 7)) << 4) : kSkinnyOob;
+  }
+  const int vrow = lane < M ? lane * 4 : kSkinnyOob;
+  // LDS offsets of this lane's MFMA operands: row ch, chunks qd and qd + 4.
+  int va[2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) vsa[r] = 4 * qd + r < M ? (4 * qd + r) * 4 : kSkinnyOob;
+  for (int c = 0; c < 2; ++c) va[c] = ch * 128 + (((qd + 4 * c) ^ (ch & 7)) << 4);
 
   v4i wR[D][NT][KIND == kW8 ? 2 : 1];
   uint32_t sR[D][NT], zR[D][NT];
-  constexpr int DA = kStARing;
-  static_assert(D % DA == 0, "ring sizes");
-  v4i aR[DA][2];
-  float saR[DA][4];
-  int asR[DA][4];
   auto grp = [&](int s) { return g0 + min(s, cnt - 1); };
   auto issue_a = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
     const int g = grp(s);
+    uint8_t *st = lds + J * kStStage;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) aR[J][c] = bload16(ra, va[c], g * 128);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      saR[J][r] = __uint_as_float(bload4(rsa, vsa[r], g * M * 4));
-      if constexpr (KIND == kW4) asR[J][r] = (int)bload4(ras, vsa[r], g * M * 4);
-    }
+    for (int i = 0; i < 2; ++i) bload16_lds(ra, st + i * 1024, vdma[i], g * 128);
+    bload4_lds(rsa, st + 2048, vrow, g * M * 4);
+    if constexpr (KIND == kW4) bload4_lds(ras, st + 2304, vrow, g * M * 4);
   };
   auto issue_w = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
@@ -1057,29 +1077,43 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
       sR[J][t] = bload4(rs, bo(t) * G * 64 + (cw >> 1) * 4, g * 64);
     }
   };
-  auto compute = [&](auto jw_c, auto ja_c, int s) {
-    constexpr int JW = decltype(jw_c)::value, JA = decltype(ja_c)::value;
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto compute = [&](auto j_c, int s, bool tail) {
+    constexpr int J = decltype(j_c)::value;
+    // This step's stage has landed.  In the tail, where no later loads follow, and in the
+    // partials mode, whose stores count too and which drops the unused scale loads, wait
+    // for everything.
+    if (tail || PARTIALS)
+      wait_vm<0>();
+    else
+      wait_vm<WAIT>();
+    fence();
+    const uint8_t *st = lds + J * kStStage;
+    const v4i a0 = *reinterpret_cast<const v4i *>(st + va[0]);
+    const v4i a1 = *reinterpret_cast<const v4i *>(st + va[1]);
+    const v4i sa4 = *reinterpret_cast<const v4i *>(st + 2048 + qd * 16);
+    const v4i as4 = KIND == kW4 ? *reinterpret_cast<const v4i *>(st + 2304 + qd * 16) : v4i{0, 0, 0, 0};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cw = ht(t) * 16 + ch;
       v4i b0, b1;
       if constexpr (KIND == kW4) {
-        const v4i x = wR[JW][t][0];
+        const v4i x = wR[J][t][0];
         const uint32_t x0 = (uint32_t)x[0], x1 = (uint32_t)x[1], x2 = (uint32_t)x[2], x3 = (uint32_t)x[3];
         b0 = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
                  (int)((x1 >> 4) & 0x0F0F0F0Fu)};
         b1 = v4i{(int)(x2 & 0x0F0F0F0Fu), (int)((x2 >> 4) & 0x0F0F0F0Fu), (int)(x3 & 0x0F0F0F0Fu),
                  (int)((x3 >> 4) & 0x0F0F0F0Fu)};
       } else {
-        b0 = wR[JW][t][0];
-        b1 = wR[JW][t][1];
+        b0 = wR[J][t][0];
+        b1 = wR[J][t][1];
       }
-      v4i P = __builtin_amdgcn_mfma_i32_16x16x64_i8(aR[JA][0], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-      P = __builtin_amdgcn_mfma_i32_16x16x64_i8(aR[JA][1], b1, P, 0, 0, 0);
+      v4i P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+      P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, P, 0, 0, 0);
       if constexpr (KIND == kW4) {
-        const int z = (int)((zR[JW][t] >> ((cw & 7) * 4)) & 15u);
+        const int z = (int)((zR[J][t] >> ((cw & 7) * 4)) & 15u);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) P[r] -= z * asR[JA][r];
+        for (int r = 0; r < 4; ++r) P[r] -= z * as4[r];
       }
       if constexpr (PARTIALS) {
         const int orig = p.idx[(blk0 + bo(t)) * 32 + cw];
@@ -1089,44 +1123,44 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
             if (4 * qd + r < M) p.part[((int64_t)(4 * qd + r) * p.n_count + (orig - p.n_begin)) * G + grp(s)] = P[r];
         }
       } else {
-        const float sw = h2f((uint16_t)(sR[JW][t] >> ((cw & 1) * 16)));
+        const float sw = h2f((uint16_t)(sR[J][t] >> ((cw & 1) * 16)));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)P[r], sw * saR[JA][r], acc[t][r]);
+        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)P[r], sw * __int_as_float(sa4[r]), acc[t][r]);
       }
     }
+    fence();
   };
 
-  // Prologue: the loads of the steps before step 0 in the order they issue them
-  // (activations DA - 1 steps ahead, then weights D - 1 ahead).  The loop is unrolled by D
-  // so every slot index is a constant; the last cnt % D steps run in an unrolled tail
-  // (wave-uniform branches).
+  // Prologue: the loads of steps 0 .. D - 2, stage then weights per step, the order the
+  // loop issues them in.  The loop is unrolled by D so every slot index is a constant; the
+  // last cnt % D steps run in an unrolled tail (wave-uniform branches).  A step's loads
+  // refill the slots of the previous step, whose LDS reads completed before its matrix
+  // operations were issued.
   static_for<0, D - 1>([&](auto t_c) {
-    constexpr int T = decltype(t_c)::value - (D - 1);  // steps -(D - 1) .. -1
-    if constexpr (T + DA - 1 >= 0) issue_a(IntC<(T + DA - 1) % DA>{}, T + DA - 1);
-    issue_w(IntC<T + D - 1>{}, T + D - 1);
+    issue_a(t_c, decltype(t_c)::value);
+    issue_w(t_c, decltype(t_c)::value);
   });
   const int nfull = cnt / D * D;
   for (int s = 0; s < nfull; s += D) {
     static_for<0, D>([&](auto j_c) {
       constexpr int J = decltype(j_c)::value;
-      issue_a(IntC<(J + DA - 1) % DA>{}, s + J + DA - 1);
+      fence();
+      issue_a(IntC<(J + D - 1) % D>{}, s + J + D - 1);
       issue_w(IntC<(J + D - 1) % D>{}, s + J + D - 1);
-      compute(j_c, IntC<J % DA>{}, s + J);
+      compute(j_c, s + J, false);
     });
   }
   const int rem = cnt - nfull;
   static_for<0, D - 1>([&](auto j_c) {
     constexpr int J = decltype(j_c)::value;
-    if (J < rem) {
-      if constexpr (DA < D) issue_a(IntC<(J + DA - 1) % DA>{}, nfull + J + DA - 1);
-      compute(j_c, IntC<J % DA>{}, nfull + J);
-    }
+    if (J < rem) compute(j_c, nfull + J, true);
   });
+  wait_vm<0>();  // no load into this wave's stages is in flight past here
 }
 
 template <bool PARTIALS>
 __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArgs p, int ks, int nstrip4) {
-  __shared__ float red[kStWaves][16][64];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStLds];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int strip = blockIdx.x;
@@ -1140,6 +1174,7 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
   // (wave-uniform; read back into scalar registers for the loads' scalar offsets)
   const int g0 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * wave / ks));
   const int g1 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * (wave + 1) / ks));
+  uint8_t *lds = smem + wave * kStRing * kStStage;
   float acc[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -1147,11 +1182,13 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
     for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
   if (g1 > g0) {
     if (w4)
-      strip_body<kW4, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, acc);
+      strip_body<kW4, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, lds, acc);
     else
-      strip_body<kW8, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
+      strip_body<kW8, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, lds, acc);
   }
   if (PARTIALS) return;
+  __syncthreads();  // every wave's stages are done; the space becomes the reduction area
+  float(*red)[16][64] = reinterpret_cast<float(*)[16][64]>(smem);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
