@@ -103,6 +103,8 @@ SMALL = [
     # several groups per wave and a ragged tail, or only the tail; ragged M
     (1, 16448, 8960, 1608), (2, 16448, 8960, 1608), (3, 16448, 2688, 1640), (4, 16448, 8960, 1608),
     (9, 16448, 4480, 1608), (16, 16448, 1152, 1640),
+    # the strip kernel with one 4-bit block per strip (layers with 3/4 as many blocks as CUs)
+    (8, 8192, 2688, 820), (13, 6400, 1152, 640),
 ]
 
 

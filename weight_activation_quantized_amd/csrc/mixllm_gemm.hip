@@ -1002,13 +1002,13 @@ __device__ __forceinline__ void bload4_lds(Rsrc r, void *dst, int voff, int soff
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)dst, 4, voff, soff, 0, 0);
 }
 
-// NT column tiles: 4-bit strips hold blocks blk0 and blk0 + second (tiles 2 and 3 repeat
-// tiles 0 and 1 when the strip has one block: dup); 8-bit strips hold block blk0.  `lds`
-// is this wave's ring of kStRing stages.
-template <int KIND, bool PARTIALS>
+// NT column tiles: with SB = 2, 4-bit strips hold blocks blk0 and blk0 + second (tiles 2
+// and 3 repeat tiles 0 and 1 when the strip has one block: dup); otherwise a strip is
+// block blk0.  `lds` is this wave's ring of kStRing stages.
+template <int KIND, int SB, bool PARTIALS>
 __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
                                            int cnt, uint8_t *lds, float (&acc)[4][4]) {
-  constexpr int NT = KIND == kW8 ? 2 : 4;
+  constexpr int NT = (KIND == kW8 || SB == 1) ? 2 : 4;
   constexpr int D = kStRing;
   constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
   // Vector-memory operations per step: the stage's direct-to-LDS loads, then the weight
@@ -1031,8 +1031,8 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
   const Rsrc rsa = make_rsrc(p.sa, (int64_t)G * M * 4);
   const Rsrc ras = make_rsrc(p.asum, KIND == kW4 ? (int64_t)G * M * 4 : 0);
   // Column tile t: block offset bo(t) (in blocks from blk0) and half ht(t) of it.
-  auto bo = [&](int t) { return KIND == kW8 ? 0 : (t >> 1) * second; };
-  auto ht = [&](int t) { return KIND == kW8 ? t : (t & 1); };
+  auto bo = [&](int t) { return NT == 2 ? 0 : (t >> 1) * second; };
+  auto ht = [&](int t) { return NT == 2 ? t : (t & 1); };
   // Direct-to-LDS offsets: load i of a stage fills rows 8i .. 8i + 7 (lane l: row
   // 8i + l / 8, position l % 8, which holds chunk (l % 8) ^ (row & 7)); the scale loads
   // fill row l's word.  Rows past M load from past every descriptor (zeros, no traffic).
@@ -1158,18 +1158,19 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
   wait_vm<0>();  // no load into this wave's stages is in flight past here
 }
 
-template <bool PARTIALS>
+// SB: 4-bit blocks per strip (2 on wide layers; 1 doubles the strips of narrower ones).
+template <int SB, bool PARTIALS>
 __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArgs p, int ks, int nstrip4) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStLds];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int strip = blockIdx.x;
-  // Strips [0, nstrip4) pair the 4-bit blocks (an odd count leaves the last strip one
-  // block, repeated in tiles 2 and 3); the others hold one 8-bit block each.
+  // Strips [0, nstrip4) hold SB 4-bit blocks each (with SB = 2 an odd count leaves the
+  // last strip one block, repeated in tiles 2 and 3); the others one 8-bit block each.
   const bool w4 = strip < nstrip4;
-  const int blk0 = w4 ? 2 * strip : p.nb4 + (strip - nstrip4);
-  const bool dup = w4 && p.nb4 - blk0 < 2;
-  const int second = w4 && !dup ? 1 : 0;
+  const int blk0 = w4 ? SB * strip : p.nb4 + (strip - nstrip4);
+  const bool dup = SB == 2 && w4 && p.nb4 - blk0 < 2;
+  const int second = SB == 2 && w4 && !dup ? 1 : 0;
   const int G = p.G;
   // (wave-uniform; read back into scalar registers for the loads' scalar offsets)
   const int g0 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * wave / ks));
@@ -1182,9 +1183,9 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
     for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
   if (g1 > g0) {
     if (w4)
-      strip_body<kW4, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, lds, acc);
+      strip_body<kW4, SB, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, lds, acc);
     else
-      strip_body<kW8, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, lds, acc);
+      strip_body<kW8, SB, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, lds, acc);
   }
   if (PARTIALS) return;
   __syncthreads();  // every wave's stages are done; the space becomes the reduction area
@@ -1196,7 +1197,8 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
   __syncthreads();
   // Output: the workgroup's waves share the 16 (tile, row) slots; each sums its slot over
   // the waves in order and writes the row's channel.
-  const int nt = w4 ? (dup ? 2 : 4) : 2;
+  const bool four = SB == 2 && w4;  // four column tiles (two blocks)
+  const int nt = four && !dup ? 4 : 2;
   const int ch = lane & 15, qd = lane >> 4;
   for (int e = wave; e < 16; e += ks) {
     const int t = e >> 2, r = e & 3;
@@ -1204,8 +1206,8 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
     if (t >= nt || rowo >= p.M) continue;
     float v = 0.0f;
     for (int w = 0; w < ks; ++w) v += red[w][e][lane];
-    const int cw = (w4 ? (t & 1) : t) * 16 + ch;
-    const int orig = p.idx[(blk0 + (w4 ? (t >> 1) : 0)) * 32 + cw];
+    const int cw = (four ? (t & 1) : t) * 16 + ch;
+    const int orig = p.idx[(blk0 + (four ? (t >> 1) : 0)) * 32 + cw];
     if (orig >= 0) p.y[(int64_t)rowo * p.ldy + orig] = f2h(v);
   }
 }
@@ -1274,7 +1276,8 @@ int device_cus() {
 // Launch plan of one GEMM call, a pure function of the shape.
 struct Plan {
   bool gemv;                   // M <= 3: the one-lane-per-channel kernel
-  bool strip;                  // 4 <= M <= 16 on wide layers: the 64-channel strip kernel
+  bool strip;                  // 4 <= M <= 16 on wide layers: the strip kernel
+  int sb;                      // strip: 4-bit blocks per strip
   int nstrip4, nstrip;         // gemv: strips of 4-bit blocks, all strips
   bool skinny;
   int rb;                      // skinny: 16-row blocks
@@ -1309,12 +1312,13 @@ int skinny_waves_per_simd_rb(int rb) {
 }
 
 // Waves of the strip kernel that fit a SIMD at once (its register count, read once).
-int strip_waves_per_simd() {
+template <int SB>
+int strip_waves_per_simd_sb() {
   static int cached = 0;
   if (cached == 0) {
     hipFuncAttributes at;
     int regs = 128;
-    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(gemm_strip_kernel<false>)) == hipSuccess &&
+    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(gemm_strip_kernel<SB, false>)) == hipSuccess &&
         at.numRegs > 0)
       regs = at.numRegs;
     regs = (regs + 7) / 8 * 8;
@@ -1323,6 +1327,7 @@ int strip_waves_per_simd() {
   }
   return cached;
 }
+int strip_waves_per_simd(int sb) { return sb == 2 ? strip_waves_per_simd_sb<2>() : strip_waves_per_simd_sb<1>(); }
 
 // Waves of the gemv kernel for MT rows that fit a SIMD at once (its register count, read once).
 template <int MT>
@@ -1399,13 +1404,15 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
     return pl;
   }
   // Up to 16 tokens on layers with a strip (one workgroup) for at least 3/4 of the CUs:
-  // the strip kernel (its registers allow one 8-wave workgroup per CU, so a narrower
-  // layer would leave CUs idle; the skinny kernel's grid is finer).
-  if (M <= 16 && 4 * (int64_t)nstrip >= 3 * (int64_t)cus) {
+  // the strip kernel, with two 4-bit blocks per strip, or one if that gives the strips
+  // (its workgroups are large, so a narrower layer would leave CUs idle; the skinny
+  // kernel's grid is finer).
+  if (M <= 16 && (4 * (int64_t)nstrip >= 3 * (int64_t)cus || 4 * (int64_t)L.nb >= 3 * (int64_t)cus)) {
     pl.strip = true;
-    pl.nstrip4 = nstrip4;
-    pl.nstrip = nstrip;
-    pl.ks = pick_waves(nstrip, L.G, 4 * strip_waves_per_simd(), kStWaves, cus);
+    pl.sb = 4 * (int64_t)nstrip >= 3 * (int64_t)cus ? 2 : 1;
+    pl.nstrip4 = pl.sb == 2 ? nstrip4 : L.nb4;
+    pl.nstrip = pl.sb == 2 ? nstrip : L.nb;
+    pl.ks = pick_waves(pl.nstrip, L.G, 4 * strip_waves_per_simd(pl.sb), kStWaves, cus);
     return pl;
   }
   const int64_t tiles_n = (L.nb + kTileNB - 1) / kTileNB;
@@ -1456,8 +1463,11 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
       default: hipLaunchKernelGGL((gemm_gemv_kernel<3, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4); break;
     }
   } else if (pl.strip) {
-    hipLaunchKernelGGL((gemm_strip_kernel<PARTIALS>), dim3((unsigned)pl.nstrip), dim3((unsigned)(64 * pl.ks)), 0,
-                       stream, a, pl.ks, pl.nstrip4);
+    const dim3 grid((unsigned)pl.nstrip), block((unsigned)(64 * pl.ks));
+    if (pl.sb == 2)
+      hipLaunchKernelGGL((gemm_strip_kernel<2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+    else
+      hipLaunchKernelGGL((gemm_strip_kernel<1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
   } else if (pl.skinny) {
     const int ks = pl.ks;
     const dim3 grid((unsigned)(2 * a.nb)), block((unsigned)(64 * ks));
