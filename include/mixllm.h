@@ -216,10 +216,9 @@ int mixllm_silu_mul_quant(const uint16_t *gate_dev, const uint16_t *up_dev, int6
  * Kernel choice: M > 64 runs the tile kernel; M <= 3 runs the one-lane-per-channel gemv
  * kernel on layers with at least (CUs / 2) 64-channel strips, and 4 <= M <= 16 the strip
  * kernel on layers with at least (3 CUs / 4) strips of one or two blocks; otherwise
- * M <= 64 runs the skinny
- * kernel unless the layer has enough 128-channel tiles to keep the device busy (a cost
- * rule on M, N and the CU count).  All give results within the same tolerance; the int32
- * partials are identical.
+ * M <= 64 runs the skinny kernel unless the layer has enough 128-channel tiles to keep
+ * the device busy (a cost rule on M, N and the CU count).  All give results within the
+ * same tolerance; the int32 partials are identical.
  * Errors: E_NULL, E_SHAPE (also when the tile kernel runs and G * M * 32 exceeds
  * 2^31 - 1), E_GROUP, E_INDEX, E_SPACE, E_HIP.
  * ------------------------------------------------------------------------------------ */
