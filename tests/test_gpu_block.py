@@ -71,6 +71,10 @@ def _block(L, m, hidden, inter, n8, seed):
     (65, 256, 384, dict(gate=3, up=40, down=130), None),
     (130, 512, 1408, dict(gate=10, up=141, down=276), None),
     (512, 4096, 14336, WL.llama8b_n8(), 12),
+    # decode and small batches at the full block size: the gemv and strip kernels for the
+    # gate/up layer (28672 channels), the skinny kernel for the down projection
+    (1, 4096, 14336, WL.llama8b_n8(), None),
+    (4, 4096, 14336, WL.llama8b_n8(), None),
 ])
 def test_mlp_block_chain(L, m, hidden, inter, n8, rows):
     import oracle as O
@@ -96,14 +100,15 @@ def test_mlp_block_chain(L, m, hidden, inter, n8, rows):
     U.assert_y_close(yg, ref_dn["y16"], "down")
 
 
-def test_mlp_block_graph_replays(L):
-    (x16, *_), blk = _block(L, 130, 512, 1408, dict(gate=10, up=141, down=276), (32,))
+@pytest.mark.parametrize("m", [130, 1])
+def test_mlp_block_graph_replays(L, m):
+    (x16, *_), blk = _block(L, m, 512, 1408, dict(gate=10, up=141, down=276), (32,))
     x = torch.from_numpy(x16).cuda()
-    U.say("mlp block graph")
-    eager_bufs = blk.buffers(130)
+    U.say("mlp block graph", m)
+    eager_bufs = blk.buffers(m)
     want = blk.forward(x, eager_bufs).clone()
     torch.cuda.synchronize()
-    bufs = blk.buffers(130)
+    bufs = blk.buffers(m)
     graph = blk.capture(x, bufs)
     other = torch.randn(1 << 20, device="cuda")
     for i in range(4):
