@@ -95,7 +95,9 @@ SMALL = [
     (33, 160, 256, 64), (64, 64, 128, 1), (65, 200, 512, 31), (100, 72, 256, 8), (130, 300, 384, 30),
     (1, 1, 128, 0), (3, 1, 128, 1), (256, 520, 640, 52), (200, 33, 256, 32),
     # tile kernel: slices with an odd step count, the LDS stage ring wrapping several times
-    (160, 288, 1920, 40), (96, 130, 2688, 13),
+    # (these narrow layers take two-block tiles); four-block tiles need a grid as large as
+    # the device: a ragged last M tile
+    (160, 288, 1920, 40), (96, 130, 2688, 13), (4150, 1024, 128, 100),
     # M <= 64 on layers wide enough (on a 256-CU part) for the tile kernel's cost rule
     (48, 12800, 256, 1280), (20, 16448, 128, 100), (1, 29000, 128, 290),
     # M = 1 .. 3 on layers wide enough for the one-lane-per-channel kernel, and 4 .. 16 for

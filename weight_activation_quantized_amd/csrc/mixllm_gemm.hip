@@ -164,10 +164,9 @@ __device__ __forceinline__ void static_for(F &&f) {
 // the slice's last group read a zero group of column words and so add nothing.
 // ------------------------------------------------------------------------------------
 constexpr int kTileBM = 64;
-constexpr int kTileNB = 4;                          // channel blocks per workgroup
+constexpr int kTileNB = 4;                          // channel blocks per workgroup (at most; NB)
 constexpr int kKS = 2;                              // interleaved group slices
-constexpr int kTileWaves = kTileNB * kKS;
-constexpr int kTileThreads = 64 * kTileWaves;
+constexpr int tile_threads(int nb) { return 64 * nb * kKS; }
 #ifndef MIXLLM_STAGES
 #define MIXLLM_STAGES 4
 #endif
@@ -263,7 +262,7 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int KIND, bool PARTIALS, int PHASE, bool RDMA>
+template <int NB, int KIND, bool PARTIALS, int PHASE, bool RDMA>
 __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m0, int blk, int bi, int q,
                                           int lane) {
   constexpr bool HASW = KIND != kNone;
@@ -272,7 +271,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   // the codes before the matrix cores.
   constexpr bool ZPRE = kZeroPre && !PARTIALS && KIND == kW4;
   constexpr int NZ = ((PARTIALS && KIND == kW4) || ZPRE) ? 1 : 0;
-  constexpr int LD = RDMA ? 3 : 2;                                // direct-to-LDS loads per step
+  constexpr int kDmaRows = 64 / NB;                               // activation rows this wave loads
+  constexpr int LD = kDmaRows / 8 + (RDMA ? 1 : 0);               // direct-to-LDS loads per step
   constexpr int LW = HASW ? NW + 1 + NZ : 0;                      // weight-ring loads per step
   // Loads that may still be outstanding when a step's loads have landed.  A step issues
   // its weight batch, then its stage batch; step s's weights come kWR - 1 steps ahead and
@@ -298,10 +298,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   const Rsrc rz = make_rsrc(p.z4 + (size_t)blk * G * kZ4Chunk, NZ ? (int64_t)G * kZ4Chunk : 0);
 
   // Per-lane offsets.
-  int vdma[2];  // this wave loads rows [16 bi, 16 bi + 16) of the slice's tile, 8 rows per load
+  int vdma[kDmaRows / 8];  // this wave loads rows [kDmaRows bi, + kDmaRows) of the slice's tile, 8 per load
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 16 * bi + 8 * i + (lane >> 3), pos = lane & 7;
+  for (int i = 0; i < kDmaRows / 8; ++i) {
+    const int r = kDmaRows * bi + 8 * i + (lane >> 3), pos = lane & 7;
     vdma[i] = r * p.K + ((pos ^ swz_a(r)) << 4);
   }
   // ... and (waves 0 and 1 of a slice) the 32-byte operand records of rows [32 bi, 32 bi + 32)
@@ -329,8 +329,8 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     constexpr int J = decltype(j_c)::value;
     const int gl = min(kKS * s + q, G - 1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      bload16_lds(ra, smb + J * kAStage + q * kTileBM * 128 + (16 * bi + 8 * i) * 128, vdma[i], gl * 128);
+    for (int i = 0; i < kDmaRows / 8; ++i)
+      bload16_lds(ra, smb + J * kAStage + q * kTileBM * 128 + (kDmaRows * bi + 8 * i) * 128, vdma[i], gl * 128);
     if constexpr (RDMA) bload16_lds(rro, smb + kRBase + J * kRStage + q * kTileBM * 32 + bi * 1024, vro, gl * p.M * 32);
   };
   // Ring slot s % kWR: this wave's weights and column words of step s.
@@ -516,20 +516,20 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   float *red = reinterpret_cast<float *>(&sm.a[0][0][0]);  // [block kept by the reader][wave][r][lane]
   const int give = 1 - q;                                   // the block this wave hands over
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[((give * kTileNB + bi) * 16 + r) * 64 + lane] = q == 0 ? acc1[r] : acc0[r];
+  for (int r = 0; r < 16; ++r) red[((give * NB + bi) * 16 + r) * 64 + lane] = q == 0 ? acc1[r] : acc0[r];
   lds_barrier();
   if (KIND == kNone) return;
   v16f mine = q == 0 ? acc0 : acc1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float other = red[((q * kTileNB + bi) * 16 + r) * 64 + lane];
+    const float other = red[((q * NB + bi) * 16 + r) * 64 + lane];
     mine[r] = q == 0 ? mine[r] + other : other + mine[r];
   }
   if (p.ident) {
     // Channels in original order (all 4-bit or all 8-bit): no scatter.  The wave's
     // 32 x 32 block goes through LDS row-major, then out as 16-byte runs of 8 channels.
     uint16_t *st = reinterpret_cast<uint16_t *>(&sm.a[0][0][0] + kKS * kTileNB * 16 * 64 * 4) +
-                   (q * kTileNB + bi) * 32 * 32;
+                   (q * NB + bi) * 32 * 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[(8 * (r >> 2) + 4 * h + (r & 3)) * 32 + ch32] = f2h(mine[r]);
 #pragma unroll
@@ -558,12 +558,14 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   }
 }
 
-template <bool PARTIALS>
-__global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs p) {
+// NB: channel blocks per workgroup (4; 2 on layers too narrow to fill the CUs with 4).
+template <int NB, bool PARTIALS>
+__global__ __launch_bounds__(tile_threads(NB)) __attribute__((amdgpu_waves_per_eu(2))) void gemm_tile_kernel(
+    const GemmArgs p) {
   __shared__ __attribute__((aligned(16))) TileSmem sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave: uniform
-  const int bi = wave & 3, q = wave >> 2;
+  const int bi = wave % NB, q = wave / NB;
 
   // Workgroup w runs on XCD w % 8.  Give each XCD a contiguous range of tiles, ordered in
   // bands of kBandM M tiles (M tile fastest within a band), so the workgroups an XCD runs
@@ -582,21 +584,21 @@ __global__ __launch_bounds__(kTileThreads) void gemm_tile_kernel(const GemmArgs 
   // better.
   const int tn = (!p.spread || (p.tiles_n & 7)) ? tr : (tr & 7) * (p.tiles_n >> 3) + (tr >> 3);
   const int m0 = tm * kTileBM;
-  const int blk = tn * kTileNB + bi;
+  const int blk = tn * NB + bi;
   const int kind = blk >= p.nb ? kNone : (blk < p.nb4 ? kW4 : kW8);
   // Waves 0 and 1 of each slice also load the row operand records (32 rows each).
   constexpr int PH = MIXLLM_TILE_PHASE;
   if (bi < 2) {
     switch (kind) {
-      case kW4: tile_body<kW4, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
-      case kW8: tile_body<kW8, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
-      default: tile_body<kNone, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
+      case kW4: tile_body<NB, kW4, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
+      case kW8: tile_body<NB, kW8, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
+      default: tile_body<NB, kNone, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
     }
   } else {
     switch (kind) {
-      case kW4: tile_body<kW4, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
-      case kW8: tile_body<kW8, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
-      default: tile_body<kNone, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
+      case kW4: tile_body<NB, kW4, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
+      case kW8: tile_body<NB, kW8, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
+      default: tile_body<NB, kNone, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
     }
   }
 }
@@ -1283,6 +1285,7 @@ struct Plan {
   int rb;                      // skinny: 16-row blocks
   int ks;                      // skinny: waves per workgroup
   int tiles_m, tiles_n;        // tile kernel grid
+  int nbt;                     // tile kernel: channel blocks per workgroup
 };
 
 // Waves of the skinny kernel that fit a SIMD at once (its register count, read once).
@@ -1422,8 +1425,12 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
     pl.ks = pick_waves(2 * (int64_t)L.nb, L.G, 4 * skinny_waves_per_simd_rb(pl.rb), skinny_max_waves(pl.rb), cus);
     return pl;
   }
+  // Tile width: 4 blocks, or 2 when 4-block tiles would leave CUs without a tile (twice
+  // the workgroups, up to two per CU; where 4-block tiles fill the device their shared
+  // activation reads win).
   pl.tiles_m = (M + kTileBM - 1) / kTileBM;
-  pl.tiles_n = (L.nb + kTileNB - 1) / kTileNB;
+  pl.nbt = (int64_t)pl.tiles_m * ((L.nb + 3) / 4) < cus ? 2 : 4;
+  pl.tiles_n = (L.nb + pl.nbt - 1) / pl.nbt;
   return pl;
 }
 
@@ -1484,7 +1491,10 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
     const int64_t T = (int64_t)a.tiles_m * a.tiles_n;
     if (T > 0x7FFFFFFF) return MIXLLM_E_SHAPE;
     a.spread = T <= device_cus() ? 1 : 0;
-    hipLaunchKernelGGL((gemm_tile_kernel<PARTIALS>), dim3((unsigned)T), dim3(kTileThreads), 0, stream, a);
+    if (pl.nbt == 2)
+      hipLaunchKernelGGL((gemm_tile_kernel<2, PARTIALS>), dim3((unsigned)T), dim3(tile_threads(2)), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_tile_kernel<4, PARTIALS>), dim3((unsigned)T), dim3(tile_threads(4)), 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? MIXLLM_OK : MIXLLM_E_HIP;
 }
