@@ -105,8 +105,9 @@ SMALL = [
     # several groups per wave and a ragged tail, or only the tail; ragged M
     (1, 16448, 8960, 1608), (2, 16448, 8960, 1608), (3, 16448, 2688, 1640), (4, 16448, 8960, 1608),
     (9, 16448, 4480, 1608), (16, 16448, 1152, 1640),
-    # the strip kernel with one 4-bit block per strip (layers with 3/4 as many blocks as CUs)
-    (8, 8192, 2688, 820), (13, 6400, 1152, 640),
+    # the strip kernel with one 4-bit block per strip (layers with 3/4 as many blocks as CUs),
+    # and with two 16-row blocks (17 <= M <= 32)
+    (8, 8192, 2688, 820), (13, 6400, 1152, 640), (24, 16448, 2688, 1608), (32, 8192, 1152, 820),
 ]
 
 

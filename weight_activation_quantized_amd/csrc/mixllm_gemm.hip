@@ -992,13 +992,22 @@ __global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const 
 // own stages per wave, filled by direct-to-LDS loads), both 3 groups ahead; the
 // workgroup's waves split the groups and reduce through LDS in a fixed order.
 // ------------------------------------------------------------------------------------
+constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kStWaves = 8;  // waves per workgroup at most
-constexpr int kStRing = 4;   // weight ring (registers) and activation ring (LDS): 3 groups ahead
-// LDS stage of a wave: the group's activation codes [16 rows][128 B] (chunk c of row r at
-// position c ^ (r & 7)), then s_a and S_A of the 16 rows (4 B each, 256 B areas).
-constexpr int kStStage = 2048 + 256 + 256;
-constexpr int kStLds = kStWaves * kStRing * kStStage;
-static_assert(kStLds >= kStWaves * 16 * 64 * 4, "the reduction reuses the stage space");
+#ifndef MIXLLM_ST_MAX_ROWS
+#define MIXLLM_ST_MAX_ROWS 32
+#endif
+constexpr int kStMaxRows = MIXLLM_ST_MAX_ROWS;  // tokens the strip kernel takes (16 or 32)
+// RB 16-row blocks (M <= 16 RB).  Weight ring (registers) and activation ring (LDS) of
+// st_ring(RB) stages: 3 groups ahead for one row block, 2 for two (the explicit wait count
+// below must stay under the 6-bit vmcnt).
+constexpr int st_ring(int rb) { return rb == 1 ? 4 : 3; }
+// LDS stage of a wave: the group's activation codes [16 RB rows][128 B] (chunk c of row r
+// at position c ^ (r & 7)), then s_a and S_A of up to 64 rows (4 B each, 256 B areas).
+constexpr int st_stage(int rb) { return rb * 2048 + 256 + 256; }
+constexpr int st_lds(int rb) { return kStWaves * st_ring(rb) * st_stage(rb); }
+static_assert(st_lds(1) >= kStWaves * 16 * 64 * 4 && st_lds(2) >= kStWaves * 32 * 64 * 4,
+              "the reduction reuses the stage space");
 
 __device__ __forceinline__ void bload4_lds(Rsrc r, void *dst, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)dst, 4, voff, soff, 0, 0);
@@ -1006,19 +1015,20 @@ __device__ __forceinline__ void bload4_lds(Rsrc r, void *dst, int voff, int soff
 
 // NT column tiles: with SB = 2, 4-bit strips hold blocks blk0 and blk0 + second (tiles 2
 // and 3 repeat tiles 0 and 1 when the strip has one block: dup); otherwise a strip is
-// block blk0.  `lds` is this wave's ring of kStRing stages.
-template <int KIND, int SB, bool PARTIALS>
+// block blk0.  `lds` is this wave's ring of st_ring(RB) stages.
+template <int KIND, int SB, int RB, bool PARTIALS>
 __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
-                                           int cnt, uint8_t *lds, float (&acc)[4][4]) {
+                                           int cnt, uint8_t *lds, float (&acc)[4][RB][4]) {
   constexpr int NT = (KIND == kW8 || SB == 1) ? 2 : 4;
-  constexpr int D = kStRing;
+  constexpr int D = st_ring(RB);
+  constexpr int kStage = st_stage(RB);
   constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
   // Vector-memory operations per step: the stage's direct-to-LDS loads, then the weight
   // ring's loads.  When step s computes, the loads issued after step s's stage are the
   // weight batch of the step that issued it and D - 1 full batches; a wait for at most
   // that many outstanding proves the stage has landed (the compiler does not track LDS
   // written by these loads).
-  constexpr int LA = KIND == kW4 ? 4 : 3;
+  constexpr int LA = 2 * RB + (KIND == kW4 ? 2 : 1);
   constexpr int LW = 3 * NT;  // per column tile: codes (or two loads of 8-bit codes) and scale
                               // word, plus the zero-point word for 4-bit
   constexpr int WAIT = LW + (D - 1) * (LA + LW);
@@ -1038,17 +1048,19 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
   // Direct-to-LDS offsets: load i of a stage fills rows 8i .. 8i + 7 (lane l: row
   // 8i + l / 8, position l % 8, which holds chunk (l % 8) ^ (row & 7)); the scale loads
   // fill row l's word.  Rows past M load from past every descriptor (zeros, no traffic).
-  int vdma[2];
+  int vdma[2 * RB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 2 * RB; ++i) {
     const int r = 8 * i + (lane >> 3);
     vdma[i] = r < M ? r * p.K + (((lane & 7) ^ (r & 7)) << 4) : kSkinnyOob;
   }
   const int vrow = lane < M ? lane * 4 : kSkinnyOob;
-  // LDS offsets of this lane's MFMA operands: row ch, chunks qd and qd + 4.
-  int va[2];
+  // LDS offsets of this lane's MFMA operands: row 16 rb + ch, chunks qd and qd + 4.
+  int va[RB][2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) va[c] = ch * 128 + (((qd + 4 * c) ^ (ch & 7)) << 4);
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) va[rb][c] = (16 * rb + ch) * 128 + (((qd + 4 * c) ^ (ch & 7)) << 4);
 
   v4i wR[D][NT][KIND == kW8 ? 2 : 1];
   uint32_t sR[D][NT], zR[D][NT];
@@ -1056,11 +1068,11 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
   auto issue_a = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
     const int g = grp(s);
-    uint8_t *st = lds + J * kStStage;
+    uint8_t *st = lds + J * kStage;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) bload16_lds(ra, st + i * 1024, vdma[i], g * 128);
-    bload4_lds(rsa, st + 2048, vrow, g * M * 4);
-    if constexpr (KIND == kW4) bload4_lds(ras, st + 2304, vrow, g * M * 4);
+    for (int i = 0; i < 2 * RB; ++i) bload16_lds(ra, st + i * 1024, vdma[i], g * 128);
+    bload4_lds(rsa, st + RB * 2048, vrow, g * M * 4);
+    if constexpr (KIND == kW4) bload4_lds(ras, st + RB * 2048 + 256, vrow, g * M * 4);
   };
   auto issue_w = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
@@ -1090,11 +1102,16 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
     else
       wait_vm<WAIT>();
     fence();
-    const uint8_t *st = lds + J * kStStage;
-    const v4i a0 = *reinterpret_cast<const v4i *>(st + va[0]);
-    const v4i a1 = *reinterpret_cast<const v4i *>(st + va[1]);
-    const v4i sa4 = *reinterpret_cast<const v4i *>(st + 2048 + qd * 16);
-    const v4i as4 = KIND == kW4 ? *reinterpret_cast<const v4i *>(st + 2304 + qd * 16) : v4i{0, 0, 0, 0};
+    const uint8_t *st = lds + J * kStage;
+    v4i a0[RB], a1[RB], sa4[RB], as4[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      a0[rb] = *reinterpret_cast<const v4i *>(st + va[rb][0]);
+      a1[rb] = *reinterpret_cast<const v4i *>(st + va[rb][1]);
+      sa4[rb] = *reinterpret_cast<const v4i *>(st + RB * 2048 + (16 * rb + 4 * qd) * 4);
+      as4[rb] = KIND == kW4 ? *reinterpret_cast<const v4i *>(st + RB * 2048 + 256 + (16 * rb + 4 * qd) * 4)
+                            : v4i{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cw = ht(t) * 16 + ch;
@@ -1110,24 +1127,29 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
         b0 = wR[J][t][0];
         b1 = wR[J][t][1];
       }
-      v4i P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-      P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, P, 0, 0, 0);
-      if constexpr (KIND == kW4) {
-        const int z = (int)((zR[J][t] >> ((cw & 7) * 4)) & 15u);
+      const int z = KIND == kW4 ? (int)((zR[J][t] >> ((cw & 7) * 4)) & 15u) : 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) P[r] -= z * as4[r];
-      }
-      if constexpr (PARTIALS) {
-        const int orig = p.idx[(blk0 + bo(t)) * 32 + cw];
-        if (!(dup && t >= 2) && orig >= p.n_begin && orig < p.n_begin + p.n_count) {
+      for (int rb = 0; rb < RB; ++rb) {
+        v4i P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[rb], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+        P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[rb], b1, P, 0, 0, 0);
+        if constexpr (KIND == kW4) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * qd + r < M) p.part[((int64_t)(4 * qd + r) * p.n_count + (orig - p.n_begin)) * G + grp(s)] = P[r];
+          for (int r = 0; r < 4; ++r) P[r] -= z * as4[rb][r];
         }
-      } else {
-        const float sw = h2f((uint16_t)(sR[J][t] >> ((cw & 1) * 16)));
+        if constexpr (PARTIALS) {
+          const int orig = p.idx[(blk0 + bo(t)) * 32 + cw];
+          if (!(dup && t >= 2) && orig >= p.n_begin && orig < p.n_begin + p.n_count) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)P[r], sw * __int_as_float(sa4[r]), acc[t][r]);
+            for (int r = 0; r < 4; ++r) {
+              const int row = 16 * rb + 4 * qd + r;
+              if (row < M) p.part[((int64_t)row * p.n_count + (orig - p.n_begin)) * G + grp(s)] = P[r];
+            }
+          }
+        } else {
+          const float sw = h2f((uint16_t)(sR[J][t] >> ((cw & 1) * 16)));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][rb][r] = fmaf((float)P[r], sw * __int_as_float(sa4[rb][r]), acc[t][rb][r]);
+        }
       }
     }
     fence();
@@ -1161,9 +1183,10 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
 }
 
 // SB: 4-bit blocks per strip (2 on wide layers; 1 doubles the strips of narrower ones).
-template <int SB, bool PARTIALS>
+// RB: 16-row blocks.
+template <int SB, int RB, bool PARTIALS>
 __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArgs p, int ks, int nstrip4) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStLds];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[st_lds(RB)];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int strip = blockIdx.x;
@@ -1177,34 +1200,38 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
   // (wave-uniform; read back into scalar registers for the loads' scalar offsets)
   const int g0 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * wave / ks));
   const int g1 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * (wave + 1) / ks));
-  uint8_t *lds = smem + wave * kStRing * kStStage;
-  float acc[4][4];
+  uint8_t *lds = smem + wave * st_ring(RB) * st_stage(RB);
+  float acc[4][RB][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][rb][r] = 0.0f;
   if (g1 > g0) {
     if (w4)
-      strip_body<kW4, SB, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, lds, acc);
+      strip_body<kW4, SB, RB, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, lds, acc);
     else
-      strip_body<kW8, SB, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, lds, acc);
+      strip_body<kW8, SB, RB, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, lds, acc);
   }
   if (PARTIALS) return;
   __syncthreads();  // every wave's stages are done; the space becomes the reduction area
-  float(*red)[16][64] = reinterpret_cast<float(*)[16][64]>(smem);
+  float(*red)[16 * RB][64] = reinterpret_cast<float(*)[16 * RB][64]>(smem);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][t * 4 + r][lane] = acc[t][r];
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][(t * RB + rb) * 4 + r][lane] = acc[t][rb][r];
   __syncthreads();
-  // Output: the workgroup's waves share the 16 (tile, row) slots; each sums its slot over
-  // the waves in order and writes the row's channel.
+  // Output: the workgroup's waves share the 16 RB (tile, row block, row) slots; each sums
+  // its slot over the waves in order and writes the row's channel.
   const bool four = SB == 2 && w4;  // four column tiles (two blocks)
   const int nt = four && !dup ? 4 : 2;
   const int ch = lane & 15, qd = lane >> 4;
-  for (int e = wave; e < 16; e += ks) {
-    const int t = e >> 2, r = e & 3;
-    const int rowo = 4 * qd + r;
+  for (int e = wave; e < 16 * RB; e += ks) {
+    const int t = e / (4 * RB), rb = (e >> 2) % RB, r = e & 3;
+    const int rowo = 16 * rb + 4 * qd + r;
     if (t >= nt || rowo >= p.M) continue;
     float v = 0.0f;
     for (int w = 0; w < ks; ++w) v += red[w][e][lane];
@@ -1315,13 +1342,13 @@ int skinny_waves_per_simd_rb(int rb) {
 }
 
 // Waves of the strip kernel that fit a SIMD at once (its register count, read once).
-template <int SB>
+template <int SB, int RB>
 int strip_waves_per_simd_sb() {
   static int cached = 0;
   if (cached == 0) {
     hipFuncAttributes at;
     int regs = 128;
-    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(gemm_strip_kernel<SB, false>)) == hipSuccess &&
+    if (hipFuncGetAttributes(&at, reinterpret_cast<const void *>(gemm_strip_kernel<SB, RB, false>)) == hipSuccess &&
         at.numRegs > 0)
       regs = at.numRegs;
     regs = (regs + 7) / 8 * 8;
@@ -1330,7 +1357,10 @@ int strip_waves_per_simd_sb() {
   }
   return cached;
 }
-int strip_waves_per_simd(int sb) { return sb == 2 ? strip_waves_per_simd_sb<2>() : strip_waves_per_simd_sb<1>(); }
+int strip_waves_per_simd(int sb, int rb) {
+  if (rb == 1) return sb == 2 ? strip_waves_per_simd_sb<2, 1>() : strip_waves_per_simd_sb<1, 1>();
+  return sb == 2 ? strip_waves_per_simd_sb<2, 2>() : strip_waves_per_simd_sb<1, 2>();
+}
 
 // Waves of the gemv kernel for MT rows that fit a SIMD at once (its register count, read once).
 template <int MT>
@@ -1361,12 +1391,13 @@ int gemv_waves_per_simd_m(int m) {
 // Waves per workgroup for a grid of nwg workgroups whose waves split G groups into
 // contiguous ranges: the count that minimizes (rounds of workgroups) x (groups per wave),
 // a CU holding floor(wpc / k) workgroups of k waves (wpc: waves per CU the kernel's
-// registers allow).  Ties keep the smaller count (fewer rounds, longer loops).
-int pick_waves(int64_t nwg, int G, int wpc, int kmax, int cus) {
+// registers allow), and at most wg_cap (its LDS).  Ties keep the smaller count (fewer
+// rounds, longer loops).
+int pick_waves(int64_t nwg, int G, int wpc, int kmax, int cus, int wg_cap = 64) {
   int best = 1;
   int64_t best_cost = INT64_MAX;
   for (int k = 1; k <= kmax && k <= G; ++k) {
-    const int per_cu = wpc / k;
+    const int per_cu = min(wpc / k, wg_cap);
     if (per_cu < 1) break;
     const int64_t fit = (int64_t)cus * per_cu;
     const int64_t cost = (nwg + fit - 1) / fit * ((G + k - 1) / k);
@@ -1390,7 +1421,7 @@ int skinny_cost_pm(int M) {
 // fewer tiles than CUs leaves CUs idle (a round of tiles takes about as long as the skinny
 // kernel takes to stream the same weights at M = 1); the skinny kernel keeps every CU busy
 // but costs more per weight byte as M grows.  The tile kernel is taken when
-// tiles * cost > 0.9 * CUs.
+// tiles * cost > 0.9 * CUs (0.45 * CUs where the layer runs 2-block tiles).
 Plan make_plan(int M, const mixllm_blob_info &L) {
   Plan pl{};
   const int cus = device_cus() > 0 ? device_cus() : 256;
@@ -1406,20 +1437,25 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
     pl.ks = pick_waves(nstrip, L.G, 4 * gemv_waves_per_simd_m(M), gv_max_waves(M), cus);
     return pl;
   }
-  // Up to 16 tokens on layers with a strip (one workgroup) for at least 3/4 of the CUs:
+  // Up to 32 tokens on layers with a strip (one workgroup) for at least 3/4 of the CUs:
   // the strip kernel, with two 4-bit blocks per strip, or one if that gives the strips
   // (its workgroups are large, so a narrower layer would leave CUs idle; the skinny
   // kernel's grid is finer).
-  if (M <= 16 && (4 * (int64_t)nstrip >= 3 * (int64_t)cus || 4 * (int64_t)L.nb >= 3 * (int64_t)cus)) {
+  if (M <= kStMaxRows && (4 * (int64_t)nstrip >= 3 * (int64_t)cus || 4 * (int64_t)L.nb >= 3 * (int64_t)cus)) {
     pl.strip = true;
+    pl.rb = (M + 15) / 16;
     pl.sb = 4 * (int64_t)nstrip >= 3 * (int64_t)cus ? 2 : 1;
     pl.nstrip4 = pl.sb == 2 ? nstrip4 : L.nb4;
     pl.nstrip = pl.sb == 2 ? nstrip : L.nb;
-    pl.ks = pick_waves(pl.nstrip, L.G, 4 * strip_waves_per_simd(pl.sb), kStWaves, cus);
+    pl.ks = pick_waves(pl.nstrip, L.G, 4 * strip_waves_per_simd(pl.sb, pl.rb), kStWaves, cus,
+                       kLdsPerCu / st_lds(pl.rb));
     return pl;
   }
+  // (A layer with fewer 4-block tiles than CUs runs 2-block tiles, each half the work: the
+  // tile kernel's side of the comparison halves.)
   const int64_t tiles_n = (L.nb + kTileNB - 1) / kTileNB;
-  if (M <= 64 && tiles_n * skinny_cost_pm(M) <= (int64_t)900 * cus) {
+  const int64_t thr_pm = tiles_n < cus ? 450 : 900;
+  if (M <= 64 && tiles_n * skinny_cost_pm(M) <= thr_pm * cus) {
     pl.skinny = true;
     pl.rb = (M + 15) / 16;
     pl.ks = pick_waves(2 * (int64_t)L.nb, L.G, 4 * skinny_waves_per_simd_rb(pl.rb), skinny_max_waves(pl.rb), cus);
@@ -1471,10 +1507,17 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
     }
   } else if (pl.strip) {
     const dim3 grid((unsigned)pl.nstrip), block((unsigned)(64 * pl.ks));
-    if (pl.sb == 2)
-      hipLaunchKernelGGL((gemm_strip_kernel<2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
-    else
-      hipLaunchKernelGGL((gemm_strip_kernel<1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+    if (pl.rb == 1) {
+      if (pl.sb == 2)
+        hipLaunchKernelGGL((gemm_strip_kernel<2, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+      else
+        hipLaunchKernelGGL((gemm_strip_kernel<1, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+    } else {
+      if (pl.sb == 2)
+        hipLaunchKernelGGL((gemm_strip_kernel<2, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+      else
+        hipLaunchKernelGGL((gemm_strip_kernel<1, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+    }
   } else if (pl.skinny) {
     const int ks = pl.ks;
     const dim3 grid((unsigned)(2 * a.nb)), block((unsigned)(64 * ks));
