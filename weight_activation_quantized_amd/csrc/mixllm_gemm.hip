@@ -982,22 +982,19 @@ __global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const 
 }
 
 // ------------------------------------------------------------------------------------
-// Strip kernel (4 <= M <= 16 on wide layers).  A wave owns a strip of channels (two
-// 4-bit blocks, or one 8-bit block) and all M rows, as 16 x 16 tiles of
-// v_mfma_i32_16x16x64_i8: it loads a group's activation operands once and reuses them for
-// its four (4-bit) or two (8-bit) 16-channel column tiles, so the activation reads per
-// channel are a quarter of the skinny kernel's.  The 4-bit codes go to the matrix cores
-// raw and the zero point enters as - z * S_A on the exact integer partial.  Weights pass
+// Strip kernel (4 <= M <= 32 on wide layers).  A wave owns a strip of channels (two
+// 4-bit blocks, or one block) and all M rows (one or two 16-row blocks), as 16 x 16 tiles
+// of v_mfma_i32_16x16x64_i8: it loads a group's activation operands once and reuses them
+// for its four (or two) 16-channel column tiles, so the activation reads per channel are
+// a quarter (a half) of the skinny kernel's.  The 4-bit codes go to the matrix cores raw
+// and the zero point enters as - z * S_A on the exact integer partial.  Weights pass
 // through a register ring and the activation codes, s_a and S_A through an LDS ring (its
-// own stages per wave, filled by direct-to-LDS loads), both 3 groups ahead; the
-// workgroup's waves split the groups and reduce through LDS in a fixed order.
+// own stages per wave, filled by direct-to-LDS loads), 3 (two row blocks: 2) groups
+// ahead; the workgroup's waves split the groups and reduce through LDS in a fixed order.
 // ------------------------------------------------------------------------------------
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kStWaves = 8;  // waves per workgroup at most
-#ifndef MIXLLM_ST_MAX_ROWS
-#define MIXLLM_ST_MAX_ROWS 32
-#endif
-constexpr int kStMaxRows = MIXLLM_ST_MAX_ROWS;  // tokens the strip kernel takes (16 or 32)
+constexpr int kStMaxRows = 32;  // tokens the strip kernel takes
 // RB 16-row blocks (M <= 16 RB).  Weight ring (registers) and activation ring (LDS) of
 // st_ring(RB) stages: 3 groups ahead for one row block, 2 for two (the explicit wait count
 // below must stay under the 6-bit vmcnt).
