@@ -47,15 +47,32 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
+// Reductions over the 16 lanes of a quarter (a DPP row) with DPP lane moves, no LDS: swap
+// neighbours, swap pairs (quad permutes), then mirror each 8-lane half and the row; after
+// the four steps every lane holds the combination of all 16 lanes.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ float quarter_max(float v) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
+  v = fmaxf(v, __int_as_float(dpp<kDppXor1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<kDppXor2>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<kDppHalfMirror>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<kDppMirror>(__float_as_int(v))));
   return v;
 }
 
 __device__ __forceinline__ int quarter_sum(int v) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) v += __shfl_xor(v, m, 16);
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
   return v;
 }
 
