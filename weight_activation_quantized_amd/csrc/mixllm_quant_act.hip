@@ -6,7 +6,7 @@
 // The pages do not describe this kernel.  It is a streaming pass (2 bytes in, 1 + 4/128
 // (+ 4/128) bytes out per element), so its roofline is HBM bandwidth.  Layout: one
 // 16-lane quarter of a wave owns one (token, group) pair; each lane loads 8 fp16 values
-// (16 bytes), the quarter reduces the group maximum and the code sum with lane shuffles,
+// (16 bytes), the quarter reduces the group maximum and the code sum with DPP lane moves,
 // and each lane stores its 8 codes (8 bytes).  Consecutive quarters own consecutive
 // groups of the same token, so a wave reads 1 KB of contiguous fp16 input.
 //
