@@ -10,6 +10,11 @@
       device-to-device copy of B bytes (the runtime's copyBuffer kernel) in the same
       pass: factor = B / counter bytes of the copy.
 
+  python -m weight_activation_quantized_amd.rocprof_summary counters DIR [DIR ...] \
+      --kernel NAME --cmd "..." --title "..." > counters.txt
+      mean per dispatch of every counter that the --pmc passes in the DIRs collected for
+      kernel NAME (rows of one dispatch summed), with the pass's command.
+
 Reads only CSV files; runs nothing.
 """
 from __future__ import annotations
@@ -119,6 +124,20 @@ def cmd_traffic(a):
     print()
 
 
+def cmd_counters(a):
+    print(f"# rocprofv3 counter summary: {a.title}")
+    print(f"# command (one run per pass, PASS = the counters of one directory): {a.cmd}")
+    print(f"# kernel: {a.kernel}; values are means over its dispatches of the per-dispatch sums")
+    print("#")
+    for d in a.dirs:
+        names = sorted({r["Counter_Name"] for f in _find(d, "_counter_collection.csv")
+                        for r in csv.DictReader(open(f))})
+        print(f"# pass {os.path.basename(os.path.normpath(d))}: {' '.join(names)}")
+        for c in names:
+            vals = _pick(counter_per_dispatch(d, c), a.kernel)
+            print(f"{c:32s} {statistics.mean(vals):18.1f}   ({len(vals)} dispatches)")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -136,8 +155,13 @@ def main(argv=None):
     t.add_argument("--algorithmic-bytes", type=float, default=0.0)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--title", default="")
     a = ap.parse_args(argv)
-    (cmd_stats if a.what == "stats" else cmd_traffic)(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":
