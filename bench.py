@@ -108,10 +108,29 @@ def cpu_baseline(m, n, k, n8):
         O.layer_forward(a16, w16, idx8)
         dt += time.perf_counter() - t0
         reps += 1
-    return {"value": round(2.0 * m * n * k * reps / dt / 1e12, 6), "unit": "TOPS", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{reps} pass(es) of the oracle layer (quantize activations and weights + fp64 "
-                      f"two-step GEMM), M={m} N={n} K={k} n8={n8}, {dt:.2f} s"}
+    out = {"value": round(2.0 * m * n * k * reps / dt / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"{reps} pass(es) of the oracle layer (quantize activations and weights + fp64 "
+                     f"two-step GEMM), M={m} N={n} K={k} n8={n8}, {dt:.2f} s"}
+    # the same oracle on one BLAS thread: one pass
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.layer_forward(a16, w16, idx8)
+            d1 = time.perf_counter() - t0
+        out["one_thread"] = {"value": round(2.0 * m * n * k / d1 / 1e12, 6), "unit": "TOPS",
+                             "sample": f"1 pass, {d1:.2f} s"}
+        out["blas"] = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()})
+    except Exception as e:  # pragma: no cover
+        out["one_thread"] = f"not measured: {e}"
+    try:
+        with open("/proc/cpuinfo") as f:
+            out["cpu"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        out["cpu"] = None
+    out["nproc"] = os.cpu_count()
+    return out
 
 
 def mlp_main(args):
