@@ -794,7 +794,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(
 // scale and zero-point words, so the kernel is bound by the weight stream.
 // ------------------------------------------------------------------------------------
 constexpr int kGvWaves = 16;  // waves per workgroup at most
-constexpr int kGvRing = 4;    // weight ring: loads 3 groups ahead
+constexpr int kGvRing = 2;    // weight ring: loads one group ahead (deeper rings measured slower)
 constexpr int kNonTemporal = 2;  // cache-policy bit nt: the weights are read once
 constexpr int kGvMaxRows = 3;  // tokens the gemv kernel takes
 
@@ -996,9 +996,10 @@ constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kStWaves = 8;  // waves per workgroup at most
 constexpr int kStMaxRows = 32;  // tokens the strip kernel takes
 // RB 16-row blocks (M <= 16 RB).  Weight ring (registers) and activation ring (LDS) of
-// st_ring(RB) stages: 3 groups ahead for one row block, 2 for two (the explicit wait count
-// below must stay under the 6-bit vmcnt).
-constexpr int st_ring(int rb) { return rb == 1 ? 4 : 3; }
+// st_ring(RB) stages: one group ahead for one row block, 2 for two (measured: deeper rings
+// let the older waves of a CU hog its memory queue; the explicit wait count below must
+// also stay under the 6-bit vmcnt).
+constexpr int st_ring(int rb) { return rb == 1 ? 2 : 3; }
 // LDS stage of a wave: the group's activation codes [16 RB rows][128 B] (chunk c of row r
 // at position c ^ (r & 7)), then s_a and S_A of up to 64 rows (4 B each, 256 B areas).
 constexpr int st_stage(int rb) { return rb * 2048 + 256 + 256; }
