@@ -108,6 +108,9 @@ SMALL = [
     # the strip kernel with one 4-bit block per strip (layers with 3/4 as many blocks as CUs),
     # and with two 16-row blocks (17 <= M <= 32)
     (8, 8192, 2688, 820), (13, 6400, 1152, 640), (24, 16448, 2688, 1608), (32, 8192, 1152, 820),
+    # M = 1 .. 3 on a layer with fewer 4-bit block pairs than CUs (on 256 CUs): one 4-bit
+    # block per strip, the group's inputs split over the half-waves; an odd block count
+    (1, 8192, 2688, 820), (2, 8192, 1152, 820), (3, 8192, 896, 820),
 ]
 
 

@@ -797,6 +797,12 @@ constexpr int kGvWaves = 16;  // waves per workgroup at most
 constexpr int kGvRing = 2;    // weight ring: loads one group ahead (deeper rings measured slower)
 constexpr int kNonTemporal = 2;  // cache-policy bit nt: the weights are read once
 constexpr int kGvMaxRows = 3;  // tokens the gemv kernel takes
+#ifndef MIXLLM_GV_WAVES_PER_SIMD
+#define MIXLLM_GV_WAVES_PER_SIMD 7
+#endif
+// Waves per SIMD at most, whatever the registers allow: with all 8 the 70B gate at M = 1
+// ran 30 µs instead of 24 (more waves per CU, more requests queued ahead of the youngest).
+constexpr int kGvWavesPerSimd = MIXLLM_GV_WAVES_PER_SIMD;
 
 typedef const __attribute__((address_space(4))) v16i *ConstV16;
 typedef const __attribute__((address_space(4))) float *ConstF;
@@ -804,11 +810,12 @@ typedef const __attribute__((address_space(4))) int32_t *ConstI;
 
 // 4-bit: lane c (c = lane & 31) computes packed channel 32 blk + c, blk being the strip's
 // first block for lanes 0-31 and its second for lanes 32-63 (`second`; with `dup` the
-// first block again, results unused).  8-bit: blk0 is the block and kh = lane >> 5 the
-// half of the group's inputs.  MT tokens (rows): a lane decodes its codes of a group once
+// first block again, results unused).  8-bit, and 4-bit with SPLIT (one block per strip,
+// for layers whose block pairs would leave CUs idle): blk0 is the block and kh = lane >> 5
+// the half of the group's inputs.  MT tokens (rows): a lane decodes its codes of a group once
 // and runs them against each row's activation codes; the rows' operands pass through a
 // two-slot SGPR ring in (group, row) order, one item ahead.
-template <int KIND, int MT, bool PARTIALS>
+template <int KIND, int MT, bool PARTIALS, bool SPLIT>
 __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
                                           int cnt, float (&acc)[MT]) {
   constexpr int D = kGvRing;
@@ -819,9 +826,12 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
   const Rsrc rw = make_rsrc((KIND == kW8 ? p.w8 : p.w4) + (size_t)bq * G * kWChunk, (int64_t)2 * G * kWChunk);
   const Rsrc rs = make_rsrc((KIND == kW8 ? p.s8 : p.s4) + (size_t)bq * G * 32, (int64_t)2 * G * 64);
   const Rsrc rz = make_rsrc(p.z4 + (size_t)bq * G * kZ4Chunk, KIND == kW4 ? (int64_t)2 * G * kZ4Chunk : 0);
-  // 4-bit: unit (half * 4 + a) * 16 + ch holds k-chunks a and a + 4 of the channel;
-  // 8-bit: unit (half * 8 + t) * 16 + ch holds k-chunk t (this lane: t = 4 kh + a).
+  // 4-bit: unit (half * 4 + a) * 16 + ch holds k-chunks a and a + 4 of the channel (with
+  // SPLIT this lane loads a = 2 kh, 2 kh + 1); 8-bit: unit (half * 8 + t) * 16 + ch holds
+  // k-chunk t (this lane: t = 4 kh + a).
+  constexpr int NWL = KIND == kW4 && SPLIT ? 2 : 4;  // 16-byte weight loads per group
   const int vw = KIND == kW8 ? ((half * 8 + 4 * kh) * 16 + ch) * 16
+                 : SPLIT     ? ((half * 4 + 2 * kh) * 16 + ch) * 16
                              : second * G * kWChunk + ((half * 4) * 16 + ch) * 16;
   const int vs = (KIND == kW8 ? 0 : second * G * 64) + (c >> 1) * 4;
   const int vz = second * G * (int)kZ4Chunk + (c >> 3) * 4;
@@ -848,7 +858,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
     constexpr int J = decltype(j_c)::value;
     const int g = grp(s);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NWL; ++t)
       wR[J][t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, vw + t * 256, g * kWChunk, kNonTemporal));
     sR[J] = bload4(rs, vs, g * 64);
     if constexpr (KIND == kW4) zR[J] = bload4(rz, vz, g * (int)kZ4Chunk);
@@ -858,7 +868,21 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
   auto compute = [&](auto jw_c, auto u_c, int s, bool last) {
     constexpr int JW = decltype(jw_c)::value, U = decltype(u_c)::value;
     int wd[32];  // the lane's codes as 32 words of 4 consecutive inputs
-    if constexpr (KIND == kW4) {
+    if constexpr (KIND == kW4 && SPLIT) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const v4i x = wR[JW][t];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          // words 8w + 4t + [0, 4): the codes of inputs 64 w + 16 (2 kh + t) + [0, 16)
+          const uint32_t x0 = (uint32_t)x[2 * w], x1 = (uint32_t)x[2 * w + 1];
+          wd[8 * w + 4 * t + 0] = (int)(x0 & 0x0F0F0F0Fu);
+          wd[8 * w + 4 * t + 1] = (int)((x0 >> 4) & 0x0F0F0F0Fu);
+          wd[8 * w + 4 * t + 2] = (int)(x1 & 0x0F0F0F0Fu);
+          wd[8 * w + 4 * t + 3] = (int)((x1 >> 4) & 0x0F0F0F0Fu);
+        }
+      }
+    } else if constexpr (KIND == kW4) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const v4i x = wR[JW][a];
@@ -887,7 +911,18 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
       else if (!last)
         issue_a(IntC<(Q + 1) % 2>{}, s + 1, 0);
       int P = 0;
-      if constexpr (KIND == kW4) {
+      if constexpr (KIND == kW4 && SPLIT) {
+        // both halves' activation words against this lane's codes, then the lane's half;
+        // the zero point's - z S_A (over the whole group) enters once, in half 0
+        int P0 = 0, P1 = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int w = i >> 3, t = (i >> 2) & 1, j = i & 3;
+          P0 = __builtin_amdgcn_sdot4(aR[Q][w][4 * t + j], wd[i], P0, false);
+          P1 = __builtin_amdgcn_sdot4(aR[Q][w][8 + 4 * t + j], wd[i], P1, false);
+        }
+        P = kh ? P1 : P0 - z * asR[Q];
+      } else if constexpr (KIND == kW4) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) P = __builtin_amdgcn_sdot4(aR[Q][i >> 4][i & 15], wd[i], P, false);
         P -= z * asR[Q];
@@ -903,9 +938,9 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
         P = kh ? P1 : P0;
       }
       if constexpr (PARTIALS) {
-        if constexpr (KIND == kW8) P += __shfl_xor(P, 32);  // both halves of the inputs
+        if constexpr (KIND == kW8 || SPLIT) P += __shfl_xor(P, 32);  // both halves of the inputs
         const int orig = p.idx[jp];
-        if (!dup && (KIND == kW4 || kh == 0) && orig >= p.n_begin && orig < p.n_begin + p.n_count)
+        if (!dup && ((KIND == kW4 && !SPLIT) || kh == 0) && orig >= p.n_begin && orig < p.n_begin + p.n_count)
           p.part[((int64_t)m * p.n_count + (orig - p.n_begin)) * G + grp(s)] = P;
       } else {
         acc[m] = fmaf((float)P, sw * saR[Q], acc[m]);
@@ -938,17 +973,21 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
 constexpr int gv_max_waves(int mt) { return mt == 1 ? kGvWaves : kGvWaves / 2; }
 
 template <int MT, bool PARTIALS>
-__global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const GemmArgs p, int ks, int nstrip4) {
+__global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const GemmArgs p, int ks, int nstrip4,
+                                                                          int split) {
   __shared__ float red[gv_max_waves(MT)][MT][64];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int strip = blockIdx.x;
   // Strips [0, nstrip4) pair the 4-bit blocks (with an odd count the last strip has one
-  // block, and its lanes 32-63 repeat lanes 0-31); the others hold one 8-bit block each.
+  // block, and its lanes 32-63 repeat lanes 0-31), or with `split` hold one 4-bit block
+  // each, split over the two half-waves like the 8-bit blocks; the others hold one 8-bit
+  // block each.
   const bool w4 = strip < nstrip4;
-  const int blk0 = w4 ? 2 * strip : p.nb4 + (strip - nstrip4);
-  const bool dup = w4 && (lane >> 5) >= min(2, p.nb4 - blk0);
-  const int second = w4 && !dup ? (lane >> 5) : 0;
+  const bool halves = !w4 || split;  // lanes c and c + 32 share channel c
+  const int blk0 = w4 ? (split ? strip : 2 * strip) : p.nb4 + (strip - nstrip4);
+  const bool dup = w4 && !split && (lane >> 5) >= min(2, p.nb4 - blk0);
+  const int second = w4 && !split && !dup ? (lane >> 5) : 0;
   const int G = p.G;
   // (wave-uniform; read back into scalar registers for the loads' scalar offsets)
   const int g0 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * wave / ks));
@@ -957,22 +996,24 @@ __global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const 
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
   if (g1 > g0) {
-    if (w4)
-      gemv_body<kW4, MT, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, acc);
+    if (w4 && split)
+      gemv_body<kW4, MT, PARTIALS, true>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
+    else if (w4)
+      gemv_body<kW4, MT, PARTIALS, false>(p, blk0, second, dup, lane, g0, g1 - g0, acc);
     else
-      gemv_body<kW8, MT, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
+      gemv_body<kW8, MT, PARTIALS, false>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
   }
   if (PARTIALS) return;
 #pragma unroll
   for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
   __syncthreads();
-  if (wave != 0 || dup || (!w4 && lane >= 32)) return;
+  if (wave != 0 || dup || (halves && lane >= 32)) return;
   const int orig = p.idx[(blk0 + second) * 32 + (lane & 31)];
   if (orig < 0) return;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     float v = 0.0f;
-    if (w4) {
+    if (!halves) {
       for (int w = 0; w < ks; ++w) v += red[w][m][lane];
     } else {
       for (int w = 0; w < ks; ++w) v += red[w][m][lane] + red[w][m][lane + 32];
@@ -1304,7 +1345,7 @@ int device_cus() {
 struct Plan {
   bool gemv;                   // M <= 3: the one-lane-per-channel kernel
   bool strip;                  // 4 <= M <= 16 on wide layers: the strip kernel
-  int sb;                      // strip: 4-bit blocks per strip
+  int sb;                      // strip, gemv: 4-bit blocks per strip
   int nstrip4, nstrip;         // gemv: strips of 4-bit blocks, all strips
   bool skinny;
   int rb;                      // skinny: 16-row blocks
@@ -1372,7 +1413,7 @@ int gemv_waves_per_simd() {
       regs = at.numRegs;
     regs = (regs + 7) / 8 * 8;
     const int w = 512 / regs;
-    cached = w < 1 ? 1 : (w > 8 ? 8 : w);
+    cached = w < 1 ? 1 : (w > kGvWavesPerSimd ? kGvWavesPerSimd : w);
   }
   return cached;
 }
@@ -1430,9 +1471,12 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
   const int nstrip4 = (L.nb4 + 1) / 2, nstrip = nstrip4 + L.nb8;
   if (M <= kGvMaxRows && 2 * nstrip >= cus) {
     pl.gemv = true;
-    pl.nstrip4 = nstrip4;
-    pl.nstrip = nstrip;
-    pl.ks = pick_waves(nstrip, L.G, 4 * gemv_waves_per_simd_m(M), gv_max_waves(M), cus);
+    // Fewer block pairs than CUs: one 4-bit block per strip, its inputs split over the
+    // half-waves, so the strips cover the CUs.
+    pl.sb = nstrip < cus ? 1 : 2;
+    pl.nstrip4 = pl.sb == 2 ? nstrip4 : L.nb4;
+    pl.nstrip = pl.nstrip4 + L.nb8;
+    pl.ks = pick_waves(pl.nstrip, L.G, 4 * gemv_waves_per_simd_m(M), gv_max_waves(M), cus);
     return pl;
   }
   // Up to 32 tokens on layers with a strip (one workgroup) for at least 3/4 of the CUs:
@@ -1499,9 +1543,9 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
   if (pl.gemv) {
     const dim3 grid((unsigned)pl.nstrip), block((unsigned)(64 * pl.ks));
     switch (a.M) {
-      case 1: hipLaunchKernelGGL((gemm_gemv_kernel<1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4); break;
-      case 2: hipLaunchKernelGGL((gemm_gemv_kernel<2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4); break;
-      default: hipLaunchKernelGGL((gemm_gemv_kernel<3, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4); break;
+      case 1: hipLaunchKernelGGL((gemm_gemv_kernel<1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, pl.sb == 1); break;
+      case 2: hipLaunchKernelGGL((gemm_gemv_kernel<2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, pl.sb == 1); break;
+      default: hipLaunchKernelGGL((gemm_gemv_kernel<3, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, pl.sb == 1); break;
     }
   } else if (pl.strip) {
     const dim3 grid((unsigned)pl.nstrip), block((unsigned)(64 * pl.ks));
