@@ -38,8 +38,8 @@ GEMM_SRC = os.path.join(HERE, "weight_activation_quantized_amd", "csrc", "mixllm
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough for >512 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--m", type=int, default=512)
