@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--variant", default="",
                     help="time a measured variant of the tile GEMM (libmixllm_<name>.so: fold_bias, zero_pre) "
                          "instead of the library")
+    ap.add_argument("--pipelined", action="store_true",
+                    help="also time the same steps on two streams, the quant_act launches of the "
+                         "next half of the rotating sets beside the GEMMs of this half "
+                         "(reported as an extra object; the serial step stays the value)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB before the steps, as the "
                          "known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
@@ -86,6 +90,43 @@ def algorithmic_bytes(m, n, k, n8):
     g, n4 = k // 128, n - n8
     return (n4 * k / 2 + n4 * g * 2.5 + n8 * k + n8 * g * 2 + 4 * n
             + m * k + 4 * m * g + 2 * m * n)
+
+
+def pipelined_steps(args, quant_on, gemm_on, sets):
+    """ms per step of the same steps on two streams: chunks of half the rotating sets; the
+    quant_act launches of chunk c (stream Q) wait for the GEMMs of chunk c - 2, which read
+    the same buffers, and the GEMMs of chunk c (stream G) wait for chunk c's quant_act
+    launches, so quantizing the next chunk overlaps this chunk's GEMMs."""
+    import torch
+    h = sets // 2
+    if h < 1:
+        raise SystemExit("--pipelined needs at least 2 rotating sets")
+    chunks = [(i, min(h, args.steps - i)) for i in range(0, args.steps, h)]
+    sq, sg = torch.cuda.Stream(), torch.cuda.Stream()
+    eq = [torch.cuda.Event() for _ in chunks]
+    eg = [torch.cuda.Event() for _ in chunks]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sg):
+        torch.cuda._sleep(SPIN_CYCLES)
+    e0.record(sg)
+    sq.wait_event(e0)
+    rc = 0
+    for c, (i0, cnt) in enumerate(chunks):
+        if c >= 2:
+            sq.wait_event(eg[c - 2])
+        for i in range(i0, i0 + cnt):
+            rc = rc or quant_on(i, sq.cuda_stream)
+        eq[c].record(sq)
+        sg.wait_event(eq[c])
+        for i in range(i0, i0 + cnt):
+            rc = rc or gemm_on(i, sg.cuda_stream)
+        eg[c].record(sg)
+    e1.record(sg)
+    torch.cuda.synchronize()
+    if rc:
+        raise SystemExit(f"pipelined steps: status {rc}")
+    return e0.elapsed_time(e1) / args.steps
 
 
 def cpu_baseline(m, n, k, n8):
@@ -263,6 +304,12 @@ def main():
     def quant(i):
         return qa_fn(*qargs[i % sets])
 
+    def quant_args_on(i, st):
+        return qa_fn(*(qargs[i % sets][:-1] + (st,)))
+
+    def gemm_args_on(i, st):
+        return gm_fn(*(gargs[i % sets][:-1] + (st,)))
+
     def gemm(i):
         return gm_fn(*gargs[i % sets])
 
@@ -298,6 +345,7 @@ def main():
     if rc:
         raise L.MixLLMError(rc)
     step_ms = e_start.elapsed_time(e_g[-1]) / args.steps
+    piped = pipelined_steps(args, quant_args_on, gemm_args_on, sets) if args.pipelined else None
     q_ms = sum((e_start if c == 0 else e_g[c - 1]).elapsed_time(e_q[c]) for c in range(len(chunks)))
     g_ms = sum(e_q[c].elapsed_time(e_g[c]) for c in range(len(chunks)))
     gemm_us = 1e3 * g_ms / args.steps
@@ -341,6 +389,11 @@ def main():
                    "M": m, "N": n, "K": k, "n8": n8, "group": 128, "rotating_sets": sets,
                    "variant": args.variant or None},
         "roofline": roofline,
+        **({"pipelined": {"ms_per_step": round(piped, 5), "value": round(ops / (piped * 1e-3) / 1e12, 2),
+                          "unit": "TOPS",
+                          "schedule": "two streams: the quant_act launches of one half of the rotating "
+                                      "sets run beside the GEMM launches of the other half"}}
+           if piped else {}),
         "gemm_us": round(gemm_us, 3),
         "quant_act_us": round(quant_us, 3),
         "gemm_hbm_frac_algorithmic": round(alg_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
