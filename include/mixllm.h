@@ -214,9 +214,9 @@ int mixllm_silu_mul_quant(const uint16_t *gate_dev, const uint16_t *up_dev, int6
  * workspace_dev:  reserved; pass NULL and 0 (mixllm_gemm_workspace_bytes returns 0: no
  *                 kernel needs scratch memory).
  * Kernel choice: M > 64 runs the tile kernel; M <= 3 runs the one-lane-per-channel gemv
- * kernel on layers with at least (CUs / 2) 64-channel strips (32-channel strips, each
- * channel's inputs split over two lanes, when there are fewer 64-channel strips than
- * CUs), and 4 <= M <= 32 the strip
+ * kernel on layers with at least (CUs / 2) 32-channel blocks, in 64-channel strips, or in
+ * 32-channel strips with each channel's inputs split over two lanes when there are fewer
+ * 64-channel strips than CUs; 4 <= M <= 32 runs the strip
  * kernel on layers with at least (3 CUs / 4) strips of one or two blocks; otherwise
  * M <= 64 runs the skinny kernel unless the layer has enough 128-channel tiles to keep
  * the device busy (a cost rule on M, N and the CU count).  All give results within the

@@ -1464,12 +1464,12 @@ int skinny_cost_pm(int M) {
 Plan make_plan(int M, const mixllm_blob_info &L) {
   Plan pl{};
   const int cus = device_cus() > 0 ? device_cus() : 256;
-  // One to three tokens: the gemv kernel, when the layer has enough strips (one workgroup
-  // each) to occupy at least half the CUs; narrower layers run the skinny kernel, whose
-  // grid is twice as fine.  (At four tokens the gemv kernel lost to the tile kernel on
-  // the 70B layers.)
+  // One to three tokens: the gemv kernel, when the layer has enough one-block strips (one
+  // workgroup each) to occupy at least half the CUs; narrower layers run the skinny
+  // kernel, whose grid is twice as fine.  (At four tokens the gemv kernel lost to the tile
+  // kernel on the 70B layers.)
   const int nstrip4 = (L.nb4 + 1) / 2, nstrip = nstrip4 + L.nb8;
-  if (M <= kGvMaxRows && 2 * nstrip >= cus) {
+  if (M <= kGvMaxRows && 2 * (L.nb4 + L.nb8) >= cus) {
     pl.gemv = true;
     // Fewer block pairs than CUs: one 4-bit block per strip, its inputs split over the
     // half-waves, so the strips cover the CUs.
