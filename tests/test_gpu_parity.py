@@ -146,11 +146,14 @@ def test_gemm_full_compare(L, m, n, k, n8):
 
 
 @pytest.mark.parametrize("m,n,k,n8,ldy_pad", [(130, 96, 256, 0, 0), (100, 200, 384, 200, 0), (65, 4100, 256, 0, 4),
-                                              (129, 136, 512, 136, 8), (70, 100, 128, 0, 4), (80, 64, 256, 64, 3)])
+                                              (129, 136, 512, 136, 8), (70, 100, 128, 0, 4), (80, 64, 256, 64, 3),
+                                              (1, 4096, 1024, 0, 0), (2, 4096, 512, 4096, 0), (3, 8192, 384, 0, 8)])
 def test_gemm_pure_paths(L, m, n, k, n8, ldy_pad):
     """All channels 4-bit (p0) or all 8-bit (p100): no scatter, 16-byte output stores when
     the output rows allow them (row stride a multiple of 8), including a partial last run
-    of channels; a row stride that does not allow them takes the scatter path."""
+    of channels; a row stride that does not allow them takes the scatter path.  The M <= 3
+    cases run the one-lane-per-channel kernel (on 256 CUs: one-block 4-bit strips, 8-bit
+    blocks only)."""
     sh = WL.Shape(0, "edge", m, n, k, n8)
     a16, w16, idx8 = WL.make_layer_inputs(sh)
     U.say("gemm pure", sh.name, "ldy", n + ldy_pad)
