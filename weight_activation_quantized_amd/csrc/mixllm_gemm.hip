@@ -23,6 +23,12 @@
 //    (shared by the eight waves of a workgroup) with direct-to-LDS loads and streams
 //    each wave's own weights into registers; the skinny kernel streams both from L2/HBM
 //    and splits the groups over the waves of a workgroup, reducing through LDS.
+//  * Small M has two more bandwidth-bound kernels: the gemv kernel (M <= 3; one lane per
+//    channel, v_dot4_i32_i8 against activation codes held in SGPRs) and the strip kernel
+//    (4 <= M <= 32; 16x16x64 integer MFMA tiles fed from a per-wave LDS ring).  They keep
+//    one group of loads ahead (the strip kernel two, with two row blocks): with more, the
+//    older waves of a CU fill its memory queue and the younger ones lag, leaving a long
+//    tail.  make_plan picks the kernel for each call.
 //
 // MFMA layouts used (gfx950):
 //  * v_mfma_i32_32x32x32_i8: lane l supplies row/column (l % 32) and 16 bytes of k; the
