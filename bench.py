@@ -78,7 +78,7 @@ def traffic_for(gemm_hash, m, n, k, n8):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("gemm_source_sha256_16") != gemm_hash:
+    if t.get("source_sha256_16") != gemm_hash:
         return None
     return t.get("hbm_bytes_per_launch")
 

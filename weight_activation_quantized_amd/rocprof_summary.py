@@ -113,7 +113,8 @@ def cmd_traffic(a):
         "hbm_read_bytes_per_launch": round(f_kib * 1024.0 * ff),
         "hbm_write_bytes_per_launch": round(w_kib * 1024.0 * fw),
         "hbm_bytes_per_launch": round(f_kib * 1024.0 * ff + w_kib * 1024.0 * fw),
-        "gemm_source_sha256_16": src_hash,
+        "source": os.path.basename(a.source) if a.source else None,
+        "source_sha256_16": src_hash,
         "command_fetch": a.cmd_fetch,
         "command_write": a.cmd_write,
     }
