@@ -92,8 +92,8 @@ def split3(x32):
 
 def rowop_records(sa_gm, u_gm):
     """The row operand records [G][M][8] of s_a and u = fp32(S_A s_a):
-    {w(u0), w(u1), w(s0), w(s1), w(u2), 0, w(s2), 0}."""
+    {w(s0), w(s1), w(s2), 0, w(u0), w(u1), w(u2), 0}."""
     s0, s1, s2 = split3(sa_gm)
     u0, u1, u2 = split3(u_gm)
     z = np.zeros_like(s0)
-    return np.stack([u0, u1, s0, s1, u2, z, s2, z], axis=-1)
+    return np.stack([s0, s1, s2, z, u0, u1, u2, z], axis=-1)

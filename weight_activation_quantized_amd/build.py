@@ -5,9 +5,9 @@
 ``--variants`` also builds the measured alternatives of the tile GEMM (same C ABI, one
 compile-time switch each) as libmixllm_<name>.so next to the library:
 
-    fold_bias  the float-bits int-to-float conversion with its bias moved onto the matrix
-               cores (one VALU op per folded element instead of two; not exact enough to
-               be the default)
+    fold_bias  the float-bits int-to-float conversion: the partial's MFMA chain starts from
+               the integer 0x4B400000 and one exact float subtraction replaces
+               v_cvt_f32_i32
     zero_pre   4-bit zero points subtracted from the codes before the matrix cores with
                byte-wise integer ops, instead of the per-group matrix-core correction
 

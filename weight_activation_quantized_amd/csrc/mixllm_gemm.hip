@@ -63,7 +63,7 @@ struct GemmArgs {
   const int8_t *aq;
   const float *sa;
   const int32_t *asum;
-  const uint32_t *rowop;  // [G][2][M][4] row operands of the scale products
+  const uint32_t *rowop;  // [G][M][8] row operand records of the scale products and corrections
   int M, N, K, G;
   const uint8_t *w4;
   const uint16_t *s4;
@@ -131,70 +131,61 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 // ------------------------------------------------------------------------------------
-// Tile kernel.  A workgroup of 8 waves owns 64 rows x 128 channels (4 blocks of
-// 32 channels).  Wave (b, q) computes block 4 tn + b for all 64 rows over the groups
-// g = q, q + 2, q + 4, ... (two interleaved group slices, two waves per SIMD); the
-// slices' accumulators are summed through LDS at the end in slice order.
+// Tile kernel.  A workgroup of 8 waves (4 with NB = 2) owns 64 rows x NB blocks of 32
+// channels.  Wave (b, q) computes block NB tn + b for all 64 rows (two 32-row blocks)
+// over the groups g = q, q + 2, q + 4, ... (two interleaved group slices; the two waves
+// of a block share a SIMD); the slices' accumulators are summed through LDS at the end.
 //
-// Per group and wave (two 32-row blocks):
-//   * 4 x 2 v_mfma_i32_32x32x32_i8: the group partials.  4-bit blocks feed the raw
-//     codes q (3 VALU ops per 8 codes); the zero point is removed in the float domain;
-//   * per block, 1 v_mfma_f32_32x32x16_bf16 for the scale products s_a[m] s_w[n] as an
+// Per group and wave:
+//   * 2 x 4 v_mfma_i32_32x32x32_i8: the exact group partials of the two row blocks, from
+//     the raw 4-bit codes q (3 VALU ops per 8 codes) or the 8-bit codes;
+//   * per row block, 1 v_mfma_f32_32x32x16_bf16: the scale products s_a[m] s_w[n] as an
 //     outer product of exact bf16 splits (s_a = a0 + a1 + a2 from the activation
-//     quantizer, s_w = b0 + b1 from the packed weights);
-//   * per block, 1 more that adds the correction -(S_A[m] s_a[m]) (z[n] s_w[n]) to the
-//     accumulator (sum_k (q - z) a_k = sum_k q a_k - z S_A, S_A the group's code sum),
-//     and with the bias fold also -B s_a s_w; both MFMAs read the same row operand;
-//   * the fold: acc += float(P) * scale.  Two forms:
-//       exact: v_cvt_f32_i32 then fma (2 VALU ops per output element);
-//       bias:  the partial's MFMA chain starts from the integer bias 0x4B400000, so the
-//              bits of the result read as a float are exactly B + P (B = 1.5 * 2^23,
-//              |P| < 2^22), and one fma adds (B + P) * scale; the correction MFMA
-//              subtracts B s_a s_w.  This is the float-bits conversion of the talk notes
-//              (高速 I2F 変換) with the subtraction moved onto the matrix cores; it costs
-//              one VALU op per element, and the fold differs from the exact one by at
-//              most B |s_a s_w - fp32(s_a s_w)| plus one rounding at magnitude B s_a s_w,
-//              about s_a s_w per group (an error of order one unit of the integer partial).
-// Software pipeline: block 0 of a group runs on the matrix cores while block 1 of the
-// previous group folds, then block 1 while block 0 folds.
+//     quantizer, s_w = b0 + b1 from the packed blob);
+//   * the fold acc += float(P) * scale: 2 VALU ops per output element;
+//   * the zero point: sum_k (q - z) a_k = sum_k q a_k - z S_A (S_A the group's code sum),
+//     so 4-bit channels need -sum_g (S_A s_a)[m, g] (z s_w)[n, g] added: a sum of rank-one
+//     terms, put on the matrix cores two groups at a time (one per half-wave of a bf16
+//     MFMA).  Wave (b, q) adds the terms of row block q for both slices' groups of each
+//     step, so every output gets each group's term exactly once.
+// Two conversions of the int32 partial to fp32 are built: v_cvt_f32_i32 (default), and
+// the float-bits conversion of the talk notes (高速 I2F 変換), exact here: the partial's
+// MFMA chain starts from the integer 0x4B400000, so its bits read as a float are exactly
+// B + P (B = 1.5 * 2^23, |P| < 2^22), and one subtraction of B recovers P.
 //
-// Streams.  The activation tile of a group (64 rows x 128 B) and the rows' operands
-// (64 rows x 32 B) go from memory straight into LDS (buffer_load ... lds), and each
-// wave's weights and column words into registers, kSA - 1 groups ahead of their use, in
-// rings of kSA stages; the step loop is unrolled by kSA so every stage and ring index is
-// a compile-time constant.  Every wave issues the same fixed set of loads per step, so
-// a wait for "at most 2 steps' loads outstanding" proves that the current step's stage
-// and weights have landed; a workgroup barrier after that wait publishes the stage.  The
-// wait is explicit because the compiler does not track LDS written by these loads.
-// Loads address the group through the scalar offset, clamped to a valid group; steps past
-// the slice's last group read a zero group of column words and so add nothing.
+// Schedule.  A step (one group per wave) is two half-steps, one per row block.  In the
+// half-step of row block r the matrix cores run r's scale product and partial chain while
+// the vector ALUs fold the other row block's previous partials (and, in the first half,
+// decode the step's 4-bit codes); the LDS reads for the next half-step are issued in the
+// same window.  Every operand an MFMA reads was loaded one half-step earlier.
+//
+// Streams.  The activation tile of a group (64 rows x 128 B) and the rows' operand
+// records (64 rows x 32 B) go from memory straight into LDS (buffer_load ... lds) in a
+// ring of kSA stages shared by the workgroup; each wave's weights and column words go
+// into a ring of kSA register slots.  Step s (between its two half-steps) publishes stage
+// s + 1 with a workgroup barrier and refills the ring: stage s + kSA and the weights of
+// step s + kSA - 1.  The loop is unrolled by kSA so every stage and slot index is a
+// compile-time constant.  Every wave issues a fixed set of loads per step, so a wait for
+// "at most 2 steps' loads outstanding" proves the next stage has landed; the wait is
+// explicit because the compiler does not track LDS written by these loads.  Groups past
+// the slice's last one clamp their loads to a valid group and read zero column words, so
+// they add nothing.
 // ------------------------------------------------------------------------------------
 constexpr int kTileBM = 64;
 constexpr int kTileNB = 4;                          // channel blocks per workgroup (at most; NB)
 constexpr int kKS = 2;                              // interleaved group slices
 constexpr int tile_threads(int nb) { return 64 * nb * kKS; }
-#ifndef MIXLLM_STAGES
-#define MIXLLM_STAGES 4
-#endif
-constexpr int kSA = MIXLLM_STAGES;                  // LDS stages
-#ifndef MIXLLM_WRING
-#define MIXLLM_WRING 4
-#endif
-constexpr int kWR = MIXLLM_WRING;                   // weight ring slots (2 or 4)
-static_assert(kWR == 2 || kWR == 4, "weight ring");
-static_assert(kSA % kWR == 0 && kSA >= 2, "the step loop is unrolled by the number of stages");
-#ifndef MIXLLM_TILE_PHASE
-#define MIXLLM_TILE_PHASE 1
-#endif
+constexpr int kSA = 4;                              // LDS stages = weight ring slots
 #ifndef MIXLLM_ZERO_PRE
 #define MIXLLM_ZERO_PRE 0
 #endif
 // Variant: subtract 4-bit zero points from the codes (byte-wise) before the matrix cores
-// instead of the matrix-core correction per group and block (a measured ablation).
+// instead of the matrix-core correction (a measured ablation).
 constexpr bool kZeroPre = MIXLLM_ZERO_PRE != 0;
 #ifndef MIXLLM_FOLD_BIAS
 #define MIXLLM_FOLD_BIAS 0
 #endif
+// Variant: the float-bits int32 -> fp32 conversion instead of v_cvt_f32_i32.
 constexpr bool kFoldBias = MIXLLM_FOLD_BIAS != 0;
 constexpr int kBiasBits = 0x4B400000;               // float bits of B = 1.5 * 2^23
 
@@ -239,10 +230,6 @@ __device__ __forceinline__ v4i bload16(Rsrc r, int voff, int soff) {
 __device__ __forceinline__ uint32_t bload4(Rsrc r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
-typedef uint32_t v3u __attribute__((ext_vector_type(3)));
-__device__ __forceinline__ v3u bload12(Rsrc r, int voff, int soff) {
-  return __builtin_bit_cast(v3u, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0));
-}
 typedef __attribute__((address_space(3))) void *LdsPtr;
 // 16 bytes per lane from the buffer into LDS at dst + 16 * lane (dst wave-uniform).
 __device__ __forceinline__ void bload16_lds(Rsrc r, void *dst, int voff, int soff) {
@@ -268,27 +255,27 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int NB, int KIND, bool PARTIALS, int PHASE, bool RDMA>
-__device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m0, int blk, int bi, int q,
-                                          int lane) {
+template <int NB, int KIND, bool PARTIALS, bool RDMA, int Q>
+__device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m0, int blk, int bi, int lane) {
+  constexpr int q = Q;  // group slice
   constexpr bool HASW = KIND != kNone;
   constexpr int NW = KIND == kW8 ? 4 : (KIND == kW4 ? 2 : 0);     // 16-byte weight loads per step
   // Zero-point word: partials mode, and the variant that subtracts the zero point from
   // the codes before the matrix cores.
   constexpr bool ZPRE = kZeroPre && !PARTIALS && KIND == kW4;
   constexpr int NZ = ((PARTIALS && KIND == kW4) || ZPRE) ? 1 : 0;
+  constexpr bool CORR = KIND == kW4 && !ZPRE && !PARTIALS;
+  constexpr bool BIAS = kFoldBias && !PARTIALS;
   constexpr int kDmaRows = 64 / NB;                               // activation rows this wave loads
   constexpr int LD = kDmaRows / 8 + (RDMA ? 1 : 0);               // direct-to-LDS loads per step
-  constexpr int LW = HASW ? NW + 1 + NZ : 0;                      // weight-ring loads per step
-  // Loads that may still be outstanding when a step's loads have landed.  A step issues
-  // its weight batch, then its stage batch; step s's weights come kWR - 1 steps ahead and
-  // its stage kSA - 1 >= kWR - 1 steps ahead.  With weights, the last of step s's loads is
-  // its weight batch (or, when kWR == kSA, the stage batch right after it), followed by
-  // the stage batch of that step (if kWR < kSA) and the kWR - 2 full batches of the steps
-  // in between; without weights, the kSA - 2 stage batches after step s's stage.
-  constexpr int WAIT = !HASW ? (kSA - 2) * LD : (kWR < kSA ? LD : 0) + (kWR - 2) * (LW + LD);
+  constexpr int NPW = PARTIALS ? 0 : 1;                           // column-word loads per step
+  constexpr int LW = HASW ? NW + NPW + NZ : 0;                    // register-ring loads per step
+  // Step s's batch (stage s + kSA, then weights s + kSA - 1) follows the barrier of step s.
+  // Before the barrier of step s, stage s + 1 must have landed: it came first in the batch
+  // of step s + 1 - kSA, and the weights of that batch were already waited for (decoded
+  // in this step's first half); the batches of the kSA - 2 steps since may be in flight.
+  constexpr int WAIT = (kSA - 2) * (LD + LW);
   static_assert(WAIT < 64, "vmcnt range");
-  constexpr bool CORR = (KIND == kW4 && !ZPRE) || (kFoldBias && KIND != kNone);
   const int ch32 = lane & 31, h = lane >> 5;
   const int G = p.G;
   const int nsteps = (G + kKS - 1) / kKS;                          // same for every wave
@@ -300,7 +287,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   const int bq = KIND == kW8 ? blk - p.nb4 : blk;
   constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
   const Rsrc rw = make_rsrc((KIND == kW8 ? p.w8 : p.w4) + (size_t)bq * G * kWChunk, (int64_t)G * kWChunk);
-  const Rsrc rpw = make_rsrc((const uint8_t *)p.pw + (size_t)blk * (G + 1) * kPwChunk, (int64_t)(G + 1) * kPwChunk);
+  const int npairs = pw_pairs(G);
+  const Rsrc rpw = make_rsrc((const uint8_t *)p.pw + (size_t)blk * npairs * kPwPairChunk,
+                             (int64_t)npairs * kPwPairChunk);
   const Rsrc rz = make_rsrc(p.z4 + (size_t)blk * G * kZ4Chunk, NZ ? (int64_t)G * kZ4Chunk : 0);
 
   // Per-lane offsets.
@@ -312,23 +301,24 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   }
   // ... and (waves 0 and 1 of a slice) the 32-byte operand records of rows [32 bi, 32 bi + 32)
   const int vro = min(m0 + 32 * bi + (lane >> 1), p.M - 1) * 32 + (lane & 1) * 16;
-  const int vpw = ch32 * (int)(kPwWords * 4);
+  const int vpw = ch32 * 16;
   int vw[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     vw[s] = KIND == kW8 ? ((ch32 >> 4) * 8 + chunk32(s, h)) * 256 + (ch32 & 15) * 16
                         : (((ch32 >> 4) * 4 + 2 * (s & 1) + h) * 16 + (ch32 & 15)) * 16;
-  // LDS byte offsets of this lane's operands in stage 0, block 0 (block 1: + 32 rows)
+  // LDS byte offsets of this lane's operands in stage 0, row block 0 (row block 1: + 32 rows)
   int va[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) va[s] = q * kTileBM * 128 + ch32 * 128 + ((chunk32(s, h) ^ swz_a(ch32)) << 4);
-  const int vr = kRBase + q * kTileBM * 32 + ch32 * 32 + h * 16;
+  const int vrs = kRBase + q * kTileBM * 32 + ch32 * 32;       // s-part of this slice's record
+  const int vru = kRBase + h * kTileBM * 32 + ch32 * 32 + 16;  // u-part, slice h (corrections)
   uint8_t *const smb = reinterpret_cast<uint8_t *>(&sm);
 
-  // Weight ring (raw loaded bits): slot s % kWR holds step s.
-  v4i bR[kWR][NW > 0 ? NW : 1];
-  v3u pwR[kWR];
-  uint32_t zR[kWR];
+  // Register ring (raw loaded bits): slot s % kSA holds step s.
+  v4i bR[kSA][NW > 0 ? NW : 1];
+  v4i pwR[kSA];
+  uint32_t zR[kSA];
 
   // Stage s % kSA: the activation tile and the row operands of step s.
   auto issue_a = [&](auto j_c, int s) {
@@ -339,42 +329,40 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
       bload16_lds(ra, smb + J * kAStage + q * kTileBM * 128 + (kDmaRows * bi + 8 * i) * 128, vdma[i], gl * 128);
     if constexpr (RDMA) bload16_lds(rro, smb + kRBase + J * kRStage + q * kTileBM * 32 + bi * 1024, vro, gl * p.M * 32);
   };
-  // Ring slot s % kWR: this wave's weights and column words of step s.
+  // Ring slot s % kSA: this wave's weights and the column words of step s's group pair.
   auto issue_w = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
     if constexpr (HASW) {
-      const int g = kKS * s + q;
-      const int gl = min(g, G - 1);
+      const int gl = min(kKS * s + q, G - 1);
 #pragma unroll
       for (int t = 0; t < NW; ++t) bR[J][t] = bload16(rw, vw[t], gl * kWChunk);
-      pwR[J] = bload12(rpw, vpw, min(g, G) * (int)kPwChunk);
+      if constexpr (NPW) pwR[J] = bload16(rpw, vpw, min(s, npairs - 1) * (int)kPwPairChunk);
       if constexpr (NZ) zR[J] = bload4(rz, (ch32 >> 3) * 4, gl * (int)kZ4Chunk);
     }
   };
 
-  v16f acc0 = v16f{0}, acc1 = v16f{0};  // folded products
-  // Corrections: a separate accumulator that only the matrix cores touch, except in the
-  // bias fold, which is short of registers and adds them to the folded sums directly.
-  constexpr bool SEPCORR = !kFoldBias;
-  v16f cr0 = v16f{0}, cr1 = v16f{0};
-  v16i P1 = v16i{0};                    // block 1 partials of the previous step
-  v16f sc1 = v16f{0};                   // and their scale products
+  v16f acc0 = v16f{0}, acc1 = v16f{0};  // folded products of row blocks 0 and 1
+  v16i P0, P1 = v16i{0};                // group partials (P1: block 1 of the previous step)
+  v16f sc0, sc1 = v16f{0};              // and their scale products
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) P1[r] = kBiasBits;
+  }
   v16i pinit;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) pinit[r] = (kFoldBias && !PARTIALS) ? kBiasBits : 0;
+  for (int r = 0; r < 16; ++r) pinit[r] = BIAS ? kBiasBits : 0;
+  v4i a0[4], a1[4];                     // activation operands of row blocks 0 and 1
+  v4i rs0, rs1;                         // s-parts of the row records
   const int jp = blk * 32 + ch32;
   // The channel's original index for the scatter epilogue, loaded now so its latency
   // overlaps the main loop instead of delaying the final stores.
   const int orig_out = (!PARTIALS && HASW) ? p.idx[jp] : -1;
 
+  auto lds16 = [&](int off) { return *reinterpret_cast<const v4i *>(smb + off); };
   auto load_a = [&](auto j_c, int rb, v4i (&av)[4]) {
     constexpr int J = decltype(j_c)::value;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) av[k] = *reinterpret_cast<const v4i *>(smb + va[k] + J * kAStage + rb * 32 * 128);
-  };
-  auto load_rows = [&](auto j_c, int rb) {
-    constexpr int J = decltype(j_c)::value;
-    return *reinterpret_cast<const v4i *>(smb + vr + J * kRStage + rb * 32 * 32);
+    for (int k = 0; k < 4; ++k) av[k] = lds16(va[k] + J * kAStage + rb * 32 * 128);
   };
   auto chain = [&](const v4i (&av)[4], const v4i (&bw)[4]) {
     v16i P = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[0], bw[0], pinit, 0, 0, 0);
@@ -382,12 +370,17 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     for (int k = 1; k < 4; ++k) P = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[k], bw[k], P, 0, 0, 0);
     return P;
   };
+  // acc += float(P) * sc for the four output registers [4c, 4c + 4).
+  auto fold4 = [&](v16f &acc, const v16i &P, const v16f &sc, int c) {
+#pragma unroll
+    for (int r = 4 * c; r < 4 * c + 4; ++r) {
+      const float x = BIAS ? __int_as_float(P[r]) - 12582912.0f : (float)P[r];
+      acc[r] = fmaf(x, sc[r], acc[r]);
+    }
+  };
   auto fold = [&](v16f &acc, const v16i &P, const v16f &sc) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int pr = P[r];
-      acc[r] = fmaf(kFoldBias ? __int_as_float(pr) : (float)pr, sc[r], acc[r]);
-    }
+    for (int c = 0; c < 4; ++c) fold4(acc, P, sc, c);
   };
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
@@ -407,108 +400,142 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     }
   };
 
-  // One step s: stage J = s % kSA, weight slot W = s % kWR.
-  auto step = [&](auto j_c, int s) {
-    constexpr int J = decltype(j_c)::value;
-    constexpr int W = J % kWR;
-    if constexpr (PARTIALS)
-      wait_vm<0>();  // the partials' stores count too: wait for everything
-    else
-      wait_vm<WAIT>();
-    lds_barrier();
-    // Refill the weight slot and the stage of step s - 1 (whose reads all finished before
-    // the barrier): the weights of step s + kWR - 1 and the stage of step s + kSA - 1.
-    issue_w(IntC<(J + kWR - 1) % kWR>{}, s + kWR - 1);
-    issue_a(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1);
-    fence();
-    if constexpr (HASW) {
-      v4i av0[4], av1[4];
-      load_a(j_c, 0, av0);
-      v4i bw[4];
-      if constexpr (KIND == kW4) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const uint32_t x0 = (uint32_t)bR[W][e][2 * u], x1 = (uint32_t)bR[W][e][2 * u + 1];
-            if constexpr (ZPRE) {
-              // (q - z) per byte before the matrix cores (the pages' vsub4 role)
-              const uint32_t zz = ((zR[W] >> ((ch32 & 7) * 4)) & 15u) * 0x01010101u;
-              bw[2 * e + u] = w4_operand(x0, x1, zz);
-            } else {
-              bw[2 * e + u] = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
-                                  (int)((x1 >> 4) & 0x0F0F0F0Fu)};
-            }
-          }
+  // Weight operand k (k-chunks of one 32-wide step) of ring slot W: 4-bit codes as bytes
+  // (3 VALU ops per 8 codes; with the zero_pre variant, (q - z) per byte), or the 8-bit
+  // codes as loaded.
+  auto decode = [&](auto w_c, int k) -> v4i {
+    constexpr int W = decltype(w_c)::value;
+    if constexpr (KIND == kW4) {
+      const int e = k >> 1, u = k & 1;
+      const uint32_t x0 = (uint32_t)bR[W][e][2 * u], x1 = (uint32_t)bR[W][e][2 * u + 1];
+      if constexpr (ZPRE) {
+        const uint32_t zz = ((zR[W] >> ((ch32 & 7) * 4)) & 15u) * 0x01010101u;
+        return w4_operand(x0, x1, zz);
       } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) bw[k] = bR[W][k];
+        return v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
+                   (int)((x1 >> 4) & 0x0F0F0F0Fu)};
       }
-      if constexpr (PARTIALS) {
-        const int g = kKS * s + q;
-        const v16i P0 = chain(av0, bw);
-        if (g < G) emit(0, P0, g, zR[W]);
-        load_a(j_c, 1, av1);
-        const v16i Pb = chain(av1, bw);
-        if (g < G) emit(1, Pb, g, zR[W]);
-      } else {
-        const v4i r0 = load_rows(j_c, 0), r1 = load_rows(j_c, 1);
-        const int sw = (int)pwR[W].x, zw = ZPRE ? 0 : (int)pwR[W].y, cw = kFoldBias ? (int)pwR[W].z : 0;
-        const v4i bs = v4i{0, 0, sw, sw}, bc = v4i{zw, zw, cw, cw};
-        if constexpr (PHASE == 0) {
-          // the previous step's block 1 folds while this step's operands arrive
-          fold(acc1, P1, sc1);
-          fence();
-          const v16i P0 = chain(av0, bw);
-          load_a(j_c, 1, av1);
-          const v16f sc0 = mfma_bf16(r0, bs, v16f{0});
-          if constexpr (CORR && SEPCORR) cr0 = mfma_bf16(r0, bc, cr0);
-          if constexpr (CORR && !SEPCORR) acc0 = mfma_bf16(r0, bc, acc0);
-          P1 = chain(av1, bw);
-          fold(acc0, P0, sc0);
-          sc1 = mfma_bf16(r1, bs, v16f{0});
-          if constexpr (CORR && SEPCORR) cr1 = mfma_bf16(r1, bc, cr1);
-          if constexpr (CORR && !SEPCORR) acc1 = mfma_bf16(r1, bc, acc1);
-        } else {
-          // block 0 runs on the matrix cores while the previous block 1 folds
-          const v16i P0 = chain(av0, bw);
-          load_a(j_c, 1, av1);
-          fold(acc1, P1, sc1);
-          const v16f sc0 = mfma_bf16(r0, bs, v16f{0});
-          if constexpr (CORR && SEPCORR) cr0 = mfma_bf16(r0, bc, cr0);
-          if constexpr (CORR && !SEPCORR) acc0 = mfma_bf16(r0, bc, acc0);
-          fence();
-          P1 = chain(av1, bw);
-          fold(acc0, P0, sc0);
-          sc1 = mfma_bf16(r1, bs, v16f{0});
-          if constexpr (CORR && SEPCORR) cr1 = mfma_bf16(r1, bc, cr1);
-          if constexpr (CORR && !SEPCORR) acc1 = mfma_bf16(r1, bc, acc1);
-        }
-      }
+    } else {
+      return bR[W][k];
     }
   };
 
-  // Prologue: the loads of the first kSA - 1 stages and kWR - 1 weight slots, in the order
-  // the steps before step 0 would issue them (weights, then stage, per step).
-  static_for<0, kSA - 1>([&](auto t_c) {
-    constexpr int T = decltype(t_c)::value - (kSA - 1);  // steps -(kSA - 1) .. -1
-    if constexpr (T + kWR - 1 >= 0) issue_w(IntC<(T + kWR - 1) % kWR>{}, T + kWR - 1);
-    issue_a(IntC<T + kSA - 1>{}, T + kSA - 1);
+  // One step s: stage J = s % kSA.  Entry: a0 and rs0 hold row block 0's operands of step
+  // s (read during the previous step), P1 / sc1 the previous step's block 1.  The code is
+  // written in issue order; the scheduler barriers between its pieces keep each MFMA
+  // next to the vector work that overlaps it.
+  auto step = [&](auto j_c, int s) {
+    constexpr int J = decltype(j_c)::value;
+    constexpr int JN = (J + 1) % kSA;
+    if constexpr (!HASW) {
+      wait_vm<WAIT>();
+      lds_barrier();
+      issue_a(IntC<J>{}, s + kSA);
+      issue_w(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1);
+      return;
+    }
+    v4i bw[4];
+    if constexpr (PARTIALS) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bw[k] = decode(j_c, k);
+      const int g = kKS * s + q;
+      const v16i Pa = chain(a0, bw);
+      load_a(j_c, 1, a1);
+      if (g < G) emit(0, Pa, g, zR[J]);
+      wait_vm<0>();  // the partials' stores count too: wait for everything
+      lds_barrier();
+      issue_a(IntC<J>{}, s + kSA);
+      issue_w(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1);
+      const v16i Pb = chain(a1, bw);
+      load_a(IntC<JN>{}, 0, a0);
+      if (g < G) emit(1, Pb, g, zR[J]);
+      return;
+    }
+    // Column operands: s_w of this wave's group (2s + q) for the scale products (zero in
+    // the upper half-wave, whose row operand slots are unused), and for the corrections
+    // -z s_w of group 2s + h, the group whose row operands half-wave h reads.
+    const v4i pq = pwR[J];
+    // (Every word of the load stays live to here: a register written by a load still in
+    // flight cannot be reused, and reusing one would force a wait for every load.)
+    asm volatile("" ::"v"(pq));
+    const int sw = h ? 0 : pq[2 * q];
+    const v4i bs = v4i{sw, sw, sw, sw};
+    v4i bz;
+    if constexpr (CORR) {
+      const int zw = h ? pq[3] : pq[1];
+      bz = v4i{zw, zw, zw, zw};
+    }
+    // First half: row block 0 on the matrix cores, row block 1 of the previous step folds
+    // and this step's codes are decoded.
+    sc0 = mfma_bf16(rs0, bs, v16f{0});
+    bw[0] = decode(j_c, 0);
+    fence();
+    P0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[0], bw[0], pinit, 0, 0, 0);
+    bw[1] = decode(j_c, 1);
+    fold4(acc1, P1, sc1, 0);
+    a1[0] = lds16(va[0] + J * kAStage + 32 * 128);
+    fence();
+    P0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[1], bw[1], P0, 0, 0, 0);
+    bw[2] = decode(j_c, 2);
+    fold4(acc1, P1, sc1, 1);
+    a1[1] = lds16(va[1] + J * kAStage + 32 * 128);
+    fence();
+    P0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[2], bw[2], P0, 0, 0, 0);
+    bw[3] = decode(j_c, 3);
+    fold4(acc1, P1, sc1, 2);
+    a1[2] = lds16(va[2] + J * kAStage + 32 * 128);
+    fence();
+    P0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[3], bw[3], P0, 0, 0, 0);
+    fold4(acc1, P1, sc1, 3);
+    a1[3] = lds16(va[3] + J * kAStage + 32 * 128);
+    rs1 = lds16(vrs + J * kRStage + 32 * 32);
+    // The correction's row operands come from stage s too, so they are read before the
+    // barrier that frees it.
+    v4i ru;
+    if constexpr (CORR) ru = lds16(vru + J * kRStage + q * 32 * 32);
+    fence();
+    if constexpr (CORR && q == 0) acc0 = mfma_bf16(ru, bz, acc0);
+    fence();
+    wait_vm<WAIT>();
+    lds_barrier();  // stage s + 1 is published; stage s is free
+    issue_a(j_c, s + kSA);
+    issue_w(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1);
+    fence();
+    // Second half: row block 1 on the matrix cores, row block 0 folds.
+    sc1 = mfma_bf16(rs1, bs, v16f{0});
+    fence();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      P1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[k], bw[k], k ? P1 : pinit, 0, 0, 0);
+      fold4(acc0, P0, sc0, k);
+      a0[k] = lds16(va[k] + JN * kAStage);
+      if (k == 3) rs0 = lds16(vrs + JN * kRStage);
+      fence();
+    }
+    if constexpr (CORR && q == 1) acc1 = mfma_bf16(ru, bz, acc1);
+    fence();
+  };
+
+  // Prologue: the batches of the virtual steps -kSA .. -1 (stage t + kSA, then the weights
+  // of step t + kSA - 1, none for step -1), then stage 0 is published and row block 0's
+  // operands of step 0 are read.  Every load counted by the waits is one the code uses:
+  // a load whose result is never read would be deleted by the compiler and break the count.
+  static_for<0, kSA>([&](auto t_c) {
+    constexpr int T = decltype(t_c)::value;  // virtual step T - kSA
+    issue_a(IntC<T>{}, T);
+    if constexpr (T > 0) issue_w(IntC<T - 1>{}, T - 1);
   });
+  wait_vm<(kSA - 1) * (LD + LW)>();
+  lds_barrier();
+  if constexpr (HASW) {
+    load_a(IntC<0>{}, 0, a0);
+    rs0 = lds16(vrs);
+  }
   for (int it = 0; it < niter; ++it) {
     const int s = it * kSA;
     static_for<0, kSA>([&](auto j_c) { step(j_c, s + decltype(j_c)::value); });
   }
-  if constexpr (!PARTIALS && HASW) {
-    fold(acc1, P1, sc1);
-    if constexpr (CORR && SEPCORR) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc0[r] += cr0[r];
-        acc1[r] += cr1[r];
-      }
-    }
-  }
+  if constexpr (!PARTIALS && HASW) fold(acc1, P1, sc1);
   // All direct-to-LDS loads (including those past the last step) have landed before the
   // stages' space is reused.
   wait_vm<0>();
@@ -564,6 +591,25 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   }
 }
 
+// The body for one wave: its block kind, whether it loads row records, its slice.
+template <int NB, bool PARTIALS, int Q>
+__device__ __forceinline__ void tile_dispatch(const GemmArgs &p, TileSmem &sm, int m0, int blk, int bi, int lane,
+                                              int kind) {
+  if (bi < 2) {
+    switch (kind) {
+      case kW4: tile_body<NB, kW4, PARTIALS, true, Q>(p, sm, m0, blk, bi, lane); break;
+      case kW8: tile_body<NB, kW8, PARTIALS, true, Q>(p, sm, m0, blk, bi, lane); break;
+      default: tile_body<NB, kNone, PARTIALS, true, Q>(p, sm, m0, blk, bi, lane); break;
+    }
+  } else {
+    switch (kind) {
+      case kW4: tile_body<NB, kW4, PARTIALS, false, Q>(p, sm, m0, blk, bi, lane); break;
+      case kW8: tile_body<NB, kW8, PARTIALS, false, Q>(p, sm, m0, blk, bi, lane); break;
+      default: tile_body<NB, kNone, PARTIALS, false, Q>(p, sm, m0, blk, bi, lane); break;
+    }
+  }
+}
+
 // NB: channel blocks per workgroup (4; 2 on layers too narrow to fill the CUs with 4).
 template <int NB, bool PARTIALS>
 __global__ __launch_bounds__(tile_threads(NB)) __attribute__((amdgpu_waves_per_eu(2))) void gemm_tile_kernel(
@@ -593,22 +639,11 @@ __global__ __launch_bounds__(tile_threads(NB)) __attribute__((amdgpu_waves_per_e
   const int blk = tn * NB + bi;
   const int kind = blk >= p.nb ? kNone : (blk < p.nb4 ? kW4 : kW8);
   // Waves 0 and 1 of each slice also load the row operand records (32 rows each).
-  constexpr int PH = MIXLLM_TILE_PHASE;
-  if (bi < 2) {
-    switch (kind) {
-      case kW4: tile_body<NB, kW4, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
-      case kW8: tile_body<NB, kW8, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
-      default: tile_body<NB, kNone, PARTIALS, PH, true>(p, sm, m0, blk, bi, q, lane); break;
-    }
-  } else {
-    switch (kind) {
-      case kW4: tile_body<NB, kW4, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
-      case kW8: tile_body<NB, kW8, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
-      default: tile_body<NB, kNone, PARTIALS, PH, false>(p, sm, m0, blk, bi, q, lane); break;
-    }
-  }
+  if (q == 0)
+    tile_dispatch<NB, PARTIALS, 0>(p, sm, m0, blk, bi, lane, kind);
+  else
+    tile_dispatch<NB, PARTIALS, 1>(p, sm, m0, blk, bi, lane, kind);
 }
-
 // ------------------------------------------------------------------------------------
 // Skinny kernel (small M): one workgroup per 16-channel half block; its KS waves split
 // the groups into contiguous ranges, each wave computes all M <= 16 RB rows for its
@@ -1522,7 +1557,7 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
 // block's weights and column words likewise, and an activation tile as 64 rows of K.
 bool tile_offsets_fit(int M, const mixllm_blob_info &L) {
   return (int64_t)L.G * M * 32 <= 0x7FFFFFFF && (int64_t)L.G * (int64_t)kW8Chunk <= 0x7FFFFFFF &&
-         ((int64_t)L.G + 1) * (int64_t)kPwChunk <= 0x7FFFFFFF &&
+         (int64_t)pw_pairs(L.G) * (int64_t)kPwPairChunk <= 0x7FFFFFFF &&
          (int64_t)kTileBM * L.K + (int64_t)L.G * 128 <= 0x7FFFFFFF;
 }
 

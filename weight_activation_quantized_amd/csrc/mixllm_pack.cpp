@@ -169,13 +169,17 @@ uint32_t bf16_pair(float x) {
   return (b0 >> 16) | (b1 & 0xFFFF0000u);
 }
 
-// Scale words of one channel and group: s_w, -z * s_w and -B * s_w (B = 1.5 * 2^23) as
-// bf16 pairs.  All three products are exact in fp32.
+// Column words of one channel and group: s_w and -z * s_w as bf16 pairs (both products
+// are exact in fp32).
 void scale_words(uint16_t s16, int z, uint32_t *out) {
   const float s = f16_to_f32(s16);
   out[0] = bf16_pair(s);
   out[1] = bf16_pair((float)z * s) ^ 0x80008000u;  // negate both halves
-  out[2] = bf16_pair(12582912.0f * s) ^ 0x80008000u;
+}
+
+// Where the column words of (block b, channel ch32, group g) start in the pw section.
+size_t pw_index(int64_t b, int ch32, int g, int G) {
+  return (((size_t)b * (size_t)mixllm::pw_pairs(G) + (size_t)(g / 2)) * 32 + (size_t)ch32) * 4 + (size_t)(g % 2) * 2;
 }
 
 }  // namespace
@@ -264,7 +268,7 @@ int mixllm_pack_weights(const uint16_t *w, int32_t N, int32_t K, int32_t group, 
         }
         s4[cidx * 32 + ch32] = s16;
         z4[cidx * 16 + ch32 / 2] |= (uint8_t)(z << ((ch32 & 1) ? 4 : 0));
-        scale_words(s16, z, pw + (((size_t)b * (G + 1) + g) * 32 + ch32) * mixllm::kPwWords);
+        scale_words(s16, z, pw + pw_index(b, ch32, g, G));
         continue;
       }
       const size_t cidx = (size_t)(b - L.nb4) * G + g;
@@ -280,7 +284,7 @@ int mixllm_pack_weights(const uint16_t *w, int32_t N, int32_t K, int32_t group, 
         for (int k = 0; k < kGroup; ++k) chunk[w8_code_pos(ch32, k)] = q8[k];
       }
       s8[cidx * 32 + ch32] = s16;
-      scale_words(s16, 0, pw + (((size_t)b * (G + 1) + g) * 32 + ch32) * mixllm::kPwWords);  // z in the codes
+      scale_words(s16, 0, pw + pw_index(b, ch32, g, G));  // z in the codes
     }
   }
   return MIXLLM_OK;

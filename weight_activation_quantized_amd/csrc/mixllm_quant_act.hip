@@ -15,11 +15,11 @@
 // quotient (a reciprocal product where that provably rounds the same way, else hipcc's
 // default correctly rounded division; no fast-math), clamped to [-127, 127].
 //
-// Optionally the kernel also writes the row operands of the GEMM's scale products: s and
-// u = fp32(S_A * s) each as an exact sum of three bf16 values (truncate to bf16, the
-// remainder has at most 16 significant bits, truncate again, the second remainder has
-// at most 8), laid out as the two 16-byte halves of a bf16 MFMA row operand (one per
-// half-wave): [u0 u0 u1 u1 s0 s0 s1 s1] and [u2 u2 0 0 s2 s2 0 0].
+// Optionally the kernel also writes the row operands of the GEMM's matrix-core scale
+// products and zero-point corrections: s and u = fp32(S_A * s) each as an exact sum of
+// three bf16 values (truncate to bf16, the remainder has at most 16 significant bits,
+// truncate again, the second remainder has at most 8), as two 16-byte bf16 MFMA row
+// operands: [s0 s0 s1 s1 s2 s2 0 0] and [u0 u0 u1 u1 u2 u2 0 0].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -148,7 +148,7 @@ __device__ __forceinline__ void quant_pair(uint4 raw, bool live, int64_t m, int 
     split3(s, ws);
     split3((float)qsum * s, wu);
     rowop[((int64_t)g * M + m) * 2 + sub] =
-        sub == 0 ? make_uint4(wu[0], wu[1], ws[0], ws[1]) : make_uint4(wu[2], 0u, ws[2], 0u);
+        sub == 0 ? make_uint4(ws[0], ws[1], ws[2], 0u) : make_uint4(wu[0], wu[1], wu[2], 0u);
   }
 }
 
