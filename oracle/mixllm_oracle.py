@@ -304,37 +304,6 @@ def gemm_w8a8_pure(a16: np.ndarray, w16: np.ndarray, group: int = GROUP) -> np.n
 
 
 # --------------------------------------------------------------------------------------
-# Brute-force cross-checks (independent formulations)
-# --------------------------------------------------------------------------------------
-
-def bruteforce_dequant_matmul(aq, sa, q, z, s16, group: int = GROUP) -> np.ndarray:
-    """Dequantize both operands to fp64 and do one dense matmul:
-    (A_q * s_a) @ ((W_q - z) * s_w)^T.  Equal to ``gemm_mixed`` up to fp64 rounding order."""
-    a_deq = aq.astype(np.float64) * np.repeat(sa.astype(np.float64), group, axis=1)
-    zz = np.repeat(z.astype(np.float64), group, axis=1)
-    w_deq = (q.astype(np.float64) - zz) * np.repeat(s16.astype(np.float64), group, axis=1)
-    return a_deq @ w_deq.T
-
-
-def partials_python(aq, q, z, group: int = GROUP):
-    """Pure-Python nested integer loops for tiny shapes (no numpy arithmetic)."""
-    aq_l = [[int(v) for v in row] for row in aq]
-    q_l = [[int(v) for v in row] for row in q]
-    z_l = [[int(v) for v in row] for row in z]
-    m, k = len(aq_l), len(aq_l[0])
-    n = len(q_l)
-    out = [[[0] * (k // group) for _ in range(n)] for _ in range(m)]
-    for i in range(m):
-        for j in range(n):
-            for g in range(k // group):
-                acc = 0
-                for kk in range(g * group, (g + 1) * group):
-                    acc += (q_l[j][kk] - z_l[j][g]) * aq_l[i][kk]
-                out[i][j][g] = acc
-    return out
-
-
-# --------------------------------------------------------------------------------------
 # Global output-channel precision search (MixLLM talk notes, グローバル混合精度探索;
 # summary page, 核心方法)
 # --------------------------------------------------------------------------------------

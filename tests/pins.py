@@ -381,7 +381,72 @@ def pin_silu_mul(O):
     assert np.all(np.abs(h.astype(np.float64) - want) <= O.ulp_fp16(h) / 2 + 1e-300)
 
 
+# ------------------------------------------------------------------ the parity tolerance
+
+def pin_ulp_fp16(O):
+    """ulp_fp16 sets every GPU parity tolerance (2 ulp + 1e-3 max|Y|), so it is pinned on
+    hand values and, exhaustively, against the spacing numpy's fp16 type itself reports:
+    for every finite fp16 value y, the gap from |y| to the next fp16 value away from zero
+    (the gap below for the largest finite value, 65504)."""
+    hand = {1.0: 2.0 ** -10, 1.5: 2.0 ** -10, 1.999: 2.0 ** -10, 2.0: 2.0 ** -9, 2048.0: 2.0,
+            65504.0: 32.0, -3.0: 2.0 ** -9, 2.0 ** -14: 2.0 ** -24, 2.0 ** -20: 2.0 ** -24,
+            2.0 ** -24: 2.0 ** -24, 0.0: 2.0 ** -24}
+    for y, u in hand.items():
+        got = float(O.ulp_fp16(np.array([y], np.float16))[0])
+        assert got == u, (y, got, u)
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    y = bits.view(np.float16)
+    y = y[np.isfinite(y)]
+    a = np.abs(y)
+    with np.errstate(over="ignore"):
+        up = np.nextafter(a, np.float16(np.inf))
+    gap = (up.astype(np.float64) - a.astype(np.float64))
+    top = ~np.isfinite(up)
+    gap[top] = a[top].astype(np.float64) - np.nextafter(a[top], np.float16(0)).astype(np.float64)
+    assert np.array_equal(O.ulp_fp16(y), gap)
+
+
+# ------------------------------------------------------------------ the MLP block wiring
+
+def _block_case(rng, m=3, hidden=256, inter=256):
+    x = rng.normal(0, 1, size=(m, hidden)).astype(np.float16)
+    wg = rng.normal(0, 0.05, size=(inter, hidden)).astype(np.float16)
+    wu = rng.normal(0, 0.05, size=(inter, hidden)).astype(np.float16)
+    wd = rng.normal(0, 0.05, size=(hidden, inter)).astype(np.float16)
+    return x, wg, wu, wd
+
+
+def pin_mlp_block(O):
+    """The block (gate and up projections as one layer over both channel sets, h =
+    SiLU(gate) * up in fp16, quantize h, down projection):
+    * chained by hand from separate layer calls it is bit-identical (output channels are
+      independent, so one layer over gate and up equals the two layers);
+    * closed form: when the gate output is below -40 everywhere (positive inputs,
+      strongly negative gate weights) SiLU(gate) < 40 e^-40 and h rounds to 0 in fp16,
+      so the block output is exactly 0 whatever the up weights are; likewise when the up
+      weights are zero."""
+    rng = np.random.default_rng(11)
+    x, wg, wu, wd = _block_case(rng)
+    i8g, i8u, i8d = np.array([3, 17]), np.array([0, 100, 255]), np.array([5])
+    blk = O.mlp_block_forward(x, wg, wu, wd, i8g, i8u, i8d)
+    g = O.layer_forward(x, wg, i8g)["y16"]
+    u = O.layer_forward(x, wu, i8u)["y16"]
+    h = O.silu_mul_fp16(g, u)
+    y = O.layer_forward(h, wd, i8d)["y16"]
+    assert np.array_equal(blk["gu16"], np.concatenate([g, u], axis=1))
+    assert np.array_equal(blk["h16"], h)
+    assert np.array_equal(blk["y16"], y)
+    assert np.abs(y.astype(np.float64)).max() > 0
+    xp = np.abs(x).astype(np.float16) + np.float16(0.5)
+    wneg = -np.abs(wg).astype(np.float16) - np.float16(0.5)
+    assert O.layer_forward(xp, wneg, i8g)["y16"].astype(np.float64).max() < -40
+    z = O.mlp_block_forward(xp, wneg, wu, wd, i8g, i8u, i8d)
+    assert not np.any(z["h16"]) and not np.any(z["y16"]), "gate far below zero must silence the block"
+    z = O.mlp_block_forward(x, wg, np.zeros_like(wu), wd, i8g, i8u, i8d)
+    assert not np.any(z["y16"]), "zero up weights must silence the block"
+
+
 ALL_PINS = [pin_golden_quant_examples, pin_tiny_gemm_golden, pin_fp16_rounding, pin_quant_error_bounds,
             pin_partials_bruteforce, pin_y_vs_dequant, pin_p0_p100_and_disjoint, pin_i2f,
             pin_byte_model, pin_layer_fractions, pin_salience_hand, pin_assignment_bruteforce,
-            pin_silu_mul]
+            pin_silu_mul, pin_ulp_fp16, pin_mlp_block]

@@ -177,6 +177,28 @@ def _assign_per_layer(scores, total):
     return out
 
 
+def _ulp_doubled(y16):
+    """The tolerance's ulp one binade too coarse."""
+    y = np.abs(np.asarray(y16, dtype=np.float64))
+    out = np.full(y.shape, 2.0 ** -24)
+    normal = y >= 2.0 ** -14
+    out[normal] = 2.0 ** (np.floor(np.log2(y[normal])) - 9)
+    return out
+
+
+def _ulp_no_subnormal_floor(y16):
+    """Subnormal and zero outputs given a zero tolerance."""
+    y = np.abs(np.asarray(y16, dtype=np.float64))
+    out = np.zeros(y.shape)
+    normal = y >= 2.0 ** -14
+    out[normal] = 2.0 ** (np.floor(np.log2(y[normal])) - 10)
+    return out
+
+
+def _mlp_gate_up_swapped(x16, w_gate, w_up, w_down, idx8_gate, idx8_up, idx8_down, group=128):
+    """SiLU applied to the up projection instead of the gate."""
+    return core.mlp_block_forward(x16, w_up, w_gate, w_down, idx8_up, idx8_gate, idx8_down, group)
+
 
 MUTANTS = {
     "act_round_half_up": _layer_with(quant_act=_act_round_half_up),
@@ -206,6 +228,9 @@ MUTANTS = {
     "assign_per_layer": _ns(assign_channels=_assign_per_layer),
     "silu_sign": _ns(silu=lambda x: np.asarray(x, np.float64) / (1.0 + np.exp(np.asarray(x, np.float64)))),
     "silu_sigmoid_only": _ns(silu=lambda x: 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64)))),
+    "ulp_doubled": _ns(ulp_fp16=_ulp_doubled),
+    "ulp_no_subnormal_floor": _ns(ulp_fp16=_ulp_no_subnormal_floor),
+    "mlp_gate_up_swapped": _ns(mlp_block_forward=_mlp_gate_up_swapped),
 }
 
 
