@@ -19,6 +19,7 @@ events on its launch stream inside the timed region, against the dense int8 MFMA
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -188,7 +189,7 @@ def mlp_main(args):
     torch.cuda.set_device(0)
     x16, wg, wu, wd, ig, iu, idn = WL.mlp_block_inputs(m, hidden, inter, n8)
     blk0 = L.MLPBlock(wg, wu, wd, ig, iu, idn)
-    set_bytes = blk0.gu.blob.numel() + blk0.down.blob.numel() + m * (hidden + 2 * inter) * 6
+    set_bytes = blk0.gu.blob.nbytes + blk0.down.blob.nbytes + m * (hidden + 2 * inter) * 6
     sets = args.sets or max(2, int(np.ceil(512e6 / set_bytes)))
     blocks = [blk0] + [L.MLPBlock(wg, wu, wd, ig, iu, idn) for _ in range(sets - 1)]
     xs = [torch.from_numpy(x16).cuda() for _ in range(sets)]
@@ -271,6 +272,7 @@ def main():
     set_bytes = blob_host.size + m * k * 2 + m * k + 40 * g * m + 2 * m * n
     sets = args.sets or max(4, int(np.ceil(512e6 / set_bytes)))
     base_blob = torch.from_numpy(blob_host).to(dev)
+    hdr = L.blob_header(blob_host)   # the host header the GEMM checks each call against
     base_a = torch.from_numpy(a16).to(dev)
     S = []
     for _ in range(sets):
@@ -298,8 +300,9 @@ def main():
     wsp, wsb = (ws.data_ptr(), ws.numel()) if ws is not None else (None, 0)
     qargs = [(s["a"].data_ptr(), k, m, k, 128, s["aq"].data_ptr(), s["sa"].data_ptr(), s["asum"].data_ptr(),
               s["rowop"].data_ptr(), sp) for s in S]
+    hdr_p = ctypes.byref(hdr)
     gargs = [(s["aq"].data_ptr(), s["sa"].data_ptr(), s["asum"].data_ptr(), s["rowop"].data_ptr(), m, n, k, n8,
-              s["blob"].data_ptr(), s["blob"].numel(), s["y"].data_ptr(), n, wsp, wsb, sp) for s in S]
+              hdr_p, s["blob"].data_ptr(), s["blob"].numel(), s["y"].data_ptr(), n, wsp, wsb, sp) for s in S]
 
     def quant(i):
         return qa_fn(*qargs[i % sets])
@@ -363,7 +366,7 @@ def main():
     ridge = PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
     if ops / alg_bytes >= ridge:
         roofline = {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS,
-                    "unit": "TFLOP/s", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4)}
+                    "unit": "TOPS", "frac": round(gemm_tops / PEAK_INT8_TOPS, 4)}
     else:
         gbps = alg_bytes / (gemm_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,

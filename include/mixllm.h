@@ -207,9 +207,18 @@ int mixllm_silu_mul_quant(const uint16_t *gate_dev, const uint16_t *up_dev, int6
  * of a 4-bit channel enters as sum_k (q - z) a_k = sum_k q a_k - z S_A, with S_A the
  * group's activation code sum.
  *
- * aq_dev, sa_dev, asum_dev, rowop_dev: as produced by mixllm_quant_act for the same M and K
- *                 (all four are required here).
- * blob_dev:       device copy of a blob packed for this N, K, n8 (blob_bytes long).
+ * aq_dev, sa_dev, asum_dev, rowop_dev: as produced by mixllm_quant_act for the same M and K.
+ *                 asum_dev may be NULL when the blob has no whole 4-bit block (nb4 == 0: no
+ *                 zero points to correct); the other three are always required.
+ * N, K, n8:       the layer the caller expects (output channels, inputs, 8-bit channels).
+ * blob_info:      host pointer to the header of the packed blob, as mixllm_blob_get_info
+ *                 returned it for the host blob whose byte copy is blob_dev.  It must equal,
+ *                 field by field, the header a blob packed now for (N, K, n8) would carry
+ *                 (magic, format version, shape, section offsets, size); otherwise the call
+ *                 returns MIXLLM_E_FORMAT and launches nothing.  This is how a blob packed for
+ *                 another layer, another 8-bit count or an older format is rejected: the
+ *                 library does not read device memory back to check it.
+ * blob_dev:       device copy of that blob (blob_bytes long, at least blob_info->total_bytes).
  * y_fp16_dev:     output fp16 [M][ldy], ldy >= N; only columns 0..N-1 are written.
  * workspace_dev:  reserved; pass NULL and 0 (mixllm_gemm_workspace_bytes returns 0: no
  *                 kernel needs scratch memory).
@@ -222,13 +231,14 @@ int mixllm_silu_mul_quant(const uint16_t *gate_dev, const uint16_t *up_dev, int6
  * the device busy (a cost rule on M, N and the CU count).  All give results within the
  * same tolerance; the int32 partials are identical.
  * Errors: E_NULL, E_SHAPE (also when the tile kernel runs and G * M * 32 exceeds
- * 2^31 - 1), E_GROUP, E_INDEX, E_SPACE, E_HIP.
+ * 2^31 - 1), E_GROUP, E_INDEX, E_SPACE, E_FORMAT, E_HIP.
  * ------------------------------------------------------------------------------------ */
 size_t mixllm_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t n8);
 
 int mixllm_gemm_w4w8a8(const int8_t *aq_dev, const float *sa_dev, const int32_t *asum_dev, const uint32_t *rowop_dev,
-                       int32_t M, int32_t N, int32_t K, int32_t n8, const void *blob_dev, size_t blob_bytes,
-                       uint16_t *y_fp16_dev, int64_t ldy, void *workspace_dev, size_t workspace_bytes, void *stream);
+                       int32_t M, int32_t N, int32_t K, int32_t n8, const mixllm_blob_info *blob_info,
+                       const void *blob_dev, size_t blob_bytes, uint16_t *y_fp16_dev, int64_t ldy,
+                       void *workspace_dev, size_t workspace_bytes, void *stream);
 
 /*
  * Test entry point: the same integer inner loop as mixllm_gemm_w4w8a8, but instead of
@@ -239,8 +249,8 @@ int mixllm_gemm_w4w8a8(const int8_t *aq_dev, const float *sa_dev, const int32_t 
  */
 int mixllm_gemm_w4w8a8_partials(const int8_t *aq_dev, const float *sa_dev, const int32_t *asum_dev,
                                 const uint32_t *rowop_dev, int32_t M, int32_t N, int32_t K, int32_t n8,
-                                const void *blob_dev, size_t blob_bytes, int32_t n_begin, int32_t n_count,
-                                int32_t *p_dev, void *stream);
+                                const mixllm_blob_info *blob_info, const void *blob_dev, size_t blob_bytes,
+                                int32_t n_begin, int32_t n_count, int32_t *p_dev, void *stream);
 
 #ifdef __cplusplus
 }

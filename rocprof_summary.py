@@ -1,16 +1,16 @@
 """Turns rocprofv3 CSV output into the short text/JSON summaries kept under profiles/.
 
-  python -m weight_activation_quantized_amd.rocprof_summary stats DIR --cmd "..." > summary.txt
+  python rocprof_summary.py stats DIR --cmd "..." > summary.txt
       per-kernel dispatch count and mean/min/max duration from DIR's *_kernel_stats.csv.
 
-  python -m weight_activation_quantized_amd.rocprof_summary traffic --fetch DIR1 --write DIR2 \
+  python rocprof_summary.py traffic --fetch DIR1 --write DIR2 \
       --kernel NAME --copy-bytes B --cmd-fetch "..." --cmd-write "..." > traffic.json
       HBM bytes per dispatch of kernel NAME from a FETCH_SIZE pass and a WRITE_SIZE pass
       (KiB per dispatch), each scaled by what the same counter reads for the plain
       device-to-device copy of B bytes (the runtime's copyBuffer kernel) in the same
       pass: factor = B / counter bytes of the copy.
 
-  python -m weight_activation_quantized_amd.rocprof_summary counters DIR [DIR ...] \
+  python rocprof_summary.py counters DIR [DIR ...] \
       --kernel NAME --cmd "..." --title "..." > counters.txt
       mean per dispatch of every counter that the --pmc passes in the DIRs collected for
       kernel NAME (rows of one dispatch summed), with the pass's command.

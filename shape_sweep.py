@@ -3,7 +3,7 @@ Llama-3.1-70B layers, the decode/prefill mix), timed on the GPU, with both roofl
 fractions: the GEMM's ops against the dense int8 peak and its algorithmic bytes against
 HBM bandwidth, the binding one marked by the layer's arithmetic intensity.
 
-  python -m weight_activation_quantized_amd.shape_sweep [--cfgs 1,2,3,4] > table.txt
+  python shape_sweep.py [--cfgs 1,2,3,4] > table.txt
 
 Per shape: the packed layer and the activations in rotating device sets (> 512 MB, so
 the weights come from HBM), quant_act once per set, then a spin kernel and a run of GEMM
@@ -13,10 +13,11 @@ kernel runs).  One line per shape, printed as it finishes.
 from __future__ import annotations
 
 import argparse
-import os
-import sys
+import ctypes
 
 import numpy as np
+
+import bench  # the peaks and the algorithmic-bytes formula of the bench line
 
 
 def main(argv=None):
@@ -25,8 +26,6 @@ def main(argv=None):
     ap.add_argument("--target-ms", type=float, default=20.0, help="GPU time per shape (approximate)")
     args = ap.parse_args(argv)
     import torch
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
-    import bench  # the peaks and the algorithmic-bytes formula of the bench line
     from weight_activation_quantized_amd import mixllm as L
     from weight_activation_quantized_amd import workloads as WL
 
@@ -43,6 +42,7 @@ def main(argv=None):
     for (c, layer, n, k, n8, dist), shapes in layers.items():
         w16, idx8 = WL.make_layer_weights(shapes[0])
         blob_h = L.mixllm_pack_weights(w16, idx8)
+        hdr = L.blob_header(blob_h)
         del w16
         g = k // 128
         for sh in shapes:
@@ -63,8 +63,8 @@ def main(argv=None):
                           torch.empty((m, n), dtype=torch.float16, device=dev)))
             st = torch.cuda.current_stream()
             sp = st.cuda_stream
-            gargs = [(aq.data_ptr(), sa.data_ptr(), asum.data_ptr(), ro.data_ptr(), m, n, k, n8, b.data_ptr(),
-                      b.numel(), y.data_ptr(), n, None, 0, sp) for b, aq, sa, asum, ro, y in S]
+            gargs = [(aq.data_ptr(), sa.data_ptr(), asum.data_ptr(), ro.data_ptr(), m, n, k, n8, ctypes.byref(hdr),
+                      b.data_ptr(), b.numel(), y.data_ptr(), n, None, 0, sp) for b, aq, sa, asum, ro, y in S]
             rc = 0
             for i in range(3):
                 rc = rc or lib.mixllm_gemm_w4w8a8(*gargs[i % sets])

@@ -34,7 +34,7 @@ def _run(L, lib, a16, w16, idx8):
     m, k = a16.shape
     n = w16.shape[0]
     g = k // 128
-    blob = torch.from_numpy(L.mixllm_pack_weights(w16, idx8)).cuda()
+    blob = L.DeviceBlob(L.mixllm_pack_weights(w16, idx8))
     a = torch.from_numpy(np.ascontiguousarray(a16)).cuda()
     aq = torch.empty((m, k), dtype=torch.int8, device="cuda")
     sa = torch.empty((g, m), dtype=torch.float32, device="cuda")

@@ -117,7 +117,7 @@ SMALL = [
 def _run_gemm(L, a16, w16, idx8, ldy_pad=0):
     m, k = a16.shape
     n = w16.shape[0]
-    blob = _dev(L.mixllm_pack_weights(w16, idx8))
+    blob = L.DeviceBlob(L.mixllm_pack_weights(w16, idx8))
     aq, sa, asum, rowop = _quant(L, a16)
     y = torch.full((m, n + ldy_pad), float("nan"), dtype=torch.float16, device="cuda")
     assert L.mixllm_gemm_workspace_bytes(m, n, k, len(idx8)) == 0
@@ -173,7 +173,7 @@ def test_gemm_repeat_deterministic(L, m, n, k, n8):
     sh = WL.Shape(0, "edge", m, n, k, n8)
     a16, w16, idx8 = WL.make_layer_inputs(sh)
     U.say("gemm repeat", sh.name)
-    blob = _dev(L.mixllm_pack_weights(w16, idx8))
+    blob = L.DeviceBlob(L.mixllm_pack_weights(w16, idx8))
     qa = _quant(L, a16)
     ys = []
     for _ in range(3):
@@ -208,19 +208,32 @@ def test_gemm_golden_tiny(L):
 def test_gemm_m_zero_and_errors(L):
     sh = WL.Shape(0, "edge", 4, 64, 256, 3)
     a16, w16, idx8 = WL.make_layer_inputs(sh)
-    blob = _dev(L.mixllm_pack_weights(w16, idx8))
+    blob_host = L.mixllm_pack_weights(w16, idx8)
+    blob = L.DeviceBlob(blob_host)
     aq, sa, asum, rowop = _quant(L, a16)
     y = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
     L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, 0, 64, 256, 3, blob, y)
+    short = L.DeviceBlob(blob_host)
+    short.nbytes -= 1
     with pytest.raises(L.MixLLMError) as e:
-        L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, 4, 64, 256, 3, blob[:-1], y)
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, 4, 64, 256, 3, short, y)
     assert e.value.status == -5
+    # a blob packed for another 8-bit count: refused by its header, nothing launched
+    w_o, i_o = WL.make_layer_weights(WL.Shape(0, "edge", 4, 64, 256, 0))
+    other = L.DeviceBlob(L.mixllm_pack_weights(w_o, i_o))
     with pytest.raises(L.MixLLMError) as e:
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, 4, 64, 256, 3, other, y)
+    assert e.value.status == -6
+    with pytest.raises(ValueError):
         L.mixllm_gemm_w4w8a8(aq, sa, None, rowop, 4, 64, 256, 3, blob, y)
-    assert e.value.status == -1
-    with pytest.raises(L.MixLLMError) as e:
+    with pytest.raises(ValueError):
         L.mixllm_gemm_w4w8a8(aq, sa, asum, None, 4, 64, 256, 3, blob, y)
-    assert e.value.status == -1
+    with pytest.raises(ValueError):
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, 4, 64, 256, 3, blob, y[:, :32])   # too few columns
+    with pytest.raises(ValueError):
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, 4, 64, 256, 3, blob, y.cpu())    # not on the GPU
+    with pytest.raises(ValueError):
+        L.mixllm_gemm_w4w8a8(aq, sa, asum, rowop, 4, 64, 256, 3, blob.dev, y)      # no host header
     torch.cuda.synchronize()
     assert float(y.abs().max()) == 0.0
 
@@ -243,7 +256,7 @@ def test_gemm_workloads_sampled(L, key, ms):
     w16, idx8 = WL.make_layer_weights(sh0)
     U.say("pack", sh0.name)
     blob_host = L.mixllm_pack_weights(w16, idx8)
-    blob = _dev(blob_host)
+    blob = L.DeviceBlob(blob_host)
     cols = U.sample_cols(n, idx8, rng)
     # packed codes of the sampled channels against the oracle quantizers
     q, z, s16, is8 = L.mixllm_unpack_weights(blob_host)

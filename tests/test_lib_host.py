@@ -207,27 +207,56 @@ def test_device_entry_points_validate_on_host():
     nbytes = L.mixllm_packed_bytes(64, 256, 128, 2)
     gm = lib.mixllm_gemm_w4w8a8
     f4 = (fake, fake, fake, fake)
-    assert gm(*f4, 4, 64, 200, 2, fake, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(*f4, 4, 64, 256, 65, fake, nbytes, fake, 64, None, 0, s) == -4
-    assert gm(*f4, -1, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
+    # the host header of a blob packed for (N, K, n8) = (64, 256, 2)
+    wl, il = WL.make_layer_weights(WL.Shape(0, "edge", 1, 64, 256, 2))
+    hdr = L.blob_header(L.mixllm_pack_weights(wl, il))
+    hp = ctypes.byref(hdr)
+    assert gm(*f4, 4, 64, 200, 2, hp, fake, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(*f4, 4, 64, 256, 65, hp, fake, nbytes, fake, 64, None, 0, s) == -4
+    assert gm(*f4, -1, 64, 256, 2, hp, fake, nbytes, fake, 64, None, 0, s) == -2
     for i in range(4):
         args = list(f4)
         args[i] = None
-        assert gm(*args, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -1
+        assert gm(*args, 4, 64, 256, 2, hp, fake, nbytes, fake, 64, None, 0, s) == -1
         args[i] = odd
-        assert gm(*args, 4, 64, 256, 2, fake, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(*f4, 4, 64, 256, 2, None, nbytes, fake, 64, None, 0, s) == -1
-    assert gm(*f4, 4, 64, 256, 2, fake, nbytes, None, 64, None, 0, s) == -1
-    assert gm(*f4, 4, 64, 256, 2, fake, nbytes - 1, fake, 64, None, 0, s) == -5
-    assert gm(*f4, 4, 64, 256, 2, fake, nbytes, fake, 63, None, 0, s) == -2
-    assert gm(*f4, 4, 64, 256, 2, odd, nbytes, fake, 64, None, 0, s) == -2
-    assert gm(None, None, None, None, 0, 64, 256, 2, None, 0, None, 64, None, 0, s) == 0  # M = 0
+        assert gm(*args, 4, 64, 256, 2, hp, fake, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(*f4, 4, 64, 256, 2, hp, None, nbytes, fake, 64, None, 0, s) == -1
+    assert gm(*f4, 4, 64, 256, 2, None, fake, nbytes, fake, 64, None, 0, s) == -1
+    assert gm(*f4, 4, 64, 256, 2, hp, fake, nbytes, None, 64, None, 0, s) == -1
+    assert gm(*f4, 4, 64, 256, 2, hp, fake, nbytes - 1, fake, 64, None, 0, s) == -5
+    assert gm(*f4, 4, 64, 256, 2, hp, fake, nbytes, fake, 63, None, 0, s) == -2
+    assert gm(*f4, 4, 64, 256, 2, hp, odd, nbytes, fake, 64, None, 0, s) == -2
+    assert gm(None, None, None, None, 0, 64, 256, 2, hp, None, 0, None, 64, None, 0, s) == 0  # M = 0
+    # a blob packed for another layer is refused before any launch (E_FORMAT): another
+    # 8-bit count (which needs fewer bytes than the caller's buffer), another shape, an
+    # older format version, a damaged section offset
+    for other in [(64, 256, 0), (64, 256, 3), (96, 256, 2), (64, 384, 2)]:
+        wo, io = WL.make_layer_weights(WL.Shape(0, "edge", 1, *other))
+        ho = L.blob_header(L.mixllm_pack_weights(wo, io))
+        assert gm(*f4, 4, 64, 256, 2, ctypes.byref(ho), fake, 1 << 20, fake, 64, None, 0, s) == -6, other
+    for field, delta in [("version", -1), ("magic", 1), ("off_pw", 256), ("total_bytes", -256), ("nb4", 1)]:
+        h2 = L.blob_header(L.mixllm_pack_weights(wl, il))
+        setattr(h2, field, getattr(h2, field) + delta)
+        assert gm(*f4, 4, 64, 256, 2, ctypes.byref(h2), fake, 1 << 20, fake, 64, None, 0, s) == -6, field
+    # with no whole 4-bit block (all channels 8-bit) the code sums are not needed
+    w8, i8 = WL.make_layer_weights(WL.Shape(0, "edge", 1, 64, 256, 64))
+    h8 = L.blob_header(L.mixllm_pack_weights(w8, i8))
+    assert h8.nb4 == 0
+    nb8 = L.mixllm_packed_bytes(64, 256, 128, 64)
+    assert gm(fake, fake, None, fake, 4, 64, 256, 64, ctypes.byref(h8), fake, nb8, fake, 63, None, 0, s) == -2  # ldy < N: past the null checks
+    assert gm(fake, fake, None, fake, 4, 64, 256, 2, hp, fake, nbytes, fake, 64, None, 0, s) == -1
     # the tile kernel's 32-bit operand offsets: G * M * 32 must stay below 2^31
     big = L.mixllm_packed_bytes(64, 1 << 17, 128, 2)
-    assert gm(*f4, 1 << 16, 64, 1 << 17, 2, fake, big, fake, 64, None, 0, s) == -2
+    wb = np.zeros((64, 1 << 17), np.float16)
+    hb = L.blob_header(L.mixllm_pack_weights(wb, np.array([0, 1], np.int32)))
+    assert gm(*f4, 1 << 16, 64, 1 << 17, 2, ctypes.byref(hb), fake, big, fake, 64, None, 0, s) == -2
     assert L.mixllm_gemm_workspace_bytes(512, 4096, 4096, 410) == 0
     gp = lib.mixllm_gemm_w4w8a8_partials
-    assert gp(*f4, 4, 64, 256, 2, fake, nbytes, 60, 5, fake, s) == -2
-    assert gp(*f4, 4, 64, 256, 2, fake, nbytes, -1, 5, fake, s) == -2
-    assert gp(*f4, 4, 64, 256, 2, fake, nbytes, 0, 5, None, s) == -1
-    assert gp(*f4, 4, 64, 256, 2, fake, nbytes, 0, 0, None, s) == 0
+    assert gp(*f4, 4, 64, 256, 2, hp, fake, nbytes, 60, 5, fake, s) == -2
+    assert gp(*f4, 4, 64, 256, 2, hp, fake, nbytes, -1, 5, fake, s) == -2
+    for other in [(64, 256, 0), (64, 256, 3)]:
+        wo, io = WL.make_layer_weights(WL.Shape(0, "edge", 1, *other))
+        ho = L.blob_header(L.mixllm_pack_weights(wo, io))
+        assert gp(*f4, 4, 64, 256, 2, ctypes.byref(ho), fake, 1 << 20, 0, 5, fake, s) == -6
+    assert gp(*f4, 4, 64, 256, 2, hp, fake, nbytes, 0, 5, None, s) == -1
+    assert gp(*f4, 4, 64, 256, 2, hp, fake, nbytes, 0, 0, None, s) == 0

@@ -2,7 +2,7 @@
 import csv
 import json
 
-from weight_activation_quantized_amd import rocprof_summary as RS
+import rocprof_summary as RS
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 

@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "mixllm.h"
 #include "mixllm_layout.h"
@@ -1326,13 +1327,21 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
 // ------------------------------------------------------------------------------------
 
 int check_common(const int8_t *aq, const float *sa, const int32_t *asum, const uint32_t *rowop, int32_t M,
-                 int32_t N, int32_t K, int32_t n8, const void *blob, size_t blob_bytes, mixllm_blob_info *L) {
+                 int32_t N, int32_t K, int32_t n8, const mixllm_blob_info *info, const void *blob, size_t blob_bytes,
+                 mixllm_blob_info *L) {
   if (M < 0 || N <= 0 || K <= 0 || K % kGroup != 0) return MIXLLM_E_SHAPE;
   if (n8 < 0 || n8 > N) return MIXLLM_E_INDEX;
   if (!compute_layout(N, K, n8, L)) return MIXLLM_E_SHAPE;
+  // The blob's host header must describe exactly this layer in this format: the device
+  // copy cannot be read back without synchronizing, so the header copy the caller took
+  // with mixllm_blob_get_info is what stands for it.
+  if (!info) return MIXLLM_E_NULL;
+  if (memcmp(info, L, sizeof(*L)) != 0) return MIXLLM_E_FORMAT;
   if (M == 0) return MIXLLM_OK;
-  if (!aq || !sa || !asum || !rowop || !blob) return MIXLLM_E_NULL;
-  if (!is_aligned16(aq) || !is_aligned16(sa) || !is_aligned16(asum) || !is_aligned16(rowop) || !is_aligned16(blob))
+  if (!aq || !sa || !rowop || !blob) return MIXLLM_E_NULL;
+  if (!asum && L->nb4 > 0) return MIXLLM_E_NULL;  // read only by the 4-bit blocks' zero points
+  if (!is_aligned16(aq) || !is_aligned16(sa) || (asum && !is_aligned16(asum)) || !is_aligned16(rowop) ||
+      !is_aligned16(blob))
     return MIXLLM_E_SHAPE;
   if (blob_bytes < L->total_bytes) return MIXLLM_E_SPACE;
   return MIXLLM_OK;
@@ -1637,10 +1646,11 @@ extern "C" size_t mixllm_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, i
 }
 
 extern "C" int mixllm_gemm_w4w8a8(const int8_t *aq, const float *sa, const int32_t *asum, const uint32_t *rowop,
-                                  int32_t M, int32_t N, int32_t K, int32_t n8, const void *blob, size_t blob_bytes,
-                                  uint16_t *y, int64_t ldy, void *workspace, size_t workspace_bytes, void *stream) {
+                                  int32_t M, int32_t N, int32_t K, int32_t n8, const mixllm_blob_info *blob_info,
+                                  const void *blob, size_t blob_bytes, uint16_t *y, int64_t ldy, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
   mixllm_blob_info L;
-  int st = check_common(aq, sa, asum, rowop, M, N, K, n8, blob, blob_bytes, &L);
+  int st = check_common(aq, sa, asum, rowop, M, N, K, n8, blob_info, blob, blob_bytes, &L);
   if (st != MIXLLM_OK || M == 0) return st;
   if (!y) return MIXLLM_E_NULL;
   if (ldy < N) return MIXLLM_E_SHAPE;
@@ -1659,10 +1669,10 @@ extern "C" int mixllm_gemm_w4w8a8(const int8_t *aq, const float *sa, const int32
 
 extern "C" int mixllm_gemm_w4w8a8_partials(const int8_t *aq, const float *sa, const int32_t *asum,
                                            const uint32_t *rowop, int32_t M, int32_t N, int32_t K, int32_t n8,
-                                           const void *blob, size_t blob_bytes, int32_t n_begin, int32_t n_count,
-                                           int32_t *part, void *stream) {
+                                           const mixllm_blob_info *blob_info, const void *blob, size_t blob_bytes,
+                                           int32_t n_begin, int32_t n_count, int32_t *part, void *stream) {
   mixllm_blob_info L;
-  int st = check_common(aq, sa, asum, rowop, M, N, K, n8, blob, blob_bytes, &L);
+  int st = check_common(aq, sa, asum, rowop, M, N, K, n8, blob_info, blob, blob_bytes, &L);
   if (st != MIXLLM_OK) return st;
   if (n_begin < 0 || n_count < 0 || (int64_t)n_begin + n_count > N) return MIXLLM_E_SHAPE;
   if (M == 0 || n_count == 0) return MIXLLM_OK;

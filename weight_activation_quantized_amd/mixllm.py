@@ -73,10 +73,10 @@ _SIGS = {
     "mixllm_quant_act": ([_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mixllm_silu_mul_quant": ([_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mixllm_gemm_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
-    "mixllm_gemm_w4w8a8": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _i64, _vp, _sz, _vp],
-                           ctypes.c_int),
-    "mixllm_gemm_w4w8a8_partials": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp,
-                                     _vp], ctypes.c_int),
+    "mixllm_gemm_w4w8a8": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp, _i64, _vp, _sz,
+                            _vp], ctypes.c_int),
+    "mixllm_gemm_w4w8a8_partials": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _i32, _i32,
+                                     _vp, _vp], ctypes.c_int),
 }
 def _bind(lib):
     for name, (args, res) in _SIGS.items():
@@ -152,11 +152,17 @@ def mixllm_pack_weights(w_fp16: np.ndarray, idx8, group: int = GROUP) -> np.ndar
     return blob
 
 
-def mixllm_blob_get_info(blob: np.ndarray) -> dict:
+def blob_header(blob: np.ndarray) -> BlobInfo:
+    """The checked header of a host blob (mixllm_blob_get_info), as the C struct the GEMM
+    calls take."""
     b = np.ascontiguousarray(blob, dtype=np.uint8)
     info = BlobInfo()
     _check(_lib.mixllm_blob_get_info(b.ctypes.data, b.size, ctypes.byref(info)))
-    return info.as_dict()
+    return info
+
+
+def mixllm_blob_get_info(blob: np.ndarray) -> dict:
+    return blob_header(blob).as_dict()
 
 
 def mixllm_unpack_weights(blob: np.ndarray):
@@ -220,8 +226,16 @@ def mixllm_quant_act(a, aq, sa, asum=None, rowop=None, stream=None, lib=None):
     """a: fp16 [M, K] CUDA tensor (rows may be strided); aq: int8 [M, K];
     sa: fp32 [G, M]; asum: int32 [G, M] or None; rowop: 32-bit [G, M, 8] or None."""
     m, k = a.shape
-    if a.dtype != torch.float16 or a.stride(1) != 1:
-        raise ValueError("a must be fp16 with unit column stride")
+    if a.dtype != torch.float16 or a.stride(1) != 1 or not a.is_cuda:
+        raise ValueError("a must be an fp16 CUDA tensor with unit column stride")
+    if m:
+        g = k // GROUP
+        _need(aq, "aq", torch.int8, (m, k))
+        _need(sa, "sa", torch.float32, (g, m))
+        if asum is not None:
+            _need(asum, "asum", torch.int32, (g, m))
+        if rowop is not None:
+            _need(rowop, "rowop", torch.int32, (g, m, 8))
     lda = a.stride(0) if m > 1 else k
     _check((lib or _lib).mixllm_quant_act(_ptr(a), lda, m, k, GROUP, _ptr(aq), _ptr(sa), _ptr(asum),
                                           _ptr(rowop), _stream(stream)))
@@ -235,6 +249,16 @@ def mixllm_silu_mul_quant(gate, up, aq, sa, asum=None, rowop=None, h=None, strea
         raise ValueError("gate and up must be fp16 with unit column stride")
     if up.shape != gate.shape or (m > 1 and up.stride(0) != gate.stride(0)):
         raise ValueError("gate and up must have the same shape and row stride")
+    if m:
+        g = inter // GROUP
+        _need(aq, "aq", torch.int8, (m, inter))
+        _need(sa, "sa", torch.float32, (g, m))
+        if asum is not None:
+            _need(asum, "asum", torch.int32, (g, m))
+        if rowop is not None:
+            _need(rowop, "rowop", torch.int32, (g, m, 8))
+        if h is not None:
+            _need(h, "h", torch.float16, (m, inter))
     ld = gate.stride(0) if m > 1 else inter
     _check((lib or _lib).mixllm_silu_mul_quant(_ptr(gate), _ptr(up), ld, m, inter, GROUP, _ptr(aq), _ptr(sa),
                                                _ptr(asum), _ptr(rowop), _ptr(h), _stream(stream)))
@@ -244,23 +268,82 @@ def mixllm_gemm_workspace_bytes(m: int, n: int, k: int, n8: int) -> int:
     return int(_lib.mixllm_gemm_workspace_bytes(m, n, k, n8))
 
 
-def mixllm_gemm_w4w8a8(aq, sa, asum, rowop, m: int, n: int, k: int, n8: int, blob_dev, y, workspace=None,
+class DeviceBlob:
+    """A packed blob on the GPU with the host copy of its header (the GEMM calls check
+    the header against the layer they are asked to compute)."""
+
+    def __init__(self, blob_host: np.ndarray, device="cuda"):
+        self.info = blob_header(blob_host)
+        self.dev = torch.from_numpy(np.ascontiguousarray(blob_host, dtype=np.uint8)).to(device)
+        self.nbytes = int(self.dev.numel())
+
+
+def _need(t, name, dtype, shape=None, what=""):
+    """Argument checks before a device call: a CUDA tensor of this dtype whose shape
+    covers `shape` and whose innermost stride is 1."""
+    if t is None:
+        raise ValueError(f"{name} is required{what}")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit innermost stride")
+    if shape is not None:
+        if t.dim() != len(shape) or any(a < b for a, b in zip(t.shape, shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, needs at least {tuple(shape)}")
+        if not t.is_contiguous() and name != "y":
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _gemm_inputs(aq, sa, asum, rowop, m, k, nb4):
+    g = k // GROUP
+    _need(aq, "aq", torch.int8, (m, k))
+    _need(sa, "sa", torch.float32, (g, m))
+    if asum is not None or nb4 > 0:
+        _need(asum, "asum", torch.int32, (g, m), " for layers with 4-bit blocks")
+    _need(rowop, "rowop", torch.int32, (g, m, 8))
+    for t, name, shape in ((aq, "aq", (m, k)), (sa, "sa", (g, m)), (asum, "asum", (g, m)),
+                           (rowop, "rowop", (g, m, 8))):
+        if t is not None and m and tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+
+
+def _blob(blob):
+    if not isinstance(blob, DeviceBlob):
+        raise ValueError("blob must be a DeviceBlob (the device copy plus its host header)")
+    return blob
+
+
+def mixllm_gemm_w4w8a8(aq, sa, asum, rowop, m: int, n: int, k: int, n8: int, blob, y, workspace=None,
                        stream=None, lib=None):
-    """aq, sa, asum, rowop: outputs of mixllm_quant_act; y: fp16 [M, ldy] CUDA tensor;
-    blob_dev: uint8 CUDA tensor holding the packed blob."""
-    ldy = y.stride(0) if y.dim() == 2 and m > 1 else n
+    """aq, sa, asum, rowop: outputs of mixllm_quant_act; y: fp16 [M, ldy] CUDA tensor (ldy >= N);
+    blob: DeviceBlob of the packed layer."""
+    b = _blob(blob)
+    if m:
+        _gemm_inputs(aq, sa, asum, rowop, m, k, b.info.nb4)
+        _need(y, "y", torch.float16, (m, n))
+        if y.dim() != 2:
+            raise ValueError("y must be 2-D")
+    ldy = y.stride(0) if y is not None and y.dim() == 2 and m > 1 else n
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check((lib or _lib).mixllm_gemm_w4w8a8(_ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop), m, n, k, n8,
-                                            _ptr(blob_dev), blob_dev.numel(), _ptr(y), ldy, _ptr(workspace), ws,
-                                            _stream(stream)))
+                                            ctypes.byref(b.info), _ptr(b.dev), b.nbytes, _ptr(y), ldy,
+                                            _ptr(workspace), ws, _stream(stream)))
 
 
-def mixllm_gemm_w4w8a8_partials(aq, sa, asum, rowop, m: int, n: int, k: int, n8: int, blob_dev, n_begin: int,
+def mixllm_gemm_w4w8a8_partials(aq, sa, asum, rowop, m: int, n: int, k: int, n8: int, blob, n_begin: int,
                                 n_count: int, part, stream=None, lib=None):
     """part: int32 [M, n_count, G] CUDA tensor."""
+    b = _blob(blob)
+    if m and n_count:
+        _gemm_inputs(aq, sa, asum, rowop, m, k, b.info.nb4)
+        _need(part, "part", torch.int32, (m, n_count, k // GROUP))
+        if not part.is_contiguous():
+            raise ValueError("part must be contiguous")
     _check((lib or _lib).mixllm_gemm_w4w8a8_partials(_ptr(aq), _ptr(sa), _ptr(asum), _ptr(rowop), m, n, k, n8,
-                                                     _ptr(blob_dev), blob_dev.numel(), n_begin, n_count,
-                                                     _ptr(part), _stream(stream)))
+                                                     ctypes.byref(b.info), _ptr(b.dev), b.nbytes, n_begin,
+                                                     n_count, _ptr(part), _stream(stream)))
 
 
 def rowop_buffer(m: int, k: int, device="cuda"):
@@ -281,7 +364,7 @@ class PackedLinear:
         self.n8 = int(np.asarray(idx8).size)
         self.g = self.k // GROUP
         self.blob_host = mixllm_pack_weights(w_fp16, idx8)
-        self.blob = torch.from_numpy(self.blob_host).to(device)
+        self.blob = DeviceBlob(self.blob_host, device)
         self.device = device
 
     def buffers(self, m: int):
