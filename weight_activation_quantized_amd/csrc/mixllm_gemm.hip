@@ -195,15 +195,30 @@ constexpr int kBiasBits = 0x4B400000;               // float bits of B = 1.5 * 2
 // 16-byte chunk c of row r sits at position c ^ swz_a(r) of the row's 128 bytes.
 __device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
 
-struct TileSmem {
+// CW: the column words of the step's group pair go through LDS too (4-block tiles; a
+// 2-block tile stays within 80 KB so that two fit a CU, and its waves load their own).
+template <bool CW>
+struct TileSmemT {
   uint8_t a[kSA][kKS][kTileBM * 128];           // [stage][slice] activation tiles
   uint8_t r[kSA][kKS][kTileBM * 32];            // [stage][slice] row operand records
 };
+template <>
+struct TileSmemT<true> {
+  uint8_t a[kSA][kKS][kTileBM * 128];
+  uint8_t r[kSA][kKS][kTileBM * 32];
+  uint8_t c[kSA][kTileNB][32 * 16];             // [stage][block] column words
+};
+template <int NB>
+using TileSmem = TileSmemT<NB == kTileNB>;
 constexpr int kAStage = kKS * kTileBM * 128;        // bytes per activation stage
 constexpr int kRBase = kSA * kAStage;               // offset of the row operand stages
 constexpr int kRStage = kKS * kTileBM * 32;
-static_assert(offsetof(TileSmem, r) == kRBase, "LDS layout");
-static_assert(kKS * kTileNB * 16 * 64 * 4 + kKS * kTileNB * 32 * 32 * 2 <= (int)sizeof(TileSmem::a),
+constexpr int kCBase = kRBase + kSA * kRStage;      // offset of the column word stages
+constexpr int kCStage = kTileNB * 32 * 16;
+static_assert(offsetof(TileSmemT<false>, r) == kRBase && offsetof(TileSmemT<true>, r) == kRBase &&
+                  offsetof(TileSmemT<true>, c) == kCBase && sizeof(TileSmemT<false>) <= 80 * 1024,
+              "LDS layout");
+static_assert(kKS * kTileNB * 16 * 64 * 4 + kKS * kTileNB * 32 * 32 * 2 <= (int)sizeof(TileSmemT<false>::a),
               "reduction and output staging space");
 
 __device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
@@ -256,8 +271,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int NB, int KIND, bool PARTIALS, bool RDMA, int Q>
-__device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m0, int blk, int bi, int lane) {
+// RDMA: this wave also loads 32 rows of the row operand records per step; CDMA: it also
+// loads the column words of two of the tile's four blocks.
+template <int NB, int KIND, bool PARTIALS, bool RDMA, bool CDMA, int Q>
+__device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, int m0, int blk, int bi, int lane) {
   constexpr int q = Q;  // group slice
   constexpr bool HASW = KIND != kNone;
   constexpr int NW = KIND == kW8 ? 4 : (KIND == kW4 ? 2 : 0);     // 16-byte weight loads per step
@@ -268,8 +285,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   constexpr bool CORR = KIND == kW4 && !ZPRE && !PARTIALS;
   constexpr bool BIAS = kFoldBias && !PARTIALS;
   constexpr int kDmaRows = 64 / NB;                               // activation rows this wave loads
-  constexpr int LD = kDmaRows / 8 + (RDMA ? 1 : 0);               // direct-to-LDS loads per step
-  constexpr int NPW = PARTIALS ? 0 : 1;                           // column-word loads per step
+  constexpr bool CLDS = NB == kTileNB;                            // column words from LDS
+  constexpr bool CWORDS = CLDS && CDMA && !PARTIALS;               // (the partials need no column words)
+  constexpr int NPW = (!CLDS && !PARTIALS) ? 1 : 0;               // column-word loads into registers
+  constexpr int LD = kDmaRows / 8 + (RDMA ? 1 : 0) + (CWORDS ? 1 : 0);  // direct-to-LDS loads per step
   constexpr int LW = HASW ? NW + NPW + NZ : 0;                    // register-ring loads per step
   // Step s's batch (stage s + kSA, then weights s + kSA - 1) follows the barrier of step s.
   // Before the barrier of step s, stage s + 1 must have landed: it came first in the batch
@@ -289,8 +308,15 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
   const Rsrc rw = make_rsrc((KIND == kW8 ? p.w8 : p.w4) + (size_t)bq * G * kWChunk, (int64_t)G * kWChunk);
   const int npairs = pw_pairs(G);
-  const Rsrc rpw = make_rsrc((const uint8_t *)p.pw + (size_t)blk * npairs * kPwPairChunk,
-                             (int64_t)npairs * kPwPairChunk);
+  // Column words: through LDS, this wave loads blocks cb0 and cb0 + 1 of the tile (cb0 + 1
+  // past the layer's blocks reads zeros; lanes 32-63 take the second block); else each
+  // wave loads its own block's.
+  const int cb0 = CLDS ? 2 * (bi - 2) : bi;
+  const int cblk = blk - bi + cb0;
+  const Rsrc rpw = make_rsrc((const uint8_t *)p.pw + (size_t)cblk * npairs * kPwPairChunk,
+                             CWORDS ? (int64_t)(p.nb - cblk) * npairs * kPwPairChunk
+                                    : (NPW ? (int64_t)npairs * kPwPairChunk : 0));
+  const int vcw = CLDS ? (lane >> 5) * npairs * (int)kPwPairChunk + (lane & 31) * 16 : ch32 * 16;
   const Rsrc rz = make_rsrc(p.z4 + (size_t)blk * G * kZ4Chunk, NZ ? (int64_t)G * kZ4Chunk : 0);
 
   // Per-lane offsets.
@@ -302,7 +328,6 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   }
   // ... and (waves 0 and 1 of a slice) the 32-byte operand records of rows [32 bi, 32 bi + 32)
   const int vro = min(m0 + 32 * bi + (lane >> 1), p.M - 1) * 32 + (lane & 1) * 16;
-  const int vpw = ch32 * 16;
   int vw[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -329,15 +354,18 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     for (int i = 0; i < kDmaRows / 8; ++i)
       bload16_lds(ra, smb + J * kAStage + q * kTileBM * 128 + (kDmaRows * bi + 8 * i) * 128, vdma[i], gl * 128);
     if constexpr (RDMA) bload16_lds(rro, smb + kRBase + J * kRStage + q * kTileBM * 32 + bi * 1024, vro, gl * p.M * 32);
+    if constexpr (CWORDS)
+      bload16_lds(rpw, smb + kCBase + J * kCStage + cb0 * 512, vcw, min(s, npairs - 1) * (int)kPwPairChunk);
   };
-  // Ring slot s % kSA: this wave's weights and the column words of step s's group pair.
+  // Ring slot s % kSA: this wave's weights of step s (and in 2-block tiles the column
+  // words of its group pair).
   auto issue_w = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
     if constexpr (HASW) {
       const int gl = min(kKS * s + q, G - 1);
 #pragma unroll
       for (int t = 0; t < NW; ++t) bR[J][t] = bload16(rw, vw[t], gl * kWChunk);
-      if constexpr (NPW) pwR[J] = bload16(rpw, vpw, min(s, npairs - 1) * (int)kPwPairChunk);
+      if constexpr (NPW) pwR[J] = bload16(rpw, vcw, min(s, npairs - 1) * (int)kPwPairChunk);
       if constexpr (NZ) zR[J] = bload4(rz, (ch32 >> 3) * 4, gl * (int)kZ4Chunk);
     }
   };
@@ -455,10 +483,15 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
     // Column operands: s_w of this wave's group (2s + q) for the scale products (zero in
     // the upper half-wave, whose row operand slots are unused), and for the corrections
     // -z s_w of group 2s + h, the group whose row operands half-wave h reads.
-    const v4i pq = pwR[J];
-    // (Every word of the load stays live to here: a register written by a load still in
-    // flight cannot be reused, and reusing one would force a wait for every load.)
-    asm volatile("" ::"v"(pq));
+    v4i pq;
+    if constexpr (CLDS) {
+      pq = lds16(kCBase + J * kCStage + bi * 512 + ch32 * 16);
+    } else {
+      pq = pwR[J];
+      // (Every word of the load stays live to here: a register written by a load still in
+      // flight cannot be reused, and reusing one would force a wait for every load.)
+      asm volatile("" ::"v"(pq));
+    }
     const int sw = h ? 0 : pq[2 * q];
     const v4i bs = v4i{sw, sw, sw, sw};
     v4i bz;
@@ -592,22 +625,31 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem &sm, int m
   }
 }
 
-// The body for one wave: its block kind, whether it loads row records, its slice.
+// The body for one wave: its block kind, which shared loads it issues, its slice.  Waves
+// 0 and 1 of each slice load the row operand records (32 rows each); in 4-block tiles the
+// column words go to waves 2 and 3 of slice 1.
+template <int NB, bool PARTIALS, int Q, bool RDMA, bool CDMA>
+__device__ __forceinline__ void tile_kind(const GemmArgs &p, TileSmem<NB> &sm, int m0, int blk, int bi, int lane,
+                                          int kind) {
+  switch (kind) {
+    case kW4: tile_body<NB, kW4, PARTIALS, RDMA, CDMA, Q>(p, sm, m0, blk, bi, lane); break;
+    case kW8: tile_body<NB, kW8, PARTIALS, RDMA, CDMA, Q>(p, sm, m0, blk, bi, lane); break;
+    default: tile_body<NB, kNone, PARTIALS, RDMA, CDMA, Q>(p, sm, m0, blk, bi, lane); break;
+  }
+}
+
 template <int NB, bool PARTIALS, int Q>
-__device__ __forceinline__ void tile_dispatch(const GemmArgs &p, TileSmem &sm, int m0, int blk, int bi, int lane,
-                                              int kind) {
-  if (bi < 2) {
-    switch (kind) {
-      case kW4: tile_body<NB, kW4, PARTIALS, true, Q>(p, sm, m0, blk, bi, lane); break;
-      case kW8: tile_body<NB, kW8, PARTIALS, true, Q>(p, sm, m0, blk, bi, lane); break;
-      default: tile_body<NB, kNone, PARTIALS, true, Q>(p, sm, m0, blk, bi, lane); break;
-    }
+__device__ __forceinline__ void tile_dispatch(const GemmArgs &p, TileSmem<NB> &sm, int m0, int blk, int bi,
+                                              int lane, int kind) {
+  if constexpr (NB != kTileNB) {
+    tile_kind<NB, PARTIALS, Q, true, false>(p, sm, m0, blk, bi, lane, kind);
   } else {
-    switch (kind) {
-      case kW4: tile_body<NB, kW4, PARTIALS, false, Q>(p, sm, m0, blk, bi, lane); break;
-      case kW8: tile_body<NB, kW8, PARTIALS, false, Q>(p, sm, m0, blk, bi, lane); break;
-      default: tile_body<NB, kNone, PARTIALS, false, Q>(p, sm, m0, blk, bi, lane); break;
-    }
+    if (bi < 2)
+      tile_kind<NB, PARTIALS, Q, true, false>(p, sm, m0, blk, bi, lane, kind);
+    else if (Q == 1)
+      tile_kind<NB, PARTIALS, Q, false, true>(p, sm, m0, blk, bi, lane, kind);
+    else
+      tile_kind<NB, PARTIALS, Q, false, false>(p, sm, m0, blk, bi, lane, kind);
   }
 }
 
@@ -615,7 +657,7 @@ __device__ __forceinline__ void tile_dispatch(const GemmArgs &p, TileSmem &sm, i
 template <int NB, bool PARTIALS>
 __global__ __launch_bounds__(tile_threads(NB)) __attribute__((amdgpu_waves_per_eu(2))) void gemm_tile_kernel(
     const GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) TileSmem sm;
+  __shared__ __attribute__((aligned(16))) TileSmem<NB> sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave: uniform
   const int bi = wave % NB, q = wave / NB;

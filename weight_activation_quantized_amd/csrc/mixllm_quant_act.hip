@@ -42,6 +42,9 @@ namespace {
 #endif
 constexpr int kThreads = 256;
 constexpr int kPairsPerBlock = kThreads / 16;
+// Up to this many tokens the pairs go in group-major order (see quant_act_kernel):
+// 512 x 4096 4.69 -> 4.18 us, 1024 x 28672 25.8 -> 24.8 us; 2048 x 8192 17.0 -> 17.7 us.
+constexpr int32_t kGroupMajorMaxM = 1024;
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
@@ -152,8 +155,12 @@ __device__ __forceinline__ void quant_pair(uint4 raw, bool live, int64_t m, int 
   }
 }
 
-// Each quarter handles pairs pair0, pair0 + stride, ... with PPL of them in flight.
-template <int PPL>
+// Each quarter handles pairs pair0, pair0 + stride, ... with PPL of them in flight.  Pair
+// order: token-major (consecutive quarters take consecutive groups of one token: a wave
+// reads 1 KB of one row) or, with GMAJOR, group-major (consecutive quarters take one group
+// of consecutive tokens: a wave's scales, code sums and row records are contiguous, which
+// is faster while the outputs are small; measured on the Llama shapes).
+template <int PPL, bool GMAJOR>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__restrict__ a, int64_t lda,
                                                              int32_t M, int32_t K, int8_t *__restrict__ aq,
                                                              float *__restrict__ sa, int32_t *__restrict__ asum,
@@ -172,8 +179,13 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const uint16_t *__r
     for (int i = 0; i < PPL; ++i) {
       const int64_t pair = base + i * stride;
       live[i] = pair < npairs;
-      m[i] = live[i] ? pair / G : 0;
-      g[i] = live[i] ? (int)(pair - m[i] * G) : 0;
+      if (GMAJOR) {
+        g[i] = live[i] ? (int)(pair / M) : 0;
+        m[i] = live[i] ? pair - (int64_t)g[i] * M : 0;
+      } else {
+        m[i] = live[i] ? pair / G : 0;
+        g[i] = live[i] ? (int)(pair - m[i] * G) : 0;
+      }
       raw[i] = make_uint4(0, 0, 0, 0);
       if (live[i]) raw[i] = *reinterpret_cast<const uint4 *>(a + m[i] * lda + (int64_t)g[i] * MIXLLM_GROUP + sub * 8);
     }
@@ -239,8 +251,12 @@ extern "C" int mixllm_quant_act(const uint16_t *a, int64_t lda, int32_t M, int32
   constexpr int kPPL = MIXLLM_QA_PPL;
   int64_t blocks = (npairs + kPairsPerBlock * kPPL - 1) / (kPairsPerBlock * kPPL);
   if (blocks > MIXLLM_QA_MAXBLOCKS) blocks = MIXLLM_QA_MAXBLOCKS;
-  hipLaunchKernelGGL(quant_act_kernel<kPPL>, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a,
-                     lda, M, K, aq, sa, asum, reinterpret_cast<uint4 *>(rowop));
+  if (M <= kGroupMajorMaxM)
+    hipLaunchKernelGGL((quant_act_kernel<kPPL, true>), dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                       a, lda, M, K, aq, sa, asum, reinterpret_cast<uint4 *>(rowop));
+  else
+    hipLaunchKernelGGL((quant_act_kernel<kPPL, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       (hipStream_t)stream, a, lda, M, K, aq, sa, asum, reinterpret_cast<uint4 *>(rowop));
   return hipGetLastError() == hipSuccess ? MIXLLM_OK : MIXLLM_E_HIP;
 }
 
