@@ -47,9 +47,11 @@ def parse():
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--k", type=int, default=4096)
     ap.add_argument("--p8", type=float, default=0.10)
-    ap.add_argument("--workload", default="layer", choices=["layer", "mlp"],
+    ap.add_argument("--workload", default="layer", choices=["layer", "mlp", "qkv"],
                     help="layer: the W4.4A8 layer step (default); mlp: the Llama-3.1-8B MLP block "
-                         "(quantize, gate/up GEMM, SiLU*up + quantize, down GEMM) replayed as a HIP graph")
+                         "(quantize, gate/up GEMM, SiLU*up + quantize, down GEMM) replayed as a HIP graph; "
+                         "qkv: the Llama-3.1-8B q/k/v projections (one quantize, one GEMM over the three "
+                         "packed as one layer)")
     ap.add_argument("--variant", default="",
                     help="time a measured variant of the tile GEMM (libmixllm_<name>.so: fold_bias, zero_pre) "
                          "instead of the library")
@@ -177,7 +179,9 @@ def cpu_baseline(m, n, k, n8):
 
 def mlp_main(args):
     """The Llama-3.1-8B MLP block at M tokens as a second workload: four launches per
-    block captured in one HIP graph per rotating set; a step is one graph replay."""
+    block; the blocks of every rotating set captured in sequence as one HIP graph, a step
+    being one block (a replay is `sets` steps).  One graph per block and eager launches
+    through the Python wrapper are reported beside it."""
     import numpy as np
     import torch
     from weight_activation_quantized_amd import mixllm as L
@@ -198,33 +202,26 @@ def mlp_main(args):
     for i in range(args.warmup):
         graphs[i % sets].replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(SPIN_CYCLES)
-    e0.record()
-    for i in range(args.steps):
-        graphs[i % sets].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / args.steps
-    # the same blocks launched eagerly, for comparison
     stream = torch.cuda.current_stream()
+    single_ms, graph_host = timed_loop(args.steps, lambda i: graphs[i % sets].replay(), stream)
+    chain = capture_chain([lambda st, b=b, x=x, bb=bb: b.forward(x, bb, st) for b, x, bb in zip(blocks, xs, bufs)])
+    reps = max(1, args.steps // sets)
+    chain.replay()
+    step_ms, chain_host = timed_loop(reps, lambda i: chain.replay(), stream)
+    step_ms, chain_host = step_ms / sets, chain_host / sets
+    # the same blocks launched eagerly, for comparison
     for i in range(args.warmup):
         blocks[i % sets].forward(xs[i % sets], bufs[i % sets], stream)
     torch.cuda.synchronize()
-    torch.cuda._sleep(SPIN_CYCLES)
-    e0.record()
-    for i in range(args.steps):
-        blocks[i % sets].forward(xs[i % sets], bufs[i % sets], stream)
-    e1.record()
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / args.steps
+    eager_ms, eager_host = timed_loop(
+        args.steps, lambda i: blocks[i % sets].forward(xs[i % sets], bufs[i % sets], stream), stream)
     ops = 2.0 * m * 3 * inter * hidden
     out = {
-        "metric": "Llama-3.1-8B MLP block TOPS (W4.4A8, HIP graph)",
+        "metric": "Llama-3.1-8B MLP block TOPS (W4.4A8, HIP graph of one block per rotating set, chained)",
         "value": round(ops / (step_ms * 1e-3) / 1e12, 2),
         "unit": "TOPS",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": reps * sets,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 5),
         "higher_is_better": True,
@@ -238,6 +235,140 @@ def mlp_main(args):
                    "M": m, "hidden": hidden, "inter": inter, "rotating_sets": sets},
         "eager_ms_per_step": round(eager_ms, 5),
         "eager_tops": round(ops / (eager_ms * 1e-3) / 1e12, 2),
+        "steps_per_replay": sets,
+        "chain_host_us_per_step": round(chain_host, 2),
+        "single_block_graph_ms_per_step": round(single_ms, 5),
+        "single_block_graph_tops": round(ops / (single_ms * 1e-3) / 1e12, 2),
+        "graph_host_us_per_replay": round(graph_host, 2),
+        "eager_host_us_per_step": round(eager_host, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def timed_loop(steps, fn, stream=None):
+    """(GPU ms per call, host us per call) of `steps` calls of fn queued behind a spin
+    kernel: the GPU time is the events' span; the host time is how long the loop took to
+    enqueue, which bounds the GPU time from below whenever it is the larger of the two."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    host_us = (time.perf_counter() - t0) * 1e6 / steps
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, host_us
+
+
+def capture_chain(forwards):
+    """One HIP graph of several forward passes in sequence (each f(stream) enqueues one step
+    on its own buffers): the runtime leaves the GPU idle between two graph launches (about
+    8 us on this stack, against none between kernels inside a graph), so chaining the steps
+    of every rotating set into one graph pays that gap once per chain instead of per step."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in forwards:
+            f(s)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for f in forwards:
+            f(s)
+    return g
+
+
+def qkv_main(args):
+    """The Llama-3.1-8B q/k/v projections at M tokens: one quant_act of the hidden state
+    and one GEMM over the three projections packed as one layer (6144 channels).  The
+    value is the step (both launches) by raw C calls; the same steps replayed as HIP graphs
+    and launched through the Python wrapper are reported beside it with the host time each
+    takes to enqueue a step."""
+    import numpy as np
+    import torch
+    from weight_activation_quantized_amd import mixllm as L
+    from weight_activation_quantized_amd import workloads as WL
+
+    m = args.m
+    hidden, nq, nkv = WL.QKV8B["hidden"], WL.QKV8B["q"], WL.QKV8B["kv"]
+    n8 = WL.llama8b_n8()
+    torch.cuda.set_device(0)
+    x16, wq, wk, wv, iq, ik, iv = WL.qkv_inputs(m, hidden, nq, nkv, n8)
+    p0 = L.QKVProjection(wq, wk, wv, iq, ik, iv)
+    n = nq + 2 * nkv
+    n8_all = n8["q"] + n8["k"] + n8["v"]
+    set_bytes = p0.layer.blob.nbytes + m * hidden * 6 + m * n * 2
+    sets = args.sets or max(2, int(np.ceil(512e6 / set_bytes)))
+    projs = [p0] + [L.QKVProjection(wq, wk, wv, iq, ik, iv) for _ in range(sets - 1)]
+    xs = [torch.from_numpy(x16).cuda() for _ in range(sets)]
+    bufs = [pj.buffers(m) for pj in projs]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    lib = L.library_handle()
+    qa_fn, gm_fn = lib.mixllm_quant_act, lib.mixllm_gemm_w4w8a8
+    hdr_p = ctypes.byref(p0.layer.blob.info)
+    qargs = [(x.data_ptr(), hidden, m, hidden, 128, b["aq"].data_ptr(), b["sa"].data_ptr(), b["asum"].data_ptr(),
+              b["rowop"].data_ptr(), sp) for x, b in zip(xs, bufs)]
+    gargs = [(b["aq"].data_ptr(), b["sa"].data_ptr(), b["asum"].data_ptr(), b["rowop"].data_ptr(), m, n, hidden,
+              n8_all, hdr_p, pj.layer.blob.dev.data_ptr(), pj.layer.blob.nbytes, b["y"].data_ptr(), n, None, 0, sp)
+             for pj, b in zip(projs, bufs)]
+
+    def raw(i):
+        qa_fn(*qargs[i % sets])
+        gm_fn(*gargs[i % sets])
+
+    rc = 0
+    for i in range(args.warmup):
+        rc = rc or qa_fn(*qargs[i % sets]) or gm_fn(*gargs[i % sets])
+    torch.cuda.synchronize()
+    if rc:
+        raise L.MixLLMError(rc)
+    step_ms, raw_host = timed_loop(args.steps, raw, stream)
+
+    def py(i):
+        projs[i % sets].forward(xs[i % sets], bufs[i % sets], stream)
+
+    for i in range(min(args.warmup, 50)):
+        py(i)
+    py_ms, py_host = timed_loop(args.steps, py, stream)
+    graphs = [pj.capture(x, b) for pj, x, b in zip(projs, xs, bufs)]
+    for i in range(min(args.warmup, 50)):
+        graphs[i % sets].replay()
+    g_ms, g_host = timed_loop(args.steps, lambda i: graphs[i % sets].replay(), stream)
+    chain = capture_chain([lambda st, pj=pj, x=x, b=b: pj.forward(x, b, st) for pj, x, b in zip(projs, xs, bufs)])
+    reps = max(1, args.steps // sets)
+    chain.replay()
+    c_ms, c_host = timed_loop(reps, lambda i: chain.replay(), stream)
+    c_ms, c_host = c_ms / sets, c_host / sets
+    ops = 2.0 * m * n * hidden
+    tops = lambda ms: round(ops / (ms * 1e-3) / 1e12, 2)
+    out = {
+        "metric": "Llama-3.1-8B q/k/v projection TOPS (W4.4A8)",
+        "value": tops(step_ms),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"Llama-3.1-8B q/k/v projections M={m} hidden={hidden}: one quant_act, one GEMM "
+                               f"over q|k|v packed as one layer (N={n}); 8-bit channels q {n8['q']}, k {n8['k']}, "
+                               f"v {n8['v']}",
+                   "M": m, "N": n, "K": hidden, "n8": n8_all, "rotating_sets": sets},
+        "host_us_per_step": round(raw_host, 2),
+        "python_wrapper": {"ms_per_step": round(py_ms, 5), "tops": tops(py_ms), "host_us_per_step": round(py_host, 2)},
+        "hip_graph": {"ms_per_step": round(g_ms, 5), "tops": tops(g_ms), "host_us_per_replay": round(g_host, 2)},
+        "hip_graph_chain": {"ms_per_step": round(c_ms, 5), "tops": tops(c_ms), "steps_per_replay": sets,
+                            "host_us_per_step": round(c_host, 2)},
     }
     print(json.dumps(out), flush=True)
 
@@ -250,6 +381,8 @@ def main():
         sys.exit(2)
     if args.workload == "mlp":
         return mlp_main(args)
+    if args.workload == "qkv":
+        return qkv_main(args)
 
     import numpy as np
     import torch

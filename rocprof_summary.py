@@ -15,7 +15,16 @@
       mean per dispatch of every counter that the --pmc passes in the DIRs collected for
       kernel NAME (rows of one dispatch summed), with the pass's command.
 
-Reads only CSV files; runs nothing.
+  python rocprof_summary.py gaps DIR --cmd "..." [--labels a,b,c] > gaps.txt
+      from DIR's *_kernel_trace.csv: the dispatches in start order, split into phases at
+      each spin kernel (the head start the benchmark queues before a timed loop); per
+      phase the median duration of each kernel and the median and 90th-percentile idle
+      gap between consecutive kernels, by the pair (previous kernel -> next kernel).
+
+The `stats` and `counters` summaries take --source FILE to record the kernel source's
+sha256 prefix they were taken on.
+
+Reads only CSV files (and --source); runs nothing.
 """
 from __future__ import annotations
 
@@ -77,7 +86,7 @@ def _pick(table, kernel):
 
 def cmd_stats(a):
     rows = kernel_stats(a.dir)
-    print(f"# rocprofv3 kernel-trace summary: {a.title}")
+    print(f"# rocprofv3 kernel-trace summary: {a.title}{source_note(a.source)}")
     print(f"# command: {a.cmd}")
     print("#")
     print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'time%':>6s}")
@@ -125,8 +134,55 @@ def cmd_traffic(a):
     print()
 
 
+def source_note(path):
+    if not path:
+        return ""
+    with open(path, "rb") as f:
+        return f"; source {os.path.basename(path)} sha256/16 {hashlib.sha256(f.read()).hexdigest()[:16]}"
+
+
+def _pct(vals, q):
+    v = sorted(vals)
+    return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+
+def cmd_gaps(a):
+    rows = []
+    for f in _find(a.dir, "_kernel_trace.csv"):
+        for r in csv.DictReader(open(f)):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short_name(r["Kernel_Name"])))
+    rows.sort()
+    labels = a.labels.split(",") if a.labels else []
+    print(f"# rocprofv3 kernel-trace gaps: {a.title}")
+    print(f"# command: {a.cmd}")
+    print("# phases split at the spin kernels; durations and idle gaps (next start - previous end) in us")
+    phases, cur = [], []
+    for r in rows:
+        if a.split in r[2]:
+            phases.append(cur)
+            cur = []
+        else:
+            cur.append(r)
+    phases.append(cur)
+    timed = [ph for ph in phases[1:] if len(ph) >= a.min]
+    for i, ph in enumerate(timed):
+        name = labels[i] if i < len(labels) else f"phase {i}"
+        span = (ph[-1][1] - ph[0][0]) / 1e3
+        print(f"## {name}: {len(ph)} dispatches over {span:.1f} us")
+        durs = collections.defaultdict(list)
+        for st, en, n in ph:
+            durs[n].append((en - st) / 1e3)
+        for n, v in durs.items():
+            print(f"   kernel {n:40s} n={len(v):5d} duration p50 {statistics.median(v):8.2f}")
+        gaps = collections.defaultdict(list)
+        for (s0, e0, n0), (s1, e1, n1) in zip(ph[:-1], ph[1:]):
+            gaps[(n0, n1)].append((s1 - e0) / 1e3)
+        for (n0, n1), v in gaps.items():
+            print(f"   gap {n0} -> {n1}: n={len(v)} p50 {statistics.median(v):.2f} p90 {_pct(v, 0.9):.2f}")
+
+
 def cmd_counters(a):
-    print(f"# rocprofv3 counter summary: {a.title}")
+    print(f"# rocprofv3 counter summary: {a.title}{source_note(a.source)}")
     print(f"# command (one run per pass, PASS = the counters of one directory): {a.cmd}")
     print(f"# kernel: {a.kernel}; values are means over its dispatches of the per-dispatch sums")
     print("#")
@@ -146,6 +202,7 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("--cmd", required=True)
     s.add_argument("--title", default="")
+    s.add_argument("--source", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -161,8 +218,16 @@ def main(argv=None):
     c.add_argument("--kernel", required=True)
     c.add_argument("--cmd", required=True)
     c.add_argument("--title", default="")
+    c.add_argument("--source", default="")
+    g = sub.add_parser("gaps")
+    g.add_argument("dir")
+    g.add_argument("--cmd", required=True)
+    g.add_argument("--title", default="")
+    g.add_argument("--labels", default="")
+    g.add_argument("--split", default="spin_kernel")
+    g.add_argument("--min", type=int, default=10)
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters, "gaps": cmd_gaps}[a.what](a)
 
 
 if __name__ == "__main__":

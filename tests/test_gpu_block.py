@@ -1,5 +1,6 @@
-"""The Llama MLP block around the layer on the GPU, through the C ABI: the fused
-SiLU(gate) * up + quantization kernel, the block's four launches, and its HIP-graph replay.
+"""The Llama MLP block and the q/k/v projections around the layer on the GPU, through the
+C ABI: the fused SiLU(gate) * up + quantization kernel, the block's four launches, the
+three projections packed as one layer, and their HIP-graph replays.
 
 Each step is compared with the oracle applied to the GPU's own input of that step (the
 steps round to fp16 in between, so this is how a pipeline's parity is checked):
@@ -120,3 +121,80 @@ def test_mlp_block_graph_replays(L, m):
         blk.forward(x, eager_bufs)                # and an eager pass on other buffers
         torch.cuda.synchronize()
         assert torch.equal(eager_bufs["h"]["y"], want)
+
+
+@pytest.mark.parametrize("m,rows", [(1, None), (16, None), (130, None), (512, 12)])
+def test_qkv_projection(L, m, rows):
+    """Llama-3.1-8B q, k, v over one hidden state: one quant_act, one GEMM over the packed
+    6144 channels; each projection within the layer tolerance of the oracle applied to it
+    alone."""
+    n8 = WL.llama8b_n8()
+    x16, wq, wk, wv, iq, ik, iv = WL.qkv_inputs(m, WL.QKV8B["hidden"], WL.QKV8B["q"], WL.QKV8B["kv"], n8)
+    U.say("qkv projection", m)
+    proj = L.QKVProjection(wq, wk, wv, iq, ik, iv)
+    bufs = proj.buffers(m)
+    q, k, v = proj.forward(torch.from_numpy(x16).cuda(), bufs)
+    torch.cuda.synchronize()
+    assert q.shape == (m, 4096) and k.shape == (m, 1024) and v.shape == (m, 1024)
+    rs = np.arange(m) if rows is None else U.sample_rows(m, np.random.default_rng(7), rows)
+    for name, out, w, idx in (("q", q, wq, iq), ("k", k, wk, ik), ("v", v, wv, iv)):
+        ref = U.oracle_at(x16[rs], w, idx)
+        U.assert_y_close(out.cpu().numpy()[rs], ref["y16"], name)
+
+
+def test_qkv_graph_replays(L):
+    n8 = dict(q=22, k=5, v=73)
+    m = 40
+    x16, wq, wk, wv, iq, ik, iv = WL.qkv_inputs(m, 512, 512, 128, n8, (33,))
+    proj = L.QKVProjection(wq, wk, wv, iq, ik, iv)
+    x = torch.from_numpy(x16).cuda()
+    U.say("qkv graph", m)
+    eager_bufs = proj.buffers(m)
+    want = torch.cat(proj.forward(x, eager_bufs), dim=1).clone()
+    torch.cuda.synchronize()
+    bufs = proj.buffers(m)
+    graph = proj.capture(x, bufs)
+    other = torch.randn(1 << 20, device="cuda")
+    for i in range(4):
+        bufs["y"].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["y"], want), f"replay {i}"
+        other.mul_(1.0001).add_(1.0)
+        proj.forward(x, eager_bufs)
+        torch.cuda.synchronize()
+        assert torch.equal(eager_bufs["y"], want)
+
+
+def test_graph_of_chained_steps(L):
+    """Several steps (each on its own buffers) captured in sequence as one graph: every
+    step's output equals its eager forward pass, on every replay."""
+    n8 = dict(q=22, k=5, v=73)
+    m = 24
+    x16, wq, wk, wv, iq, ik, iv = WL.qkv_inputs(m, 512, 512, 128, n8, (34,))
+    projs = [L.QKVProjection(wq, wk, wv, iq, ik, iv) for _ in range(3)]
+    xs = [torch.from_numpy(x16).cuda() * (1 + j) for j in range(3)]
+    U.say("graph chain", m)
+    want = []
+    for pj, x in zip(projs, xs):
+        want.append(torch.cat(pj.forward(x, pj.buffers(m)), dim=1).clone())
+    torch.cuda.synchronize()
+    bufs = [pj.buffers(m) for pj in projs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for pj, x, b in zip(projs, xs, bufs):
+            pj.forward(x, b, s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for pj, x, b in zip(projs, xs, bufs):
+            pj.forward(x, b, s)
+    for r in range(3):
+        for b in bufs:
+            b["y"].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for j, b in enumerate(bufs):
+            assert torch.equal(b["y"], want[j]), f"replay {r} step {j}"

@@ -57,6 +57,25 @@ def test_pack_matches_oracle(n, k, n8):
     assert info["total_bytes"] == blob.size == L.mixllm_packed_bytes(n, k, 128, n8)
 
 
+def test_concat_layers_packs_each_projection_as_alone():
+    """q, k, v packed as one layer: each slice of the unpacked blob equals that projection
+    quantized on its own (the concatenation shifts only the 8-bit indices)."""
+    n8 = dict(q=22, k=5, v=73)
+    x, wq, wk, wv, iq, ik, iv = WL.qkv_inputs(1, 256, 128, 96, n8)
+    w, idx, bounds = L.concat_layers((wq, wk, wv), (iq, ik, iv))
+    assert bounds == [(0, 128), (128, 224), (224, 320)]
+    assert idx.size == 22 + 5 + 73 and np.all(np.diff(idx) > 0)
+    q, z, s16, is8 = L.mixllm_unpack_weights(L.mixllm_pack_weights(w, idx))
+    for (a, b), wp, ip in zip(bounds, (wq, wk, wv), (iq, ik, iv)):
+        oq, oz, os_, ois8 = O.quant_weights_mixed(wp, ip)
+        assert np.array_equal(is8[a:b], ois8)
+        assert np.array_equal(q[a:b], (oq.astype(np.int16) & 0xFF).astype(np.uint8))
+        assert np.array_equal(z[a:b], oz)
+        assert np.array_equal(s16[a:b].view(np.uint16), os_.view(np.uint16))
+    with pytest.raises(ValueError):
+        L.concat_layers((wq, wk[:, :128]), (iq, ik))
+
+
 def _bf16_pair_value(words):
     """Value of packed bf16 pairs (low half + high half), exactly, in float64."""
     lo = ((words & 0xFFFF).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

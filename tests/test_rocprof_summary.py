@@ -42,3 +42,32 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path, capsys):
     # the copy read 1 MiB but FETCH_SIZE saw 512 KiB: factor 2; WRITE_SIZE saw all of it
     assert d["fetch_scale"] == 2.0 and d["write_scale"] == 1.0
     assert d["hbm_bytes_per_launch"] == 100 * 1024 * 2 + 10 * 1024
+
+
+def test_gaps_split_at_spin_kernels_and_pair_neighbours(tmp_path, capsys):
+    d = tmp_path / "t"
+    d.mkdir()
+    cols = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    rows = [("warmup_kernel(A)", 0, 10),
+            ("at::cuda::spin_kernel(long)", 20, 1000)]
+    t = 1000
+    for i in range(10):                       # phase "raw": back to back
+        rows.append(("void (anonymous namespace)::quant_act_kernel<1>(A)", t, t + 3000)); t += 3000
+        rows.append(("void (anonymous namespace)::gemm_tile_kernel<4, false>(G)", t, t + 9000)); t += 9000
+    rows.append(("at::cuda::spin_kernel(long)", t, t + 500)); t += 500
+    for i in range(10):                       # phase "graph": 8 us before each step
+        t += 8000
+        rows.append(("void (anonymous namespace)::quant_act_kernel<1>(A)", t, t + 3000)); t += 3000
+        rows.append(("void (anonymous namespace)::gemm_tile_kernel<4, false>(G)", t, t + 9000)); t += 9000
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        w.writerows(rows)
+    RS.main(["gaps", str(d), "--cmd", "c", "--labels", "raw,graph"])
+    out = capsys.readouterr().out
+    raw, graph = out.split("## graph")
+    assert "## raw: 20 dispatches" in raw and "warmup" not in out
+    assert "gap gemm_tile_kernel<4, false> -> quant_act_kernel<1>: n=9 p50 0.00" in raw
+    assert "gap gemm_tile_kernel<4, false> -> quant_act_kernel<1>: n=9 p50 8.00 p90 8.00" in graph
+    assert "gap quant_act_kernel<1> -> gemm_tile_kernel<4, false>: n=10 p50 0.00" in graph
+    assert "duration p50     9.00" in graph

@@ -389,6 +389,52 @@ class PackedLinear:
         return bufs["y"]
 
 
+def concat_layers(weights, idx8s):
+    """Several layers over the same input as one: their fp16 weights stacked along the output
+    channels, each layer's 8-bit channel indices shifted to its rows.  Returns (w, idx8,
+    bounds), bounds[i] = the output columns (begin, end) of layer i."""
+    ws = [np.asarray(w, np.float16) for w in weights]
+    if len({w.shape[1] for w in ws}) != 1:
+        raise ValueError("the layers must share the input width")
+    offs = np.cumsum([0] + [w.shape[0] for w in ws])
+    idx = np.concatenate([np.asarray(i, np.int32).reshape(-1) + np.int32(o) for i, o in zip(idx8s, offs[:-1])])
+    return np.concatenate(ws), idx, [(int(offs[i]), int(offs[i + 1])) for i in range(len(ws))]
+
+
+class QKVProjection:
+    """The attention input projections of one hidden state: q, k and v packed together as
+    one layer (their output channels concatenated, each keeping its own 8-bit channels),
+    so one activation quantization and one GEMM launch produce all three.  ``forward``
+    returns views of the one output.  Argument marshalling only."""
+
+    def __init__(self, w_q, w_k, w_v, idx8_q, idx8_k, idx8_v, device="cuda"):
+        w, idx, self.bounds = concat_layers((w_q, w_k, w_v), (idx8_q, idx8_k, idx8_v))
+        self.layer = PackedLinear(w, idx, device)
+        self.device = device
+
+    def buffers(self, m: int):
+        return self.layer.buffers(m)
+
+    def split(self, y):
+        return tuple(y[:, a:b] for a, b in self.bounds)
+
+    def forward(self, x, bufs, stream=None):
+        return self.split(self.layer.forward(x, bufs, stream))
+
+    def capture(self, x, bufs):
+        """A HIP graph of one forward pass on these buffers (torch.cuda.CUDAGraph)."""
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.forward(x, bufs, s)  # warm-up outside the capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self.forward(x, bufs, s)
+        return g
+
+
 class MLPBlock:
     """The Llama MLP block on the packed layers: one activation quantization feeds one GEMM
     over the gate and up channels (packed together as one layer of 2I channels), the fused
@@ -397,8 +443,7 @@ class MLPBlock:
 
     def __init__(self, w_gate, w_up, w_down, idx8_gate, idx8_up, idx8_down, device="cuda"):
         self.inter, self.hidden = np.asarray(w_gate).shape
-        w_gu = np.concatenate([np.asarray(w_gate, np.float16), np.asarray(w_up, np.float16)])
-        idx_gu = np.concatenate([np.asarray(idx8_gate, np.int32), np.asarray(idx8_up, np.int32) + self.inter])
+        w_gu, idx_gu, _ = concat_layers((w_gate, w_up), (idx8_gate, idx8_up))
         self.gu = PackedLinear(w_gu, idx_gu, device)
         self.down = PackedLinear(np.asarray(w_down, np.float16), idx8_down, device)
         self.device = device

@@ -178,3 +178,20 @@ def mlp_block_inputs(m: int, hidden: int, inter: int, n8: dict, seed=(9,), dist:
     wd = make_weights(hidden, inter, key + (3,))
     return (x, wg, wu, wd, make_idx8(inter, n8["gate"], key + (1,)), make_idx8(inter, n8["up"], key + (2,)),
             make_idx8(hidden, n8["down"], key + (3,)))
+
+
+# Llama-3.1-8B attention input projections: q (4096 channels), k and v (1024 each, grouped
+# query attention), all over the 4096-wide hidden state; 8-bit counts as in llama8b_n8().
+QKV8B = dict(hidden=4096, q=4096, kv=1024)
+
+
+def qkv_inputs(m: int, hidden: int, nq: int, nkv: int, n8: dict, seed=(11,), dist: str = "normal"):
+    """(x fp16 [M, hidden], w_q [nq, hidden], w_k, w_v [nkv, hidden] fp16, idx8_q, idx8_k,
+    idx8_v) for the three projections that read one hidden state."""
+    key = tuple(seed) + (hidden, nq, nkv)
+    x = make_acts(m, hidden, key + (m,), dist)
+    wq = make_weights(nq, hidden, key + (1,))
+    wk = make_weights(nkv, hidden, key + (2,))
+    wv = make_weights(nkv, hidden, key + (3,))
+    return (x, wq, wk, wv, make_idx8(nq, n8["q"], key + (1,)), make_idx8(nkv, n8["k"], key + (2,)),
+            make_idx8(nkv, n8["v"], key + (3,)))
