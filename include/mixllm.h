@@ -43,7 +43,7 @@ extern "C" {
 
 #define MIXLLM_GROUP 128
 #define MIXLLM_BLOB_MAGIC 0x344C584Du /* "MXL4" little-endian */
-#define MIXLLM_BLOB_VERSION 5u
+#define MIXLLM_BLOB_VERSION 6u
 
 typedef enum mixllm_status {
   MIXLLM_OK = 0,
@@ -65,7 +65,7 @@ typedef struct mixllm_blob_info {
   int32_t nb4;                  /* 4-bit blocks: floor(n4 / 32) */
   int32_t nb8;                  /* 8-bit blocks: nb - nb4 */
   int32_t n4_promoted;          /* n4 - 32 nb4 4-bit channels stored in the first 8-bit block */
-  uint64_t off_w4, off_s4, off_z4, off_w8, off_s8, off_zp, off_idx, off_pw, total_bytes;
+  uint64_t off_w4, off_s4, off_z4, off_w8, off_s8, off_zp, off_idx, total_bytes;
 } mixllm_blob_info;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -92,9 +92,8 @@ const char *mixllm_status_str(int status);
  * to a multiple of 32, in blocks of 32 channels.  Whole blocks of 4-bit channels keep
  * packed nibbles; the n4 % 32 leftover 4-bit channels share the first 8-bit block,
  * stored as their int8 partial dequantization (q - z) (the same two-step arithmetic).
- * The blob also holds, per channel and group, s_w and -z * s_w as exact sums of two bf16
- * values (the column operands of the GEMM's scale products).  The blob is position
- * independent: a byte copy of it to device memory is what the GEMM reads.
+ * The blob is position independent: a byte copy of it to device memory is what the GEMM
+ * reads.
  * ------------------------------------------------------------------------------------ */
 
 /* Size in bytes of the blob for these parameters, or 0 if they are invalid. */

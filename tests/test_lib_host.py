@@ -76,45 +76,43 @@ def test_concat_layers_packs_each_projection_as_alone():
         L.concat_layers((wq, wk[:, :128]), (iq, ik))
 
 
-def _bf16_pair_value(words):
-    """Value of packed bf16 pairs (low half + high half), exactly, in float64."""
-    lo = ((words & 0xFFFF).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    hi = ((words >> 16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return lo + hi
+def _split_bf16_pair(x32):
+    """The tile kernel's operand split, restated: the leading 8 significant bits of the
+    fp32 value (its bf16 truncation) and the remainder, as float64 values."""
+    x32 = np.asarray(x32, np.float32)
+    b0 = x32.view(np.uint32) & np.uint32(0xFFFF0000)
+    hi = b0.view(np.float32)
+    lo = (x32 - hi).astype(np.float32)
+    return hi.astype(np.float64), lo
 
 
-@pytest.mark.parametrize("n,k,n8", [(200, 512, 169), (100, 384, 7), (64, 256, 0), (96, 640, 40)])
-def test_pack_scale_words(n, k, n8):
-    """The pw section holds, per packed channel and group pair, s_w and -z * s_w of both
-    groups as exact bf16 pairs (0 in the second word for 8-bit, promoted and empty
-    channels), and zeros for every group from G on (at least one whole pair per block)."""
-    sh = WL.Shape(0, "edge", 1, n, k, n8)
-    w, idx8 = WL.make_layer_weights(sh)
-    blob = L.mixllm_pack_weights(w, idx8)
-    info = L.mixllm_blob_get_info(blob)
-    q, z, s16, is8 = L.mixllm_unpack_weights(blob)
-    g = k // 128
-    nb = info["nb"]
-    npairs = (g + 1) // 2 + 1
-    pw = blob[info["off_pw"]: info["off_pw"] + nb * npairs * 512].view(np.uint32).reshape(nb, npairs, 32, 2, 2)
-    # [block][pair][channel][group of the pair][word] -> [block][group][channel][word]
-    pw = pw.transpose(0, 1, 3, 2, 4).reshape(nb, 2 * npairs, 32, 2)
-    assert 2 * npairs >= g + 2
-    assert not pw[:, g:].any()
-    idx = blob[info["off_idx"]: info["off_idx"] + nb * 32 * 4].view(np.int32)
-    s64 = s16.astype(np.float64)
-    for j in range(nb * 32):
-        b, c = divmod(j, 32)
-        sw = _bf16_pair_value(pw[b, :g, c, 0])
-        zw = _bf16_pair_value(pw[b, :g, c, 1])
-        o = idx[j]
-        if o < 0:
-            assert not sw.any() and not zw.any()
-            continue
-        assert np.array_equal(sw, s64[o]), j
-        in_nibbles = j < 32 * info["nb4"]
-        expect_z = -(z[o].astype(np.float64) * s64[o]) if in_nibbles else np.zeros(g)
-        assert np.array_equal(zw, expect_z), j
+def test_column_operands_split_exactly_into_bf16_pairs():
+    """The GEMM's scale-product operands s_w and z * s_w (z in 0..15) are formed on the
+    device as two bf16 values each: exhaustively over every finite fp16 s_w, both
+    products are exact in fp32 and the remainder after the bf16 truncation is itself a
+    bf16 value (its low 16 bits are zero), so the pair sums to the value exactly."""
+    s16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    s16 = s16[np.isfinite(s16)]
+    for z in range(16):
+        v64 = z * s16.astype(np.float64)
+        v32 = v64.astype(np.float32)
+        assert np.array_equal(v32.astype(np.float64), v64), z     # z * s_w exact in fp32
+        hi, lo = _split_bf16_pair(v32)
+        assert not (lo.view(np.uint32) & np.uint32(0xFFFF)).any(), z  # a bf16 value
+        assert np.array_equal(hi + lo.astype(np.float64), v64), z
+
+
+def test_blob_has_no_column_word_section():
+    """Every byte after the channel indices is alignment padding: the tile kernel reads
+    the column scales and zero points from s4, s8 and z4."""
+    for n, k, n8 in [(200, 512, 169), (100, 384, 7), (64, 256, 0)]:
+        w, idx8 = WL.make_layer_weights(WL.Shape(0, "edge", 1, n, k, n8))
+        blob = L.mixllm_pack_weights(w, idx8)
+        info = L.mixllm_blob_get_info(blob)
+        nb = info["nb"]
+        end_idx = info["off_idx"] + nb * 32 * 4
+        assert info["total_bytes"] == (end_idx + 255) // 256 * 256
+        assert not blob[end_idx:].any()
 
 
 def test_pack_special_groups():
@@ -151,7 +149,6 @@ def test_packed_bytes_formula():
         g = k // 128
         w_bytes = 32 * k * (nb4 * O.weight_footprint(4) + nb8 * O.weight_footprint(8))
         side = 32 * g  # zero points of the <= 31 promoted 4-bit channels (unpacking only)
-        side += nb * ((g + 1) // 2 + 1) * 512  # the tile kernel's column words: 8 bytes per channel and group, plus a zero pair
         size = L.mixllm_packed_bytes(n, k, 128, n8)
         assert w_bytes + 4 * 32 * nb + side <= size <= w_bytes + 4 * 32 * nb + side + 8 * 256 + 256
         # the padding to 32-channel blocks and the <= 31 4-bit channels stored as int8
@@ -253,7 +250,7 @@ def test_device_entry_points_validate_on_host():
         wo, io = WL.make_layer_weights(WL.Shape(0, "edge", 1, *other))
         ho = L.blob_header(L.mixllm_pack_weights(wo, io))
         assert gm(*f4, 4, 64, 256, 2, ctypes.byref(ho), fake, 1 << 20, fake, 64, None, 0, s) == -6, other
-    for field, delta in [("version", -1), ("magic", 1), ("off_pw", 256), ("total_bytes", -256), ("nb4", 1)]:
+    for field, delta in [("version", -1), ("magic", 1), ("off_idx", 256), ("total_bytes", -256), ("nb4", 1)]:
         h2 = L.blob_header(L.mixllm_pack_weights(wl, il))
         setattr(h2, field, getattr(h2, field) + delta)
         assert gm(*f4, 4, 64, 256, 2, ctypes.byref(h2), fake, 1 << 20, fake, 64, None, 0, s) == -6, field

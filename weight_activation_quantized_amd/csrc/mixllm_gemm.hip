@@ -72,7 +72,6 @@ struct GemmArgs {
   const uint8_t *w8;
   const uint16_t *s8;
   const int32_t *idx;
-  const uint32_t *pw;
   int n4, nb, nb4;
   uint16_t *y;
   int64_t ldy;
@@ -195,8 +194,9 @@ constexpr int kBiasBits = 0x4B400000;               // float bits of B = 1.5 * 2
 // 16-byte chunk c of row r sits at position c ^ swz_a(r) of the row's 128 bytes.
 __device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
 
-// CW: the column words of the step's group pair go through LDS too (4-block tiles; a
-// 2-block tile stays within 80 KB so that two fit a CU, and its waves load their own).
+// CW: the column scales and zero points of the step's two groups go through LDS too
+// (4-block tiles; a 2-block tile stays within 80 KB so that two fit a CU, and its waves
+// load their own).
 template <bool CW>
 struct TileSmemT {
   uint8_t a[kSA][kKS][kTileBM * 128];           // [stage][slice] activation tiles
@@ -206,15 +206,17 @@ template <>
 struct TileSmemT<true> {
   uint8_t a[kSA][kKS][kTileBM * 128];
   uint8_t r[kSA][kKS][kTileBM * 32];
-  uint8_t c[kSA][kTileNB][32 * 16];             // [stage][block] column words
+  uint8_t c[kSA][2048];  // [stage]: fp16 scales [block][group of the pair][32], zero points at 1024
 };
 template <int NB>
 using TileSmem = TileSmemT<NB == kTileNB>;
 constexpr int kAStage = kKS * kTileBM * 128;        // bytes per activation stage
 constexpr int kRBase = kSA * kAStage;               // offset of the row operand stages
 constexpr int kRStage = kKS * kTileBM * 32;
-constexpr int kCBase = kRBase + kSA * kRStage;      // offset of the column word stages
-constexpr int kCStage = kTileNB * 32 * 16;
+constexpr int kCBase = kRBase + kSA * kRStage;      // offset of the column stages
+constexpr int kCStage = 2048;
+constexpr int kCZero = 1024;                        // zero points within a column stage
+static_assert(kTileNB * 2 * 64 <= kCZero && kCZero + 64 * 16 <= kCStage, "column stage");
 static_assert(offsetof(TileSmemT<false>, r) == kRBase && offsetof(TileSmemT<true>, r) == kRBase &&
                   offsetof(TileSmemT<true>, c) == kCBase && sizeof(TileSmemT<false>) <= 80 * 1024,
               "LDS layout");
@@ -246,6 +248,24 @@ __device__ __forceinline__ v4i bload16(Rsrc r, int voff, int soff) {
 __device__ __forceinline__ uint32_t bload4(Rsrc r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+__device__ __forceinline__ uint32_t bload2(Rsrc r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bload1(Rsrc r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+// A per-lane offset past every descriptor's range: the load returns zeros, moves nothing.
+constexpr int kOob = 0x7FFFFF00;
+
+// x (at most 16 significant bits) as an exact sum of two bf16 values, packed as a word
+// for a bf16 matrix-core operand: the leading 8 significant bits in the low half, the
+// remainder (exact: at most 8 bits) in the high half.
+__device__ __forceinline__ uint32_t bf16_pair(float x) {
+  const uint32_t b0 = __float_as_uint(x) & 0xFFFF0000u;
+  const uint32_t b1 = __float_as_uint(x - __uint_as_float(b0));
+  // bytes 2, 3 of b0 into bytes 0, 1 and bytes 2, 3 of b1 into bytes 2, 3 (one v_perm_b32)
+  return __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+}
 typedef __attribute__((address_space(3))) void *LdsPtr;
 // 16 bytes per lane from the buffer into LDS at dst + 16 * lane (dst wave-uniform).
 __device__ __forceinline__ void bload16_lds(Rsrc r, void *dst, int voff, int soff) {
@@ -272,7 +292,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // RDMA: this wave also loads 32 rows of the row operand records per step; CDMA: it also
-// loads the column words of two of the tile's four blocks.
+// loads the column scales (wave 2) or zero points (wave 3) of the tile's four blocks.
 template <int NB, int KIND, bool PARTIALS, bool RDMA, bool CDMA, int Q>
 __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, int m0, int blk, int bi, int lane) {
   constexpr int q = Q;  // group slice
@@ -285,9 +305,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
   constexpr bool CORR = KIND == kW4 && !ZPRE && !PARTIALS;
   constexpr bool BIAS = kFoldBias && !PARTIALS;
   constexpr int kDmaRows = 64 / NB;                               // activation rows this wave loads
-  constexpr bool CLDS = NB == kTileNB;                            // column words from LDS
-  constexpr bool CWORDS = CLDS && CDMA && !PARTIALS;               // (the partials need no column words)
-  constexpr int NPW = (!CLDS && !PARTIALS) ? 1 : 0;               // column-word loads into registers
+  constexpr bool CLDS = NB == kTileNB;                            // column values from LDS
+  constexpr bool CWORDS = CLDS && CDMA && !PARTIALS;               // (the partials need no column values)
+  constexpr int NPW = (!CLDS && !PARTIALS) ? (CORR ? 2 : 1) : 0;  // column-value loads into registers
   constexpr int LD = kDmaRows / 8 + (RDMA ? 1 : 0) + (CWORDS ? 1 : 0);  // direct-to-LDS loads per step
   constexpr int LW = HASW ? NW + NPW + NZ : 0;                    // register-ring loads per step
   // Step s's batch (stage s + kSA, then weights s + kSA - 1) follows the barrier of step s.
@@ -307,16 +327,31 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
   const int bq = KIND == kW8 ? blk - p.nb4 : blk;
   constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
   const Rsrc rw = make_rsrc((KIND == kW8 ? p.w8 : p.w4) + (size_t)bq * G * kWChunk, (int64_t)G * kWChunk);
-  const int npairs = pw_pairs(G);
-  // Column words: through LDS, this wave loads blocks cb0 and cb0 + 1 of the tile (cb0 + 1
-  // past the layer's blocks reads zeros; lanes 32-63 take the second block); else each
-  // wave loads its own block's.
-  const int cb0 = CLDS ? 2 * (bi - 2) : bi;
-  const int cblk = blk - bi + cb0;
-  const Rsrc rpw = make_rsrc((const uint8_t *)p.pw + (size_t)cblk * npairs * kPwPairChunk,
-                             CWORDS ? (int64_t)(p.nb - cblk) * npairs * kPwPairChunk
-                                    : (NPW ? (int64_t)npairs * kPwPairChunk : 0));
-  const int vcw = CLDS ? (lane >> 5) * npairs * (int)kPwPairChunk + (lane & 31) * 16 : ch32 * 16;
+  // Column values of step s (groups 2s and 2s + 1): the fp16 scales s_w and, for the
+  // corrections of 4-bit blocks, the zero points z.  Through LDS (4-block tiles) wave 2 of
+  // slice 1 loads the scales of the tile's blocks (lane l < 32: block l / 8, group
+  // l / 4 % 2, channels 8 (l % 4) .. + 8, from s4 or s8 through one descriptor over both
+  // sections) and wave 3 their zero points (lane l < 8: block l / 2, group l % 2, 32
+  // nibbles); other lanes, groups past the layer and blocks past it (or not 4-bit, for
+  // the zero points) read zeros.  Else each wave loads its own channel's values.
+  const uint8_t *s4b = reinterpret_cast<const uint8_t *>(p.s4);
+  const int64_t s8off = reinterpret_cast<const uint8_t *>(p.s8) - s4b;
+  const bool zrole = bi == 3;
+  const Rsrc rcol = !CWORDS ? make_rsrc(s4b, 0)
+                    : zrole ? make_rsrc(p.z4, (int64_t)p.nb4 * G * (int)kZ4Chunk)
+                            : make_rsrc(s4b, s8off + (int64_t)(p.nb - p.nb4) * G * 64);
+  int vcol = kOob, cgp = 0;  // DMA lane: offset of its chunk in group cgp (step 0), its group parity
+  if constexpr (CWORDS) {
+    const int tb = blk - bi + (zrole ? (lane >> 1) : (lane >> 3));  // the lane's block
+    cgp = zrole ? (lane & 1) : ((lane >> 2) & 1);
+    if (zrole ? (lane < 8 && tb < p.nb4) : (lane < 32 && tb < p.nb))
+      vcol = zrole ? (tb * G + cgp) * (int)kZ4Chunk
+                   : (int)((tb < p.nb4 ? (int64_t)tb * G * 64 : s8off + (int64_t)(tb - p.nb4) * G * 64) + cgp * 64 +
+                           (lane & 3) * 16);
+  }
+  const Rsrc rsw = make_rsrc((KIND == kW8 ? s4b + s8off + (size_t)bq * G * 64 : s4b + (size_t)blk * G * 64),
+                             NPW ? (int64_t)G * 64 : 0);
+  const Rsrc rzw = make_rsrc(p.z4 + (size_t)blk * G * kZ4Chunk, NPW == 2 ? (int64_t)G * kZ4Chunk : 0);
   const Rsrc rz = make_rsrc(p.z4 + (size_t)blk * G * kZ4Chunk, NZ ? (int64_t)G * kZ4Chunk : 0);
 
   // Per-lane offsets.
@@ -343,7 +378,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
 
   // Register ring (raw loaded bits): slot s % kSA holds step s.
   v4i bR[kSA][NW > 0 ? NW : 1];
-  v4i pwR[kSA];
+  uint32_t cR[kSA][2];  // column values (2-block tiles): s_w and z of group 2s + h (s_w of 2s + q without z)
   uint32_t zR[kSA];
 
   // Stage s % kSA: the activation tile and the row operands of step s.
@@ -355,17 +390,25 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
       bload16_lds(ra, smb + J * kAStage + q * kTileBM * 128 + (kDmaRows * bi + 8 * i) * 128, vdma[i], gl * 128);
     if constexpr (RDMA) bload16_lds(rro, smb + kRBase + J * kRStage + q * kTileBM * 32 + bi * 1024, vro, gl * p.M * 32);
     if constexpr (CWORDS)
-      bload16_lds(rpw, smb + kCBase + J * kCStage + cb0 * 512, vcw, min(s, npairs - 1) * (int)kPwPairChunk);
+      bload16_lds(rcol, smb + kCBase + J * kCStage + (zrole ? kCZero : 0),
+                  vcol != kOob && 2 * s + cgp < G ? vcol + 2 * s * (zrole ? (int)kZ4Chunk : 64) : kOob, 0);
   };
-  // Ring slot s % kSA: this wave's weights of step s (and in 2-block tiles the column
-  // words of its group pair).
+  // Ring slot s % kSA: this wave's weights of step s (and in 2-block tiles its column
+  // values; groups past the layer read zeros).
   auto issue_w = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
     if constexpr (HASW) {
       const int gl = min(kKS * s + q, G - 1);
 #pragma unroll
       for (int t = 0; t < NW; ++t) bR[J][t] = bload16(rw, vw[t], gl * kWChunk);
-      if constexpr (NPW) pwR[J] = bload16(rpw, vcw, min(s, npairs - 1) * (int)kPwPairChunk);
+      // (whole words: the lane's fp16 scale and zero-point byte are extracted when used;
+      // 2-byte and 1-byte loads measured slower)
+      if constexpr (NPW == 1) {
+        cR[J][0] = bload4(rsw, (ch32 >> 1) * 4, (2 * s + q) * 64);
+      } else if constexpr (NPW == 2) {
+        cR[J][0] = bload4(rsw, h * 64 + (ch32 >> 1) * 4, 2 * s * 64);
+        cR[J][1] = bload4(rzw, h * (int)kZ4Chunk + (ch32 >> 3) * 4, 2 * s * (int)kZ4Chunk);
+      }
       if constexpr (NZ) zR[J] = bload4(rz, (ch32 >> 3) * 4, gl * (int)kZ4Chunk);
     }
   };
@@ -449,6 +492,50 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
     }
   };
 
+  // Column operands of step s (stage / ring slot J), as exact bf16 pairs: s_w of this
+  // wave's group (2s + q) for the scale products (zero in the upper half-wave, whose row
+  // operand slots are unused), and for the corrections -z s_w of group 2s + h, the group
+  // whose row operands half-wave h reads (z s_w has at most 15 significant bits, so it is
+  // exact in fp32 too).  Each step forms the next step's, off its own critical path.
+  struct ColOps {
+    int sw, zw;
+  };
+  auto col_ops = [&](auto j_c) -> ColOps {
+    constexpr int J = decltype(j_c)::value;
+    uint32_t sq16, sh16 = 0, zh = 0;
+    if constexpr (CLDS) {
+      // (whole words, as for the loads below: the lane's half or byte is extracted)
+      const uint8_t *cst = smb + kCBase + J * kCStage;
+      auto word = [&](int off) { return *reinterpret_cast<const uint32_t *>(cst + off); };
+      sq16 = word(bi * 128 + q * 64 + (ch32 >> 1) * 4) >> ((ch32 & 1) * 16);
+      if constexpr (CORR) {
+        sh16 = word(bi * 128 + h * 64 + (ch32 >> 1) * 4) >> ((ch32 & 1) * 16);
+        zh = word(kCZero + (bi * 2 + h) * 16 + (ch32 >> 3) * 4) >> ((ch32 & 6) * 4);
+      }
+    } else if constexpr (CORR) {
+      // s_w of group 2s + q is what half-wave q loaded: swapping the halves of two copies
+      // leaves the lower half-wave's values in every lane of the first result and the
+      // upper half-wave's in the second.
+      sh16 = cR[J][0] >> ((ch32 & 1) * 16);
+      zh = cR[J][1] >> ((ch32 & 6) * 4);  // the byte of channels ch32 & ~1, ch32 | 1
+      const auto halves = __builtin_amdgcn_permlane32_swap(sh16, sh16, false, false);
+      sq16 = halves[q];
+    } else {
+      sq16 = cR[J][0] >> ((ch32 & 1) * 16);
+    }
+    // (computed in every lane and pinned there: a conditional computation would become a
+    // branch, which splits the step's schedule)
+    uint32_t swl = bf16_pair(h2f((uint16_t)sq16));
+    asm volatile("" : "+v"(swl));
+    ColOps c{h ? 0 : (int)swl, 0};
+    if constexpr (CORR) {
+      const float zf = (float)((zh >> ((ch32 & 1) * 4)) & 15u);
+      c.zw = (int)(bf16_pair(zf * h2f((uint16_t)sh16)) ^ 0x80008000u);
+    }
+    return c;
+  };
+  ColOps co{0, 0};  // this step's
+
   // One step s: stage J = s % kSA.  Entry: a0 and rs0 hold row block 0's operands of step
   // s (read during the previous step), P1 / sc1 the previous step's block 1.  The code is
   // written in issue order; the scheduler barriers between its pieces keep each MFMA
@@ -480,25 +567,9 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
       if (g < G) emit(1, Pb, g, zR[J]);
       return;
     }
-    // Column operands: s_w of this wave's group (2s + q) for the scale products (zero in
-    // the upper half-wave, whose row operand slots are unused), and for the corrections
-    // -z s_w of group 2s + h, the group whose row operands half-wave h reads.
-    v4i pq;
-    if constexpr (CLDS) {
-      pq = lds16(kCBase + J * kCStage + bi * 512 + ch32 * 16);
-    } else {
-      pq = pwR[J];
-      // (Every word of the load stays live to here: a register written by a load still in
-      // flight cannot be reused, and reusing one would force a wait for every load.)
-      asm volatile("" ::"v"(pq));
-    }
-    const int sw = h ? 0 : pq[2 * q];
-    const v4i bs = v4i{sw, sw, sw, sw};
+    const v4i bs = v4i{co.sw, co.sw, co.sw, co.sw};
     v4i bz;
-    if constexpr (CORR) {
-      const int zw = h ? pq[3] : pq[1];
-      bz = v4i{zw, zw, zw, zw};
-    }
+    if constexpr (CORR) bz = v4i{co.zw, co.zw, co.zw, co.zw};
     // First half: row block 0 on the matrix cores, row block 1 of the previous step folds
     // and this step's codes are decoded.
     sc0 = mfma_bf16(rs0, bs, v16f{0});
@@ -546,8 +617,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
       if (k == 3) rs0 = lds16(vrs + JN * kRStage);
       fence();
     }
+    const ColOps nxt = col_ops(IntC<JN>{});  // stage s + 1 was published at this step's barrier
     if constexpr (CORR && q == 1) acc1 = mfma_bf16(ru, bz, acc1);
     fence();
+    co = nxt;
   };
 
   // Prologue: the batches of the virtual steps -kSA .. -1 (stage t + kSA, then the weights
@@ -564,6 +637,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
   if constexpr (HASW) {
     load_a(IntC<0>{}, 0, a0);
     rs0 = lds16(vrs);
+    if constexpr (!PARTIALS) co = col_ops(IntC<0>{});
   }
   for (int it = 0; it < niter; ++it) {
     const int s = it * kSA;
@@ -1406,7 +1480,6 @@ void fill_args(GemmArgs &a, const int8_t *aq, const float *sa, const int32_t *as
   a.w8 = base + L.off_w8;
   a.s8 = (const uint16_t *)(base + L.off_s8);
   a.idx = (const int32_t *)(base + L.off_idx);
-  a.pw = (const uint32_t *)(base + L.off_pw);
   a.n4 = L.n4;
   a.nb = L.nb;
   a.nb4 = L.nb4;
@@ -1605,10 +1678,12 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
 }
 
 // The tile kernel addresses the row operands with 32-bit offsets (G * M * 32 bytes), a
-// block's weights and column words likewise, and an activation tile as 64 rows of K.
+// block's weights likewise, an activation tile as 64 rows of K, and the column scales of
+// every block from the start of s4 to the end of s8 (and the zero points) below kOob.
 bool tile_offsets_fit(int M, const mixllm_blob_info &L) {
+  const int64_t scales = (int64_t)(L.off_s8 - L.off_s4) + (int64_t)L.nb8 * L.G * 64;
   return (int64_t)L.G * M * 32 <= 0x7FFFFFFF && (int64_t)L.G * (int64_t)kW8Chunk <= 0x7FFFFFFF &&
-         (int64_t)pw_pairs(L.G) * (int64_t)kPwPairChunk <= 0x7FFFFFFF &&
+         scales + 2 * (int64_t)L.G * 64 <= kOob && (int64_t)L.nb4 * L.G * (int64_t)kZ4Chunk + 256 <= kOob &&
          (int64_t)kTileBM * L.K + (int64_t)L.G * 128 <= 0x7FFFFFFF;
 }
 

@@ -9,11 +9,6 @@
 //   s8   [nb8][G][32]  fp16 scales of the 8-bit blocks
 //   zp   [32][G]       zero points of the promoted 4-bit channels (unpacking only)
 //   idx  [nb * 32]     int32 original channel index of every packed channel (-1: empty)
-//   pw   [nb][P][32][4] column words of group pairs (P = ceil(G / 2) + 1): for
-//                      channel c of a block and pair j, s_w and -z * s_w of group 2j,
-//                      then of group 2j + 1, each as an exact sum of two bf16 values
-//                      (low half first); -z * s_w is zero for 8-bit, promoted and empty
-//                      channels; groups G and above (at least the whole last pair) are zero
 //
 // Packed channel order: the n4 4-bit channels (ascending original index), then the n8
 // 8-bit channels (ascending), then empty channels up to nb * 32 = 32 ceil(N / 32).
@@ -25,10 +20,9 @@
 // product for them either way, so every block has one kind, and the block count is
 // ceil(N / 32): no tile is spent on padding between the two subsets.
 //
-// The pw words feed the matrix-core products of the tile kernel directly: s_w (an fp16,
-// at most 11 significant bits) and z * s_w (at most 15) both split exactly into a bf16
-// holding the leading 8 significant bits plus a bf16 remainder.  One 16-byte load gives
-// a channel both groups of a pair, the pair a tile-kernel step covers.
+// The tile kernel's matrix-core scale products take s_w (an fp16, at most 11 significant
+// bits) and z * s_w (at most 15) as exact sums of two bf16 values, which it forms from
+// s4 / s8 and z4 as it reads them.
 //
 // Inside a 4-bit (block, group) chunk of 2048 B, 16-byte unit u = ((half * 4 + a) * 16 + ch)
 // holds channel 16 * half + ch, k-chunks a (bytes 0..7) and a + 4 (bytes 8..15) of the
@@ -61,10 +55,6 @@ constexpr size_t kW8Chunk = 4096;   // bytes per (block, group), 8-bit part
 constexpr size_t kS4Chunk = 64;     // 32 fp16 scales
 constexpr size_t kZ4Chunk = 16;     // 32 nibbles
 constexpr size_t kS8Chunk = 64;
-constexpr size_t kPwPairChunk = 32 * 4 * 4;  // bytes per (block, group pair) in pw
-
-// Group pairs of the pw section: ceil(G / 2) pairs of groups, then one all-zero pair.
-constexpr int pw_pairs(int G) { return (G + 1) / 2 + 1; }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -106,8 +96,6 @@ inline bool compute_layout(int32_t N, int32_t K, int32_t n8, mixllm_blob_info *L
   off = align256(off + (size_t)kBlock * G);
   L->off_idx = off;
   off = align256(off + (size_t)nb * kBlock * 4);
-  L->off_pw = off;
-  off = align256(off + (size_t)nb * (size_t)pw_pairs((int)G) * kPwPairChunk);
   L->total_bytes = off;
   return true;
 }

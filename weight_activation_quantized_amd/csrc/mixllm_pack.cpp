@@ -149,39 +149,6 @@ inline size_t w8_code_pos(int ch32, int k) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-uint32_t f32_bits(float f) {
-  uint32_t b;
-  memcpy(&b, &f, 4);
-  return b;
-}
-
-float bits_f32(uint32_t b) {
-  float f;
-  memcpy(&f, &b, 4);
-  return f;
-}
-
-// x = p0 + p1 exactly, both bf16 (x has at most 16 significant bits): p0 keeps the
-// leading 8 significant bits (truncation), p1 is the remainder.  Returns p0 | p1 << 16.
-uint32_t bf16_pair(float x) {
-  const uint32_t b0 = f32_bits(x) & 0xFFFF0000u;
-  const uint32_t b1 = f32_bits(x - bits_f32(b0));
-  return (b0 >> 16) | (b1 & 0xFFFF0000u);
-}
-
-// Column words of one channel and group: s_w and -z * s_w as bf16 pairs (both products
-// are exact in fp32).
-void scale_words(uint16_t s16, int z, uint32_t *out) {
-  const float s = f16_to_f32(s16);
-  out[0] = bf16_pair(s);
-  out[1] = bf16_pair((float)z * s) ^ 0x80008000u;  // negate both halves
-}
-
-// Where the column words of (block b, channel ch32, group g) start in the pw section.
-size_t pw_index(int64_t b, int ch32, int g, int G) {
-  return (((size_t)b * (size_t)mixllm::pw_pairs(G) + (size_t)(g / 2)) * 32 + (size_t)ch32) * 4 + (size_t)(g % 2) * 2;
-}
-
 }  // namespace
 
 extern "C" {
@@ -241,7 +208,6 @@ int mixllm_pack_weights(const uint16_t *w, int32_t N, int32_t K, int32_t group, 
   uint16_t *s8 = (uint16_t *)(base + L.off_s8);
   uint8_t *zp = base + L.off_zp;
   int32_t *idx = (int32_t *)(base + L.off_idx);
-  uint32_t *pw = (uint32_t *)(base + L.off_pw);
 
   for (int64_t j = 0; j < (int64_t)L.nb * kBlock; ++j) idx[j] = j < N ? perm[(size_t)j] : -1;
 
@@ -268,7 +234,6 @@ int mixllm_pack_weights(const uint16_t *w, int32_t N, int32_t K, int32_t group, 
         }
         s4[cidx * 32 + ch32] = s16;
         z4[cidx * 16 + ch32 / 2] |= (uint8_t)(z << ((ch32 & 1) ? 4 : 0));
-        scale_words(s16, z, pw + pw_index(b, ch32, g, G));
         continue;
       }
       const size_t cidx = (size_t)(b - L.nb4) * G + g;
@@ -284,7 +249,6 @@ int mixllm_pack_weights(const uint16_t *w, int32_t N, int32_t K, int32_t group, 
         for (int k = 0; k < kGroup; ++k) chunk[w8_code_pos(ch32, k)] = q8[k];
       }
       s8[cidx * 32 + ch32] = s16;
-      scale_words(s16, 0, pw + pw_index(b, ch32, g, G));  // z in the codes
     }
   }
   return MIXLLM_OK;

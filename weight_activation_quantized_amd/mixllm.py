@@ -55,7 +55,7 @@ class BlobInfo(ctypes.Structure):
                 ("n4_promoted", ctypes.c_int32),
                 ("off_w4", ctypes.c_uint64), ("off_s4", ctypes.c_uint64), ("off_z4", ctypes.c_uint64),
                 ("off_w8", ctypes.c_uint64), ("off_s8", ctypes.c_uint64), ("off_zp", ctypes.c_uint64),
-                ("off_idx", ctypes.c_uint64), ("off_pw", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
+                ("off_idx", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
