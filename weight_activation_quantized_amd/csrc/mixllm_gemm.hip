@@ -381,26 +381,37 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
   uint32_t cR[kSA][2];  // column values (2-block tiles): s_w and z of group 2s + h (s_w of 2s + q without z)
   uint32_t zR[kSA];
 
-  // Stage s % kSA: the activation tile and the row operands of step s.
-  auto issue_a = [&](auto j_c, int s) {
+  // Stage s % kSA: the activation tile and the row operands of step s, in two pieces (the
+  // first half of this wave's activation rows; the rest with the records and column values).
+  constexpr int NA = kDmaRows / 8;
+  auto issue_stage = [&](auto j_c, int s, int piece) {
     constexpr int J = decltype(j_c)::value;
     const int gl = min(kKS * s + q, G - 1);
 #pragma unroll
-    for (int i = 0; i < kDmaRows / 8; ++i)
+    for (int i = piece ? (NA + 1) / 2 : 0; i < (piece ? NA : (NA + 1) / 2); ++i)
       bload16_lds(ra, smb + J * kAStage + q * kTileBM * 128 + (kDmaRows * bi + 8 * i) * 128, vdma[i], gl * 128);
-    if constexpr (RDMA) bload16_lds(rro, smb + kRBase + J * kRStage + q * kTileBM * 32 + bi * 1024, vro, gl * p.M * 32);
-    if constexpr (CWORDS)
-      bload16_lds(rcol, smb + kCBase + J * kCStage + (zrole ? kCZero : 0),
-                  vcol != kOob && 2 * s + cgp < G ? vcol + 2 * s * (zrole ? (int)kZ4Chunk : 64) : kOob, 0);
+    if (piece) {
+      if constexpr (RDMA) bload16_lds(rro, smb + kRBase + J * kRStage + q * kTileBM * 32 + bi * 1024, vro, gl * p.M * 32);
+      if constexpr (CWORDS)
+        bload16_lds(rcol, smb + kCBase + J * kCStage + (zrole ? kCZero : 0),
+                    vcol != kOob && 2 * s + cgp < G ? vcol + 2 * s * (zrole ? (int)kZ4Chunk : 64) : kOob, 0);
+    }
+  };
+  auto issue_a = [&](auto j_c, int s) {
+    issue_stage(j_c, s, 0);
+    issue_stage(j_c, s, 1);
   };
   // Ring slot s % kSA: this wave's weights of step s (and in 2-block tiles its column
-  // values; groups past the layer read zeros).
-  auto issue_w = [&](auto j_c, int s) {
+  // values; groups past the layer read zeros), in two pieces (the first half of the
+  // weights; the rest with the column values and zero-point word).
+  auto issue_weights = [&](auto j_c, int s, int piece) {
     constexpr int J = decltype(j_c)::value;
     if constexpr (HASW) {
       const int gl = min(kKS * s + q, G - 1);
 #pragma unroll
-      for (int t = 0; t < NW; ++t) bR[J][t] = bload16(rw, vw[t], gl * kWChunk);
+      for (int t = piece ? (NW + 1) / 2 : 0; t < (piece ? NW : (NW + 1) / 2); ++t)
+        bR[J][t] = bload16(rw, vw[t], gl * kWChunk);
+      if (!piece) return;
       // (whole words: the lane's fp16 scale and zero-point byte are extracted when used;
       // 2-byte and 1-byte loads measured slower)
       if constexpr (NPW == 1) {
@@ -411,6 +422,10 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
       }
       if constexpr (NZ) zR[J] = bload4(rz, (ch32 >> 3) * 4, gl * (int)kZ4Chunk);
     }
+  };
+  auto issue_w = [&](auto j_c, int s) {
+    issue_weights(j_c, s, 0);
+    issue_weights(j_c, s, 1);
   };
 
   v16f acc0 = v16f{0}, acc1 = v16f{0};  // folded products of row blocks 0 and 1
@@ -603,15 +618,20 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
     fence();
     wait_vm<WAIT>();
     lds_barrier();  // stage s + 1 is published; stage s is free
-    issue_a(j_c, s + kSA);
-    issue_w(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1);
     fence();
-    // Second half: row block 1 on the matrix cores, row block 0 folds.
+    // Second half: row block 1 on the matrix cores, row block 0 folds, and this step's
+    // batch (stage s + kSA, then the weights of step s + kSA - 1) goes out one piece per
+    // matrix-core operation rather than all at once after the barrier (measured 2-6%
+    // faster: the workgroup's loads reach the memory path spread over the half-step).
     sc1 = mfma_bf16(rs1, bs, v16f{0});
     fence();
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       P1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[k], bw[k], k ? P1 : pinit, 0, 0, 0);
+      if (k < 2)
+        issue_stage(j_c, s + kSA, k);
+      else
+        issue_weights(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1, k - 2);
       fold4(acc0, P0, sc0, k);
       a0[k] = lds16(va[k] + JN * kAStage);
       if (k == 3) rs0 = lds16(vrs + JN * kRStage);
