@@ -6,8 +6,10 @@
   (scalar registers spill into lanes of vector registers, without memory, and are
   allowed);
 * in every main loop of the tile kernel the wait before each barrier allows exactly the
-  loads of the two steps issued since the stage it publishes, i.e. twice the loads the
-  loop issues per step: every load the waits count is one the code actually emits.
+  loads issued since the stage it publishes: with LD direct-to-LDS loads (the stages) and
+  LW register loads (the weights) per step, 2 LD + 3 LW where the weights go out a step
+  early (the folding waves), 2 (LD + LW) otherwise: every load the waits count is one the
+  code actually emits.
 """
 import os
 import re
@@ -59,8 +61,8 @@ def test_no_kernel_uses_scratch(asm):
 
 
 def _tile_loops(lines):
-    """(kernel, [(loads, wait before the barrier) per barrier segment], loads after the
-    last barrier) of each loop inside a tile kernel's body."""
+    """(kernel, loads per step as (direct-to-LDS, register) counts, [wait before each
+    barrier]) of each loop inside a tile kernel's body that has barriers."""
     cur, out = None, []
     for i, line in enumerate(lines):
         m = re.match(r"^(_ZN\S*gemm_tile_kernel\S*):", line)
@@ -69,29 +71,31 @@ def _tile_loops(lines):
         elif re.match(r"^_ZN\S*:", line) or line.startswith(".Lfunc_end"):
             cur = None
         if cur and "Loop Header" in line:
-            j, segs, loads, waits = i + 1, [], 0, []
+            j, nb, ld, lw, waits, last = i + 1, 0, 0, 0, [], None
             while not re.search(r"s_cbranch_scc[01] \.LBB", lines[j]):
                 t = lines[j].strip()
                 if t.startswith(("buffer_load", "global_load")):
-                    loads += 1
+                    if re.search(r"\blds\b", t):
+                        ld += 1
+                    else:
+                        lw += 1
                 m2 = re.search(r"vmcnt\((\d+)\)", t)
                 if m2:
-                    waits.append(int(m2.group(1)))
+                    last = int(m2.group(1))
                 if t.startswith("s_barrier"):
-                    segs.append((loads, waits[-1] if waits else None))
-                    loads = 0
+                    nb += 1
+                    waits.append(last)
                 j += 1
-            if segs:
-                out.append((cur, segs, loads))
+            if nb:
+                assert ld % nb == 0 and lw % nb == 0, (cur, ld, lw, nb)
+                out.append((cur, (ld // nb, lw // nb), waits))
     return out
 
 
 def test_tile_waits_match_the_loads(asm):
     loops = _tile_loops(asm)
     assert len(loops) >= 12
-    for name, segs, tail in loops:
-        # the loop is rotated: the loads after its last barrier belong to the first step
-        per_step = [tail] + [n for n, _ in segs[1:]]
-        waits = [w for _, w in segs]
-        assert len(set(per_step)) == 1 and per_step[0] > 0, (name, segs, tail)
-        assert waits == [2 * per_step[0]] * len(waits), (name, segs, tail)
+    for name, (ld, lw), waits in loops:
+        assert ld > 0, name
+        expect = 2 * ld + 3 * lw if lw and "Lb0" in name else 2 * (ld + lw)
+        assert waits == [expect] * len(waits), (name, ld, lw, waits)

@@ -310,11 +310,17 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
   constexpr int NPW = (!CLDS && !PARTIALS) ? (CORR ? 2 : 1) : 0;  // column-value loads into registers
   constexpr int LD = kDmaRows / 8 + (RDMA ? 1 : 0) + (CWORDS ? 1 : 0);  // direct-to-LDS loads per step
   constexpr int LW = HASW ? NW + NPW + NZ : 0;                    // register-ring loads per step
-  // Step s's batch (stage s + kSA, then weights s + kSA - 1) follows the barrier of step s.
-  // Before the barrier of step s, stage s + 1 must have landed: it came first in the batch
-  // of step s + 1 - kSA, and the weights of that batch were already waited for (decoded
-  // in this step's first half); the batches of the kSA - 2 steps since may be in flight.
-  constexpr int WAIT = (kSA - 2) * (LD + LW);
+  // Issue order.  A wave that folds (HASW, not partials) loads the weights of step
+  // t + kSA - 1 in the first half of step t (their ring slot is free once step t - 1 has
+  // decoded it) and stage t + kSA in the second half, after the barrier that frees it;
+  // the prologue keeps the same order (weights t before stage t + 1).  Before the barrier
+  // of step s, stage s + 1 must have landed; after it came the weights of steps s + 1 ..
+  // s + kSA - 1 and the stages s + 2 .. s + kSA - 1.  Other waves issue both parts of
+  // their batch after the barrier of step s (stage, then the weights of step s + kSA - 1):
+  // after stage s + 1 came its batch's weights, already waited for by the decode of this
+  // step, and the batches of the kSA - 2 steps since.
+  constexpr bool WEARLY = HASW && !PARTIALS;
+  constexpr int WAIT = WEARLY ? (kSA - 2) * LD + (kSA - 1) * LW : (kSA - 2) * (LD + LW);
   static_assert(WAIT < 64, "vmcnt range");
   const int ch32 = lane & 31, h = lane >> 5;
   const int G = p.G;
@@ -596,11 +602,13 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
     a1[0] = lds16(va[0] + J * kAStage + 32 * 128);
     fence();
     P0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[1], bw[1], P0, 0, 0, 0);
+    issue_weights(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1, 0);  // slot of step s - 1, decoded
     bw[2] = decode(j_c, 2);
     fold4(acc1, P1, sc1, 1);
     a1[1] = lds16(va[1] + J * kAStage + 32 * 128);
     fence();
     P0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[2], bw[2], P0, 0, 0, 0);
+    issue_weights(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1, 1);
     bw[3] = decode(j_c, 3);
     fold4(acc1, P1, sc1, 2);
     a1[2] = lds16(va[2] + J * kAStage + 32 * 128);
@@ -619,19 +627,16 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
     wait_vm<WAIT>();
     lds_barrier();  // stage s + 1 is published; stage s is free
     fence();
-    // Second half: row block 1 on the matrix cores, row block 0 folds, and this step's
-    // batch (stage s + kSA, then the weights of step s + kSA - 1) goes out one piece per
-    // matrix-core operation rather than all at once after the barrier (measured 2-6%
-    // faster: the workgroup's loads reach the memory path spread over the half-step).
+    // Second half: row block 1 on the matrix cores, row block 0 folds, and stage s + kSA
+    // goes out in two pieces between the matrix-core operations.  (Spreading the batch over
+    // the step rather than issuing it at once after the barrier measured 3-7% faster: the
+    // workgroup's loads reach the memory path spread out.)
     sc1 = mfma_bf16(rs1, bs, v16f{0});
     fence();
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       P1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[k], bw[k], k ? P1 : pinit, 0, 0, 0);
-      if (k < 2)
-        issue_stage(j_c, s + kSA, k);
-      else
-        issue_weights(IntC<(J + kSA - 1) % kSA>{}, s + kSA - 1, k - 2);
+      if (k == 0 || k == 2) issue_stage(j_c, s + kSA, k >> 1);
       fold4(acc0, P0, sc0, k);
       a0[k] = lds16(va[k] + JN * kAStage);
       if (k == 3) rs0 = lds16(vrs + JN * kRStage);
@@ -643,14 +648,19 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
     co = nxt;
   };
 
-  // Prologue: the batches of the virtual steps -kSA .. -1 (stage t + kSA, then the weights
-  // of step t + kSA - 1, none for step -1), then stage 0 is published and row block 0's
-  // operands of step 0 are read.  Every load counted by the waits is one the code uses:
+  // Prologue: stages 0 .. kSA - 1 and the weights of steps 0 .. kSA - 2 in the loop's
+  // order (see WAIT), then stage 0 is published and row block 0's operands of step 0 are
+  // read.  Every load counted by the waits is one the code uses:
   // a load whose result is never read would be deleted by the compiler and break the count.
   static_for<0, kSA>([&](auto t_c) {
     constexpr int T = decltype(t_c)::value;  // virtual step T - kSA
-    issue_a(IntC<T>{}, T);
-    if constexpr (T > 0) issue_w(IntC<T - 1>{}, T - 1);
+    if constexpr (WEARLY) {
+      issue_a(IntC<T>{}, T);
+      if constexpr (T < kSA - 1) issue_w(IntC<T>{}, T);
+    } else {
+      issue_a(IntC<T>{}, T);
+      if constexpr (T > 0) issue_w(IntC<T - 1>{}, T - 1);
+    }
   });
   wait_vm<(kSA - 1) * (LD + LW)>();
   lds_barrier();
