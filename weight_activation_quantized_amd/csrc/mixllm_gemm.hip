@@ -792,9 +792,10 @@ __global__ __launch_bounds__(tile_threads(NB)) __attribute__((amdgpu_waves_per_e
     tile_dispatch<NB, PARTIALS, 1>(p, sm, m0, blk, bi, lane, kind);
 }
 // ------------------------------------------------------------------------------------
-// Skinny kernel (small M): one workgroup per 16-channel half block; its KS waves split
-// the groups into contiguous ranges, each wave computes all M <= 16 RB rows for its
-// groups with v_mfma_i32_16x16x64_i8, and the partial sums are reduced through LDS.
+// Skinny kernel (small M): one workgroup per 16-channel half block; its KS waves share
+// the groups (wave w takes groups w, w + KS, w + 2 KS, ...), each wave computes all
+// M <= 16 RB rows for its groups with v_mfma_i32_16x16x64_i8, and the partial sums are
+// reduced through LDS.
 // The kernel is bound by the weight stream from HBM: every wave keeps the loads of the
 // next D - 1 groups in flight (a register ring, unrolled so the slot indices are
 // constants; the compiler places the waits), then finishes the last cnt % D groups in an
@@ -805,6 +806,12 @@ __global__ __launch_bounds__(tile_threads(NB)) __attribute__((amdgpu_waves_per_e
 // scalar offset added (the host checks M * K and G * M * 4 stay below it).
 constexpr int kSkinnyOob = 0x7FFFFF00;
 
+// The groups of wave `wave` among `ks` sharing G: wave, wave + ks, ... (interleaved, so
+// the workgroup reads a block's group chunks in address order, ks chunks at a time:
+// measured 2-14% faster on the Llama-3.1 8B and 70B layers at one to 32 tokens than
+// contiguous ranges per wave, whose concurrent streams sit G / ks chunks apart).
+__device__ __forceinline__ int wave_groups(int G, int wave, int ks) { return (G - wave + ks - 1) / ks; }
+
 // Ring depths (measured on the Llama-3.1 8B and 70B layers): weights 8 groups for one
 // 16-row block of 4-bit codes, else 4; activations 8 for one block, 4 for two, 2 for three
 // or four (deeper rings spill there).
@@ -812,8 +819,8 @@ constexpr int skinny_wring(int rb, int kind) { return rb == 1 && kind == kW4 ? 8
 constexpr int skinny_aring(int rb) { return rb == 1 ? 8 : (rb == 2 ? 4 : 2); }
 
 template <int RB, int KIND, bool PARTIALS>
-__device__ __forceinline__ void skinny_body(const GemmArgs &p, int blk, int half, int lane, int g0, int cnt,
-                                            float (&acc)[RB][4]) {
+__device__ __forceinline__ void skinny_body(const GemmArgs &p, int blk, int half, int lane, int g0, int gstep,
+                                            int cnt, float (&acc)[RB][4]) {
   constexpr int DW = skinny_wring(RB, KIND);         // weight ring: loads DW - 1 groups ahead
   constexpr int DA = skinny_aring(RB) < DW ? skinny_aring(RB) : DW;  // activation ring: DA - 1 ahead
   constexpr int NWL = KIND == kW8 ? 2 : 1;           // 16-byte weight loads per group
@@ -843,7 +850,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs &p, int blk, int half
   v4i wR[DW][NWL];
   uint32_t zR[DW], sR[DW];
   v4i aR[DA][RB][2], saR[DA][RB];
-  auto grp = [&](int s) { return g0 + min(s, cnt - 1); };
+  auto grp = [&](int s) { return g0 + min(s, cnt - 1) * gstep; };
   // The activation loads of step s go first in a step's batch: waiting for them then
   // leaves the deeper weight loads issued after them in flight.
   auto issue_a = [&](auto j_c, int s) {
@@ -939,18 +946,18 @@ __global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(
   const int sub = blockIdx.x;
   const int blk = sub >> 1, half = sub & 1;
   const int G = p.G;
-  const int g0 = (int)((int64_t)G * wave / ks), g1 = (int)((int64_t)G * (wave + 1) / ks);
+  const int cnt = wave_groups(G, wave, ks);
 
   float acc[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[rb][r] = 0.0f;
-  if (g1 > g0) {
+  if (cnt > 0) {
     if (blk < p.nb4)
-      skinny_body<RB, kW4, PARTIALS>(p, blk, half, lane, g0, g1 - g0, acc);
+      skinny_body<RB, kW4, PARTIALS>(p, blk, half, lane, wave, ks, cnt, acc);
     else
-      skinny_body<RB, kW8, PARTIALS>(p, blk, half, lane, g0, g1 - g0, acc);
+      skinny_body<RB, kW8, PARTIALS>(p, blk, half, lane, wave, ks, cnt, acc);
   }
   if (PARTIALS) return;
 
@@ -977,8 +984,8 @@ __global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(
 // through scalar loads into SGPRs.  A 4-bit wave owns two blocks (64 channels, one per
 // lane; the 64 bytes are the channel's 128 codes); an 8-bit wave owns one block, lanes c
 // and c + 32 holding the first and second 64 inputs of channel c.  The zero point enters
-// as - z * S_A.  A workgroup's waves split the groups into contiguous ranges and reduce
-// through LDS in a fixed order.  The vector memory path carries only weights and their
+// as - z * S_A.  A workgroup's waves share the groups (wave w takes every ks-th, from w)
+// and reduce through LDS in a fixed order.  The vector memory path carries only weights and their
 // scale and zero-point words, so the kernel is bound by the weight stream.
 // ------------------------------------------------------------------------------------
 constexpr int kGvWaves = 16;  // waves per workgroup at most
@@ -1005,7 +1012,7 @@ typedef const __attribute__((address_space(4))) int32_t *ConstI;
 // two-slot SGPR ring in (group, row) order, one item ahead.
 template <int KIND, int MT, bool PARTIALS, bool SPLIT>
 __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
-                                          int cnt, float (&acc)[MT]) {
+                                          int gstep, int cnt, float (&acc)[MT]) {
   constexpr int D = kGvRing;
   constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
   const int c = lane & 31, half = c >> 4, ch = c & 15, kh = lane >> 5;
@@ -1031,7 +1038,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
   v16i aR[2][2];
   float saR[2];
   int asR[2];
-  auto grp = [&](int s) { return g0 + min(s, cnt - 1); };
+  auto grp = [&](int s) { return g0 + min(s, cnt - 1) * gstep; };
   // Item (s, m): row m's operands of step s's group into slot Q.
   auto issue_a = [&](auto q_c, int s, int m) {
     constexpr int Q = decltype(q_c)::value;
@@ -1178,18 +1185,17 @@ __global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const 
   const int second = w4 && !split && !dup ? (lane >> 5) : 0;
   const int G = p.G;
   // (wave-uniform; read back into scalar registers for the loads' scalar offsets)
-  const int g0 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * wave / ks));
-  const int g1 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * (wave + 1) / ks));
+  const int cnt = wave_groups(G, wave, ks);
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-  if (g1 > g0) {
+  if (cnt > 0) {
     if (w4 && split)
-      gemv_body<kW4, MT, PARTIALS, true>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
+      gemv_body<kW4, MT, PARTIALS, true>(p, blk0, 0, false, lane, wave, ks, cnt, acc);
     else if (w4)
-      gemv_body<kW4, MT, PARTIALS, false>(p, blk0, second, dup, lane, g0, g1 - g0, acc);
+      gemv_body<kW4, MT, PARTIALS, false>(p, blk0, second, dup, lane, wave, ks, cnt, acc);
     else
-      gemv_body<kW8, MT, PARTIALS, false>(p, blk0, 0, false, lane, g0, g1 - g0, acc);
+      gemv_body<kW8, MT, PARTIALS, false>(p, blk0, 0, false, lane, wave, ks, cnt, acc);
   }
   if (PARTIALS) return;
 #pragma unroll
@@ -1219,7 +1225,8 @@ __global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const 
 // and the zero point enters as - z * S_A on the exact integer partial.  Weights pass
 // through a register ring and the activation codes, s_a and S_A through an LDS ring (its
 // own stages per wave, filled by direct-to-LDS loads), 3 (two row blocks: 2) groups
-// ahead; the workgroup's waves split the groups and reduce through LDS in a fixed order.
+// ahead; the workgroup's waves share the groups (wave w takes every ks-th, from w) and
+// reduce through LDS in a fixed order.
 // ------------------------------------------------------------------------------------
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kStWaves = 8;  // waves per workgroup at most
@@ -1245,7 +1252,7 @@ __device__ __forceinline__ void bload4_lds(Rsrc r, void *dst, int voff, int soff
 // block blk0.  `lds` is this wave's ring of st_ring(RB) stages.
 template <int KIND, int SB, int RB, bool PARTIALS>
 __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
-                                           int cnt, uint8_t *lds, float (&acc)[4][RB][4]) {
+                                           int gstep, int cnt, uint8_t *lds, float (&acc)[4][RB][4]) {
   constexpr int NT = (KIND == kW8 || SB == 1) ? 2 : 4;
   constexpr int D = st_ring(RB);
   constexpr int kStage = st_stage(RB);
@@ -1291,7 +1298,7 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
 
   v4i wR[D][NT][KIND == kW8 ? 2 : 1];
   uint32_t sR[D][NT], zR[D][NT];
-  auto grp = [&](int s) { return g0 + min(s, cnt - 1); };
+  auto grp = [&](int s) { return g0 + min(s, cnt - 1) * gstep; };
   auto issue_a = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
     const int g = grp(s);
@@ -1425,8 +1432,7 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
   const int second = SB == 2 && w4 && !dup ? 1 : 0;
   const int G = p.G;
   // (wave-uniform; read back into scalar registers for the loads' scalar offsets)
-  const int g0 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * wave / ks));
-  const int g1 = __builtin_amdgcn_readfirstlane((int)((int64_t)G * (wave + 1) / ks));
+  const int cnt = wave_groups(G, wave, ks);
   uint8_t *lds = smem + wave * st_ring(RB) * st_stage(RB);
   float acc[4][RB][4];
 #pragma unroll
@@ -1435,11 +1441,11 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[t][rb][r] = 0.0f;
-  if (g1 > g0) {
+  if (cnt > 0) {
     if (w4)
-      strip_body<kW4, SB, RB, PARTIALS>(p, blk0, second, dup, lane, g0, g1 - g0, lds, acc);
+      strip_body<kW4, SB, RB, PARTIALS>(p, blk0, second, dup, lane, wave, ks, cnt, lds, acc);
     else
-      strip_body<kW8, SB, RB, PARTIALS>(p, blk0, 0, false, lane, g0, g1 - g0, lds, acc);
+      strip_body<kW8, SB, RB, PARTIALS>(p, blk0, 0, false, lane, wave, ks, cnt, lds, acc);
   }
   if (PARTIALS) return;
   __syncthreads();  // every wave's stages are done; the space becomes the reduction area
@@ -1613,6 +1619,14 @@ int gemv_waves_per_simd() {
   return cached;
 }
 
+// Waves per workgroup at most for one token: 6 with one-block strips, 8 with block pairs.
+// A single row gives a wave little arithmetic per weight byte, so few waves keep the
+// weight stream going, and more of them only queue more requests: measured on the
+// Llama-3.1 70B layers at M = 1, the o, down and q/k/v projections took 10.6, 28.1 and
+// 13.7 us with the counts the cost alone picks (16, 16, 13) against 9.1, 24.6 and 12.5
+// with 6; the gate (block pairs) 23.5 with 13 against 22.7 with 8.
+int gv_one_row_waves(int sb) { return sb == 1 ? 6 : 8; }
+
 int gemv_waves_per_simd_m(int m) {
   static_assert(kGvMaxRows == 3, "one case per row count");
   switch (m) {
@@ -1622,8 +1636,8 @@ int gemv_waves_per_simd_m(int m) {
   }
 }
 
-// Waves per workgroup for a grid of nwg workgroups whose waves split G groups into
-// contiguous ranges: the count that minimizes (rounds of workgroups) x (groups per wave),
+// Waves per workgroup for a grid of nwg workgroups whose waves share G groups: the
+// count that minimizes (rounds of workgroups) x (groups per wave),
 // a CU holding floor(wpc / k) workgroups of k waves (wpc: waves per CU the kernel's
 // registers allow), and at most wg_cap (its LDS).  Ties keep the smaller count (fewer
 // rounds, longer loops).
@@ -1671,7 +1685,8 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
     pl.sb = nstrip < cus ? 1 : 2;
     pl.nstrip4 = pl.sb == 2 ? nstrip4 : L.nb4;
     pl.nstrip = pl.nstrip4 + L.nb8;
-    pl.ks = pick_waves(pl.nstrip, L.G, 4 * gemv_waves_per_simd_m(M), gv_max_waves(M), cus);
+    pl.ks = pick_waves(pl.nstrip, L.G, 4 * gemv_waves_per_simd_m(M), M == 1 ? gv_one_row_waves(pl.sb) : gv_max_waves(M),
+                       cus);
     return pl;
   }
   // Up to 32 tokens on layers with a strip (one workgroup) for at least 3/4 of the CUs:
