@@ -245,6 +245,11 @@ __device__ __forceinline__ Rsrc make_rsrc(const void *base, int64_t bytes) {
 __device__ __forceinline__ v4i bload16(Rsrc r, int voff, int soff) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// With the cache-policy bit nt (non-temporal), for weights that a kernel reads once.
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ v4i bload16_nt(Rsrc r, int voff, int soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal));
+}
 __device__ __forceinline__ uint32_t bload4(Rsrc r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
@@ -868,7 +873,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs &p, int blk, int half
     constexpr int J = decltype(j_c)::value;
     const int g = grp(s);
 #pragma unroll
-    for (int t = 0; t < NWL; ++t) wR[J][t] = bload16(rw, vw + t * 1024, g * kWChunk);
+    for (int t = 0; t < NWL; ++t) wR[J][t] = bload16_nt(rw, vw + t * 1024, g * kWChunk);
     sR[J] = bload4(rs, (ch32 >> 1) * 4, g * 64);
     if constexpr (KIND == kW4) zR[J] = bload4(rz, (ch32 >> 3) * 4, g * (int)kZ4Chunk);
   };
@@ -990,7 +995,6 @@ __global__ __launch_bounds__(64 * skinny_max_waves(RB)) void gemm_skinny_kernel(
 // ------------------------------------------------------------------------------------
 constexpr int kGvWaves = 16;  // waves per workgroup at most
 constexpr int kGvRing = 2;    // weight ring: loads one group ahead (deeper rings measured slower)
-constexpr int kNonTemporal = 2;  // cache-policy bit nt: the weights are read once
 constexpr int kGvMaxRows = 3;  // tokens the gemv kernel takes
 #ifndef MIXLLM_GV_WAVES_PER_SIMD
 #define MIXLLM_GV_WAVES_PER_SIMD 7
@@ -1054,7 +1058,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &p, int blk0, int secon
     const int g = grp(s);
 #pragma unroll
     for (int t = 0; t < NWL; ++t)
-      wR[J][t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, vw + t * 256, g * kWChunk, kNonTemporal));
+      wR[J][t] = bload16_nt(rw, vw + t * 256, g * kWChunk);
     sR[J] = bload4(rs, vs, g * 64);
     if constexpr (KIND == kW4) zR[J] = bload4(rz, vz, g * (int)kZ4Chunk);
   };
@@ -1317,9 +1321,9 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
       if constexpr (KIND == kW8) {
 #pragma unroll
         for (int mf = 0; mf < 2; ++mf)
-          wR[J][t][mf] = bload16(rw, ht(t) * 2048 + mf * 1024 + lane * 16, g * kWChunk);
+          wR[J][t][mf] = bload16_nt(rw, ht(t) * 2048 + mf * 1024 + lane * 16, g * kWChunk);
       } else {
-        wR[J][t][0] = bload16(rw, bo(t) * G * kWChunk + ht(t) * 1024 + lane * 16, g * kWChunk);
+        wR[J][t][0] = bload16_nt(rw, bo(t) * G * kWChunk + ht(t) * 1024 + lane * 16, g * kWChunk);
         zR[J][t] = bload4(rz, bo(t) * G * (int)kZ4Chunk + (cw >> 3) * 4, g * (int)kZ4Chunk);
       }
       sR[J][t] = bload4(rs, bo(t) * G * 64 + (cw >> 1) * 4, g * 64);
