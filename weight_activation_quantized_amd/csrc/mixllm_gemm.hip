@@ -298,7 +298,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 // RDMA: this wave also loads 32 rows of the row operand records per step; CDMA: it also
 // loads the column scales (wave 2) or zero points (wave 3) of the tile's four blocks.
-template <int NB, int KIND, bool PARTIALS, bool RDMA, bool CDMA, int Q>
+template <int NB, int KIND, bool PARTIALS, bool RDMA, bool CDMA, int Q, bool WNT>
 __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, int m0, int blk, int bi, int lane) {
   constexpr int q = Q;  // group slice
   constexpr bool HASW = KIND != kNone;
@@ -421,7 +421,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
       const int gl = min(kKS * s + q, G - 1);
 #pragma unroll
       for (int t = piece ? (NW + 1) / 2 : 0; t < (piece ? NW : (NW + 1) / 2); ++t)
-        bR[J][t] = bload16(rw, vw[t], gl * kWChunk);
+        bR[J][t] = WNT ? bload16_nt(rw, vw[t], gl * kWChunk) : bload16(rw, vw[t], gl * kWChunk);
       if (!piece) return;
       // (whole words: the lane's fp16 scale and zero-point byte are extracted when used;
       // 2-byte and 1-byte loads measured slower)
@@ -737,33 +737,42 @@ __device__ __forceinline__ void tile_body(const GemmArgs &p, TileSmem<NB> &sm, i
 // The body for one wave: its block kind, which shared loads it issues, its slice.  Waves
 // 0 and 1 of each slice load the row operand records (32 rows each); in 4-block tiles the
 // column words go to waves 2 and 3 of slice 1.
-template <int NB, bool PARTIALS, int Q, bool RDMA, bool CDMA>
+template <int NB, bool PARTIALS, int Q, bool RDMA, bool CDMA, bool WNT>
 __device__ __forceinline__ void tile_kind(const GemmArgs &p, TileSmem<NB> &sm, int m0, int blk, int bi, int lane,
                                           int kind) {
   switch (kind) {
-    case kW4: tile_body<NB, kW4, PARTIALS, RDMA, CDMA, Q>(p, sm, m0, blk, bi, lane); break;
-    case kW8: tile_body<NB, kW8, PARTIALS, RDMA, CDMA, Q>(p, sm, m0, blk, bi, lane); break;
-    default: tile_body<NB, kNone, PARTIALS, RDMA, CDMA, Q>(p, sm, m0, blk, bi, lane); break;
+    case kW4: tile_body<NB, kW4, PARTIALS, RDMA, CDMA, Q, WNT>(p, sm, m0, blk, bi, lane); break;
+    case kW8: tile_body<NB, kW8, PARTIALS, RDMA, CDMA, Q, WNT>(p, sm, m0, blk, bi, lane); break;
+    default: tile_body<NB, kNone, PARTIALS, RDMA, CDMA, Q, WNT>(p, sm, m0, blk, bi, lane); break;
   }
 }
 
-template <int NB, bool PARTIALS, int Q>
+template <int NB, bool PARTIALS, int Q, bool WNT>
 __device__ __forceinline__ void tile_dispatch(const GemmArgs &p, TileSmem<NB> &sm, int m0, int blk, int bi,
                                               int lane, int kind) {
   if constexpr (NB != kTileNB) {
-    tile_kind<NB, PARTIALS, Q, true, false>(p, sm, m0, blk, bi, lane, kind);
+    tile_kind<NB, PARTIALS, Q, true, false, WNT>(p, sm, m0, blk, bi, lane, kind);
   } else {
     if (bi < 2)
-      tile_kind<NB, PARTIALS, Q, true, false>(p, sm, m0, blk, bi, lane, kind);
+      tile_kind<NB, PARTIALS, Q, true, false, WNT>(p, sm, m0, blk, bi, lane, kind);
     else if (Q == 1)
-      tile_kind<NB, PARTIALS, Q, false, true>(p, sm, m0, blk, bi, lane, kind);
+      tile_kind<NB, PARTIALS, Q, false, true, WNT>(p, sm, m0, blk, bi, lane, kind);
     else
-      tile_kind<NB, PARTIALS, Q, false, false>(p, sm, m0, blk, bi, lane, kind);
+      tile_kind<NB, PARTIALS, Q, false, false, WNT>(p, sm, m0, blk, bi, lane, kind);
   }
 }
 
+// Workgroup w runs on XCD w % 8.  The tiles go to the XCDs in contiguous ranges, ordered
+// in bands of kTileBand M tiles (M tile fastest within a band), so the workgroups an XCD
+// runs at once share both activation rows and weight blocks in its L2.
+constexpr int kTileBand = 4;
+
 // NB: channel blocks per workgroup (4; 2 on layers too narrow to fill the CUs with 4).
-template <int NB, bool PARTIALS>
+// WNT: the weights load with the non-temporal policy, for grids of one band, whose
+// workgroups reading a weight block all run at once (with more bands a later band reads
+// it again from L2: measured 7% slower with the policy at M = 512 and 2048, and 2-5% faster
+// at M = 64-256).
+template <int NB, bool PARTIALS, bool WNT>
 __global__ __launch_bounds__(tile_threads(NB)) __attribute__((amdgpu_waves_per_eu(2))) void gemm_tile_kernel(
     const GemmArgs p) {
   __shared__ __attribute__((aligned(16))) TileSmem<NB> sm;
@@ -771,17 +780,13 @@ __global__ __launch_bounds__(tile_threads(NB)) __attribute__((amdgpu_waves_per_e
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave: uniform
   const int bi = wave % NB, q = wave / NB;
 
-  // Workgroup w runs on XCD w % 8.  Give each XCD a contiguous range of tiles, ordered in
-  // bands of kBandM M tiles (M tile fastest within a band), so the workgroups an XCD runs
-  // at once share both activation rows and weight blocks in its L2.
-  constexpr int kBandM = 4;
   const int T = p.tiles_m * p.tiles_n;
   const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
   const int per = T >> 3, rem = T & 7;
   const int t = xcd * per + (xcd < rem ? xcd : rem) + i;
-  const int band = t / (kBandM * p.tiles_n), in_band = t - band * (kBandM * p.tiles_n);
-  const int bm = min(kBandM, p.tiles_m - band * kBandM);  // M tiles in this band
-  const int tm = band * kBandM + in_band % bm, tr = in_band / bm;
+  const int band = t / (kTileBand * p.tiles_n), in_band = t - band * (kTileBand * p.tiles_n);
+  const int bm = min(kTileBand, p.tiles_m - band * kTileBand);  // M tiles in this band
+  const int tm = band * kTileBand + in_band % bm, tr = in_band / bm;
   // When the whole grid runs at once, N tiles go in a stride-8 order so that the XCDs
   // sharing a band each get some of the 8-bit blocks (the last N tiles) instead of one
   // XCD getting all of them; in longer grids the contiguous order streams the weights
@@ -792,9 +797,9 @@ __global__ __launch_bounds__(tile_threads(NB)) __attribute__((amdgpu_waves_per_e
   const int kind = blk >= p.nb ? kNone : (blk < p.nb4 ? kW4 : kW8);
   // Waves 0 and 1 of each slice also load the row operand records (32 rows each).
   if (q == 0)
-    tile_dispatch<NB, PARTIALS, 0>(p, sm, m0, blk, bi, lane, kind);
+    tile_dispatch<NB, PARTIALS, 0, WNT>(p, sm, m0, blk, bi, lane, kind);
   else
-    tile_dispatch<NB, PARTIALS, 1>(p, sm, m0, blk, bi, lane, kind);
+    tile_dispatch<NB, PARTIALS, 1, WNT>(p, sm, m0, blk, bi, lane, kind);
 }
 // ------------------------------------------------------------------------------------
 // Skinny kernel (small M): one workgroup per 16-channel half block; its KS waves share
@@ -1792,10 +1797,17 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
     const int64_t T = (int64_t)a.tiles_m * a.tiles_n;
     if (T > 0x7FFFFFFF) return MIXLLM_E_SHAPE;
     a.spread = T <= device_cus() ? 1 : 0;
-    if (pl.nbt == 2)
-      hipLaunchKernelGGL((gemm_tile_kernel<2, PARTIALS>), dim3((unsigned)T), dim3(tile_threads(2)), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_tile_kernel<4, PARTIALS>), dim3((unsigned)T), dim3(tile_threads(4)), 0, stream, a);
+    const dim3 grid((unsigned)T);
+    if (!PARTIALS && a.tiles_m <= kTileBand) {
+      if (pl.nbt == 2)
+        hipLaunchKernelGGL((gemm_tile_kernel<2, PARTIALS, !PARTIALS>), grid, dim3(tile_threads(2)), 0, stream, a);
+      else
+        hipLaunchKernelGGL((gemm_tile_kernel<4, PARTIALS, !PARTIALS>), grid, dim3(tile_threads(4)), 0, stream, a);
+    } else if (pl.nbt == 2) {
+      hipLaunchKernelGGL((gemm_tile_kernel<2, PARTIALS, false>), grid, dim3(tile_threads(2)), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((gemm_tile_kernel<4, PARTIALS, false>), grid, dim3(tile_threads(4)), 0, stream, a);
+    }
   }
   return hipGetLastError() == hipSuccess ? MIXLLM_OK : MIXLLM_E_HIP;
 }
