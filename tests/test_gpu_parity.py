@@ -111,6 +111,12 @@ SMALL = [
     # M = 1 .. 3 on a layer with fewer 4-bit block pairs than CUs (on 256 CUs): one 4-bit
     # block per strip, the group's inputs split over the half-waves; an odd block count
     (1, 8192, 2688, 820), (2, 8192, 1152, 820), (3, 8192, 896, 820),
+    # the one-lane-per-channel kernel with one-block strips on the headline's width and a
+    # ragged last block (4100); the strip kernel with one-block strips whose 8-bit blocks
+    # go in 16-channel halves (every strip fits a CU), one and two row blocks, and a last
+    # 8-bit block whose second half holds no channel (6150 = 192 * 32 + 6)
+    (1, 4096, 640, 410), (2, 4096, 256, 410), (3, 4100, 384, 411),
+    (8, 6150, 1280, 615), (13, 6400, 1152, 640), (24, 6400, 640, 650),
 ]
 
 

@@ -1258,11 +1258,14 @@ __device__ __forceinline__ void bload4_lds(Rsrc r, void *dst, int voff, int soff
 
 // NT column tiles: with SB = 2, 4-bit strips hold blocks blk0 and blk0 + second (tiles 2
 // and 3 repeat tiles 0 and 1 when the strip has one block: dup); otherwise a strip is
-// block blk0.  `lds` is this wave's ring of st_ring(RB) stages.
-template <int KIND, int SB, int RB, bool PARTIALS>
-__device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int second, bool dup, int lane, int g0,
-                                           int gstep, int cnt, uint8_t *lds, float (&acc)[4][RB][4]) {
-  constexpr int NT = (KIND == kW8 || SB == 1) ? 2 : 4;
+// block blk0, or for 8-bit strips with SB = 1 its 16-channel half `half`.  `lds` is this
+// wave's ring of st_ring(RB) stages.
+template <int KIND, int SB, int RB, bool PARTIALS, bool H8 = false>
+__device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int second, bool dup, int half, int lane,
+                                           int g0, int gstep, int cnt, uint8_t *lds, float (&acc)[4][RB][4]) {
+  // Column tiles: 4 (two 4-bit blocks), 2 (one 4-bit block, or one 8-bit block), or 1 (H8:
+  // the 16-channel half `half` of an 8-bit block).
+  constexpr int NT = KIND == kW8 ? (H8 ? 1 : 2) : (SB == 1 ? 2 : 4);
   constexpr int D = st_ring(RB);
   constexpr int kStage = st_stage(RB);
   constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
@@ -1286,8 +1289,8 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
   const Rsrc rsa = make_rsrc(p.sa, (int64_t)G * M * 4);
   const Rsrc ras = make_rsrc(p.asum, KIND == kW4 ? (int64_t)G * M * 4 : 0);
   // Column tile t: block offset bo(t) (in blocks from blk0) and half ht(t) of it.
-  auto bo = [&](int t) { return NT == 2 ? 0 : (t >> 1) * second; };
-  auto ht = [&](int t) { return NT == 2 ? t : (t & 1); };
+  auto bo = [&](int t) { return NT == 4 ? (t >> 1) * second : 0; };
+  auto ht = [&](int t) { return NT == 1 ? half : (t & 1); };
   // Direct-to-LDS offsets: load i of a stage fills rows 8i .. 8i + 7 (lane l: row
   // 8i + l / 8, position l % 8, which holds chunk (l % 8) ^ (row & 7)); the scale loads
   // fill row l's word.  Rows past M load from past every descriptor (zeros, no traffic).
@@ -1428,15 +1431,21 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
 // SB: 4-bit blocks per strip (2 on wide layers; 1 doubles the strips of narrower ones).
 // RB: 16-row blocks.
 template <int SB, int RB, bool PARTIALS>
-__global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArgs p, int ks, int nstrip4) {
+__global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArgs p, int ks, int nstrip4,
+                                                                   int halves8) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[st_lds(RB)];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int strip = blockIdx.x;
   // Strips [0, nstrip4) hold SB 4-bit blocks each (with SB = 2 an odd count leaves the
-  // last strip one block, repeated in tiles 2 and 3); the others one 8-bit block each.
+  // last strip one block, repeated in tiles 2 and 3); the others one 8-bit block each, or
+  // with `halves8` (SB = 1) one 16-channel half of an 8-bit block, so that every strip
+  // streams 16 bytes of weights per input, as a one-block 4-bit strip does.
   const bool w4 = strip < nstrip4;
-  const int blk0 = w4 ? SB * strip : p.nb4 + (strip - nstrip4);
+  const bool h8 = SB == 1 && halves8 && !w4;
+  const int s8 = strip - nstrip4;
+  const int half = h8 ? (s8 & 1) : 0;
+  const int blk0 = w4 ? SB * strip : p.nb4 + (h8 ? (s8 >> 1) : s8);
   const bool dup = SB == 2 && w4 && p.nb4 - blk0 < 2;
   const int second = SB == 2 && w4 && !dup ? 1 : 0;
   const int G = p.G;
@@ -1452,9 +1461,11 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
       for (int r = 0; r < 4; ++r) acc[t][rb][r] = 0.0f;
   if (cnt > 0) {
     if (w4)
-      strip_body<kW4, SB, RB, PARTIALS>(p, blk0, second, dup, lane, wave, ks, cnt, lds, acc);
+      strip_body<kW4, SB, RB, PARTIALS>(p, blk0, second, dup, 0, lane, wave, ks, cnt, lds, acc);
+    else if (SB == 1 && h8)
+      strip_body<kW8, 1, RB, PARTIALS, true>(p, blk0, 0, false, half, lane, wave, ks, cnt, lds, acc);
     else
-      strip_body<kW8, SB, RB, PARTIALS>(p, blk0, 0, false, lane, wave, ks, cnt, lds, acc);
+      strip_body<kW8, SB, RB, PARTIALS>(p, blk0, 0, false, 0, lane, wave, ks, cnt, lds, acc);
   }
   if (PARTIALS) return;
   __syncthreads();  // every wave's stages are done; the space becomes the reduction area
@@ -1469,7 +1480,8 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
   // Output: the workgroup's waves share the 16 RB (tile, row block, row) slots; each sums
   // its slot over the waves in order and writes the row's channel.
   const bool four = SB == 2 && w4;  // four column tiles (two blocks)
-  const int nt = four && !dup ? 4 : 2;
+  const bool one = h8;              // one column tile (half an 8-bit block)
+  const int nt = four && !dup ? 4 : (one ? 1 : 2);
   const int ch = lane & 15, qd = lane >> 4;
   for (int e = wave; e < 16 * RB; e += ks) {
     const int t = e / (4 * RB), rb = (e >> 2) % RB, r = e & 3;
@@ -1477,7 +1489,7 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
     if (t >= nt || rowo >= p.M) continue;
     float v = 0.0f;
     for (int w = 0; w < ks; ++w) v += red[w][e][lane];
-    const int cw = (four ? (t & 1) : t) * 16 + ch;
+    const int cw = (four ? (t & 1) : (one ? half : t)) * 16 + ch;
     const int orig = p.idx[(blk0 + (four ? (t >> 1) : 0)) * 32 + cw];
     if (orig >= 0) p.y[(int64_t)rowo * p.ldy + orig] = f2h(v);
   }
@@ -1556,6 +1568,7 @@ struct Plan {
   bool gemv;                   // M <= 3: the one-lane-per-channel kernel
   bool strip;                  // 4 <= M <= 16 on wide layers: the strip kernel
   int sb;                      // strip, gemv: 4-bit blocks per strip
+  bool h8;                     // strip with sb = 1: 8-bit blocks in 16-channel halves
   int nstrip4, nstrip;         // gemv: strips of 4-bit blocks, all strips
   bool skinny;
   int rb;                      // skinny: 16-row blocks
@@ -1679,6 +1692,16 @@ int skinny_cost_pm(int M) {
 // kernel takes to stream the same weights at M = 1); the skinny kernel keeps every CU busy
 // but costs more per weight byte as M grows.  The tile kernel is taken when
 // tiles * cost > 0.9 * CUs (0.45 * CUs where the layer runs 2-block tiles).
+// One-block strips of the strip kernel: an 8-bit block streams twice the bytes of a
+// 4-bit one, so it goes in two 16-channel halves, each as heavy as a 4-bit strip, when
+// all the strips still fit the CUs at one each (measured: 6144 x 8192 at M = 8 10.2 ->
+// 8.4 us, 6144 x 4096 at M = 16 7.4 -> 6.5 us).  With more strips than CUs some CUs would
+// run two, which measured slower than the 2:1 imbalance it removes (Llama-3.1-70B down
+// projection at M = 4 / 8: 28.3 / 29.6 us against 33.7 / 35.6).  (The same split of the
+// one-lane-per-channel kernel's 8-bit strips, inputs in quarters, measured 2-6% slower at
+// M = 1..3 on 4096 x 4096 and 6144 x 4096, and is not used.)
+bool halves8_fit(const mixllm_blob_info &L, int cus) { return L.nb4 + 2 * (int64_t)L.nb8 <= cus; }
+
 Plan make_plan(int M, const mixllm_blob_info &L) {
   Plan pl{};
   const int cus = device_cus() > 0 ? device_cus() : 256;
@@ -1707,7 +1730,8 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
     pl.rb = (M + 15) / 16;
     pl.sb = 4 * (int64_t)nstrip >= 3 * (int64_t)cus ? 2 : 1;
     pl.nstrip4 = pl.sb == 2 ? nstrip4 : L.nb4;
-    pl.nstrip = pl.sb == 2 ? nstrip : L.nb;
+    pl.h8 = pl.sb == 1 && halves8_fit(L, cus);
+    pl.nstrip = pl.sb == 2 ? nstrip : L.nb4 + (pl.h8 ? 2 : 1) * L.nb8;
     pl.ks = pick_waves(pl.nstrip, L.G, 4 * strip_waves_per_simd(pl.sb, pl.rb), kStWaves, cus,
                        kLdsPerCu / st_lds(pl.rb));
     return pl;
@@ -1772,14 +1796,14 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
     const dim3 grid((unsigned)pl.nstrip), block((unsigned)(64 * pl.ks));
     if (pl.rb == 1) {
       if (pl.sb == 2)
-        hipLaunchKernelGGL((gemm_strip_kernel<2, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+        hipLaunchKernelGGL((gemm_strip_kernel<2, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, (int)pl.h8);
       else
-        hipLaunchKernelGGL((gemm_strip_kernel<1, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+        hipLaunchKernelGGL((gemm_strip_kernel<1, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, (int)pl.h8);
     } else {
       if (pl.sb == 2)
-        hipLaunchKernelGGL((gemm_strip_kernel<2, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+        hipLaunchKernelGGL((gemm_strip_kernel<2, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, (int)pl.h8);
       else
-        hipLaunchKernelGGL((gemm_strip_kernel<1, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4);
+        hipLaunchKernelGGL((gemm_strip_kernel<1, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, (int)pl.h8);
     }
   } else if (pl.skinny) {
     const int ks = pl.ks;
