@@ -98,6 +98,9 @@ SMALL = [
     # (these narrow layers take two-block tiles); four-block tiles need a grid as large as
     # the device: a ragged last M tile
     (160, 288, 1920, 40), (96, 130, 2688, 13), (4150, 1024, 128, 100),
+    # more 8-bit blocks than N tiles: consecutive blocks per tile, tiles of both kinds
+    # (two-block and four-block tiles; the cases above interleave the blocks over the tiles)
+    (160, 640, 512, 400), (4150, 1024, 128, 700),
     # M <= 64 on layers wide enough (on a 256-CU part) for the tile kernel's cost rule
     (48, 12800, 256, 1280), (20, 16448, 128, 100), (1, 29000, 128, 290),
     # M = 1 .. 3 on layers wide enough for the one-lane-per-channel kernel, and 4 .. 16 for
