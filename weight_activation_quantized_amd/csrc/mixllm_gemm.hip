@@ -1244,6 +1244,9 @@ __global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const 
 // ------------------------------------------------------------------------------------
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kStWaves = 8;  // waves per workgroup at most
+#ifndef MIXLLM_ST_MIX
+#define MIXLLM_ST_MIX 1
+#endif
 constexpr int kStMaxRows = 32;  // tokens the strip kernel takes
 // RB 16-row blocks (M <= 16 RB).  Weight ring (registers) and activation ring (LDS) of
 // st_ring(RB) stages: one group ahead for one row block, 2 for two (measured: deeper rings
@@ -1263,39 +1266,51 @@ __device__ __forceinline__ void bload4_lds(Rsrc r, void *dst, int voff, int soff
 
 // NT column tiles: with SB = 2, 4-bit strips hold blocks blk0 and blk0 + second (tiles 2
 // and 3 repeat tiles 0 and 1 when the strip has one block: dup); otherwise a strip is
-// block blk0, or for 8-bit strips with SB = 1 its 16-channel half `half`.  `lds` is this
-// wave's ring of st_ring(RB) stages.
-template <int KIND, int SB, int RB, bool PARTIALS, bool H8 = false>
+// block blk0, or for 8-bit strips with SB = 1 (MODE 1) its 16-channel half `half`, or
+// (MODE 2, a mixed strip) the half `half` of 8-bit block blk0 as tile 0 and the half
+// `half` of 4-bit block `second` as tile 1.  `lds` is this wave's ring of st_ring(RB)
+// stages.
+template <int KIND, int SB, int RB, bool PARTIALS, int MODE = 0>
 __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int second, bool dup, int half, int lane,
                                            int g0, int gstep, int cnt, uint8_t *lds, float (&acc)[4][RB][4]) {
-  // Column tiles: 4 (two 4-bit blocks), 2 (one 4-bit block, or one 8-bit block), or 1 (H8:
-  // the 16-channel half `half` of an 8-bit block).
-  constexpr int NT = KIND == kW8 ? (H8 ? 1 : 2) : (SB == 1 ? 2 : 4);
+  constexpr bool H8 = MODE == 1, MIX = MODE == 2;
+  static_assert(!MIX || (KIND == kW8 && SB == 1), "mixed strips");
+  // Column tiles: 4 (two 4-bit blocks), 2 (one 4-bit block, one 8-bit block, or a mixed
+  // strip), or 1 (H8: the 16-channel half `half` of an 8-bit block).
+  constexpr int NT = MIX ? 2 : (KIND == kW8 ? (H8 ? 1 : 2) : (SB == 1 ? 2 : 4));
+  constexpr bool ANY4 = MIX || KIND == kW4;  // a 4-bit tile: the group's code sums are loaded
+  constexpr bool ANY8 = MIX || KIND == kW8;
   constexpr int D = st_ring(RB);
   constexpr int kStage = st_stage(RB);
-  constexpr int kWChunk = KIND == kW8 ? (int)kW8Chunk : (int)kW4Chunk;
   // Vector-memory operations per step: the stage's direct-to-LDS loads, then the weight
   // ring's loads.  When step s computes, the loads issued after step s's stage are the
   // weight batch of the step that issued it and D - 1 full batches; a wait for at most
   // that many outstanding proves the stage has landed (the compiler does not track LDS
   // written by these loads).
-  constexpr int LA = 2 * RB + (KIND == kW4 ? 2 : 1);
+  constexpr int LA = 2 * RB + (ANY4 ? 2 : 1);
   constexpr int LW = 3 * NT;  // per column tile: codes (or two loads of 8-bit codes) and scale
                               // word, plus the zero-point word for 4-bit
   constexpr int WAIT = LW + (D - 1) * (LA + LW);
   static_assert(WAIT < 64, "vmcnt range");
   const int ch = lane & 15, qd = lane >> 4;
   const int G = p.G, M = p.M;
-  const int bq = KIND == kW8 ? blk0 - p.nb4 : blk0;
-  const Rsrc rw = make_rsrc((KIND == kW8 ? p.w8 : p.w4) + (size_t)bq * G * kWChunk, (int64_t)2 * G * kWChunk);
-  const Rsrc rs = make_rsrc((KIND == kW8 ? p.s8 : p.s4) + (size_t)bq * G * 32, (int64_t)2 * G * 64);
-  const Rsrc rz = make_rsrc(p.z4 + (size_t)bq * G * kZ4Chunk, KIND == kW4 ? (int64_t)2 * G * kZ4Chunk : 0);
+  // The strip's 8-bit block (index among the 8-bit blocks) and 4-bit block.
+  const int b8 = ANY8 ? blk0 - p.nb4 : 0, b4 = MIX ? second : (KIND == kW4 ? blk0 : 0);
+  const Rsrc rw8 = make_rsrc(p.w8 + (size_t)b8 * G * kW8Chunk, ANY8 ? (int64_t)2 * G * kW8Chunk : 0);
+  const Rsrc rs8 = make_rsrc(p.s8 + (size_t)b8 * G * 32, ANY8 ? (int64_t)2 * G * 64 : 0);
+  const Rsrc rw4 = make_rsrc(p.w4 + (size_t)b4 * G * kW4Chunk, ANY4 ? (int64_t)2 * G * kW4Chunk : 0);
+  const Rsrc rs4 = make_rsrc(p.s4 + (size_t)b4 * G * 32, ANY4 ? (int64_t)2 * G * 64 : 0);
+  const Rsrc rz = make_rsrc(p.z4 + (size_t)b4 * G * kZ4Chunk, ANY4 ? (int64_t)2 * G * kZ4Chunk : 0);
   const Rsrc ra = make_rsrc(p.aq, (int64_t)M * p.K);
   const Rsrc rsa = make_rsrc(p.sa, (int64_t)G * M * 4);
-  const Rsrc ras = make_rsrc(p.asum, KIND == kW4 ? (int64_t)G * M * 4 : 0);
-  // Column tile t: block offset bo(t) (in blocks from blk0) and half ht(t) of it.
+  const Rsrc ras = make_rsrc(p.asum, ANY4 ? (int64_t)G * M * 4 : 0);
+  // Column tile t: its kind, block offset bo(t) (in blocks from the strip's 4-bit block)
+  // and half ht(t) of it; blkt(t) is its block.  (t is a constant in every unrolled loop,
+  // so these fold.)
+  auto is8 = [&](int t) { return MIX ? t == 0 : KIND == kW8; };
   auto bo = [&](int t) { return NT == 4 ? (t >> 1) * second : 0; };
-  auto ht = [&](int t) { return NT == 1 ? half : (t & 1); };
+  auto ht = [&](int t) { return (NT == 1 || MIX) ? half : (t & 1); };
+  auto blkt = [&](int t) { return MIX ? (t == 0 ? blk0 : second) : blk0 + bo(t); };
   // Direct-to-LDS offsets: load i of a stage fills rows 8i .. 8i + 7 (lane l: row
   // 8i + l / 8, position l % 8, which holds chunk (l % 8) ^ (row & 7)); the scale loads
   // fill row l's word.  Rows past M load from past every descriptor (zeros, no traffic).
@@ -1313,7 +1328,7 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
 #pragma unroll
     for (int c = 0; c < 2; ++c) va[rb][c] = (16 * rb + ch) * 128 + (((qd + 4 * c) ^ (ch & 7)) << 4);
 
-  v4i wR[D][NT][KIND == kW8 ? 2 : 1];
+  v4i wR[D][NT][ANY8 ? 2 : 1];
   uint32_t sR[D][NT], zR[D][NT];
   auto grp = [&](int s) { return g0 + min(s, cnt - 1) * gstep; };
   auto issue_a = [&](auto j_c, int s) {
@@ -1323,7 +1338,7 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
 #pragma unroll
     for (int i = 0; i < 2 * RB; ++i) bload16_lds(ra, st + i * 1024, vdma[i], g * 128);
     bload4_lds(rsa, st + RB * 2048, vrow, g * M * 4);
-    if constexpr (KIND == kW4) bload4_lds(ras, st + RB * 2048 + 256, vrow, g * M * 4);
+    if constexpr (ANY4) bload4_lds(ras, st + RB * 2048 + 256, vrow, g * M * 4);
   };
   auto issue_w = [&](auto j_c, int s) {
     constexpr int J = decltype(j_c)::value;
@@ -1331,15 +1346,18 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cw = ht(t) * 16 + ch;  // the lane's channel within its block
-      if constexpr (KIND == kW8) {
+      if (is8(t)) {
+        if constexpr (ANY8) {
 #pragma unroll
-        for (int mf = 0; mf < 2; ++mf)
-          wR[J][t][mf] = bload16_nt(rw, ht(t) * 2048 + mf * 1024 + lane * 16, g * kWChunk);
+          for (int mf = 0; mf < 2; ++mf)
+            wR[J][t][mf] = bload16_nt(rw8, ht(t) * 2048 + mf * 1024 + lane * 16, g * (int)kW8Chunk);
+          sR[J][t] = bload4(rs8, (cw >> 1) * 4, g * 64);
+        }
       } else {
-        wR[J][t][0] = bload16_nt(rw, bo(t) * G * kWChunk + ht(t) * 1024 + lane * 16, g * kWChunk);
+        wR[J][t][0] = bload16_nt(rw4, bo(t) * G * (int)kW4Chunk + ht(t) * 1024 + lane * 16, g * (int)kW4Chunk);
         zR[J][t] = bload4(rz, bo(t) * G * (int)kZ4Chunk + (cw >> 3) * 4, g * (int)kZ4Chunk);
+        sR[J][t] = bload4(rs4, bo(t) * G * 64 + (cw >> 1) * 4, g * 64);
       }
-      sR[J][t] = bload4(rs, bo(t) * G * 64 + (cw >> 1) * 4, g * 64);
     }
   };
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
@@ -1360,14 +1378,14 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
       a0[rb] = *reinterpret_cast<const v4i *>(st + va[rb][0]);
       a1[rb] = *reinterpret_cast<const v4i *>(st + va[rb][1]);
       sa4[rb] = *reinterpret_cast<const v4i *>(st + RB * 2048 + (16 * rb + 4 * qd) * 4);
-      as4[rb] = KIND == kW4 ? *reinterpret_cast<const v4i *>(st + RB * 2048 + 256 + (16 * rb + 4 * qd) * 4)
-                            : v4i{0, 0, 0, 0};
+      as4[rb] = ANY4 ? *reinterpret_cast<const v4i *>(st + RB * 2048 + 256 + (16 * rb + 4 * qd) * 4)
+                     : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int cw = ht(t) * 16 + ch;
       v4i b0, b1;
-      if constexpr (KIND == kW4) {
+      if (!is8(t)) {
         const v4i x = wR[J][t][0];
         const uint32_t x0 = (uint32_t)x[0], x1 = (uint32_t)x[1], x2 = (uint32_t)x[2], x3 = (uint32_t)x[3];
         b0 = v4i{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu),
@@ -1376,19 +1394,19 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
                  (int)((x3 >> 4) & 0x0F0F0F0Fu)};
       } else {
         b0 = wR[J][t][0];
-        b1 = wR[J][t][1];
+        if constexpr (ANY8) b1 = wR[J][t][1];
       }
-      const int z = KIND == kW4 ? (int)((zR[J][t] >> ((cw & 7) * 4)) & 15u) : 0;
+      const int z = !is8(t) ? (int)((zR[J][t] >> ((cw & 7) * 4)) & 15u) : 0;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         v4i P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[rb], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
         P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[rb], b1, P, 0, 0, 0);
-        if constexpr (KIND == kW4) {
+        if (!is8(t)) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) P[r] -= z * as4[rb][r];
         }
         if constexpr (PARTIALS) {
-          const int orig = p.idx[(blk0 + bo(t)) * 32 + cw];
+          const int orig = p.idx[blkt(t) * 32 + cw];
           if (!(dup && t >= 2) && orig >= p.n_begin && orig < p.n_begin + p.n_count) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1437,20 +1455,24 @@ __device__ __forceinline__ void strip_body(const GemmArgs &p, int blk0, int seco
 // RB: 16-row blocks.
 template <int SB, int RB, bool PARTIALS>
 __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArgs p, int ks, int nstrip4,
-                                                                   int halves8) {
+                                                                   int mode8) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[st_lds(RB)];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int strip = blockIdx.x;
   // Strips [0, nstrip4) hold SB 4-bit blocks each (with SB = 2 an odd count leaves the
   // last strip one block, repeated in tiles 2 and 3); the others one 8-bit block each, or
-  // with `halves8` (SB = 1) one 16-channel half of an 8-bit block, so that every strip
-  // streams 16 bytes of weights per input, as a one-block 4-bit strip does.
+  // with SB = 1 and mode8 = 1 one 16-channel half of an 8-bit block (every strip then
+  // streams 16 bytes of weights per input, as a one-block 4-bit strip does), or with
+  // mode8 = 2 a mixed strip: half j of 8-bit block i and half j of 4-bit block nstrip4 + i
+  // (the last nb8 4-bit blocks go in halves beside the 8-bit ones: 24 bytes per input).
   const bool w4 = strip < nstrip4;
-  const bool h8 = SB == 1 && halves8 && !w4;
+  const bool h8 = SB == 1 && mode8 == 1 && !w4;
+  const bool mix = SB == 1 && mode8 == 2 && !w4;
   const int s8 = strip - nstrip4;
-  const int half = h8 ? (s8 & 1) : 0;
-  const int blk0 = w4 ? SB * strip : p.nb4 + (h8 ? (s8 >> 1) : s8);
+  const int half = h8 || mix ? (s8 & 1) : 0;
+  const int blk0 = w4 ? SB * strip : p.nb4 + (h8 || mix ? (s8 >> 1) : s8);
+  const int blk4 = mix ? nstrip4 + (s8 >> 1) : 0;  // a mixed strip's 4-bit block
   const bool dup = SB == 2 && w4 && p.nb4 - blk0 < 2;
   const int second = SB == 2 && w4 && !dup ? 1 : 0;
   const int G = p.G;
@@ -1468,7 +1490,9 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
     if (w4)
       strip_body<kW4, SB, RB, PARTIALS>(p, blk0, second, dup, 0, lane, wave, ks, cnt, lds, acc);
     else if (SB == 1 && h8)
-      strip_body<kW8, 1, RB, PARTIALS, true>(p, blk0, 0, false, half, lane, wave, ks, cnt, lds, acc);
+      strip_body<kW8, 1, RB, PARTIALS, 1>(p, blk0, 0, false, half, lane, wave, ks, cnt, lds, acc);
+    else if (SB == 1 && mix)
+      strip_body<kW8, 1, RB, PARTIALS, 2>(p, blk0, blk4, false, half, lane, wave, ks, cnt, lds, acc);
     else
       strip_body<kW8, SB, RB, PARTIALS>(p, blk0, 0, false, 0, lane, wave, ks, cnt, lds, acc);
   }
@@ -1494,8 +1518,8 @@ __global__ __launch_bounds__(64 * kStWaves) void gemm_strip_kernel(const GemmArg
     if (t >= nt || rowo >= p.M) continue;
     float v = 0.0f;
     for (int w = 0; w < ks; ++w) v += red[w][e][lane];
-    const int cw = (four ? (t & 1) : (one ? half : t)) * 16 + ch;
-    const int orig = p.idx[(blk0 + (four ? (t >> 1) : 0)) * 32 + cw];
+    const int cw = (four ? (t & 1) : (one || mix ? half : t)) * 16 + ch;
+    const int orig = p.idx[(mix ? (t == 0 ? blk0 : blk4) : blk0 + (four ? (t >> 1) : 0)) * 32 + cw];
     if (orig >= 0) p.y[(int64_t)rowo * p.ldy + orig] = f2h(v);
   }
 }
@@ -1575,6 +1599,7 @@ struct Plan {
   bool strip;                  // 4 <= M <= 16 on wide layers: the strip kernel
   int sb;                      // strip, gemv: 4-bit blocks per strip
   bool h8;                     // strip with sb = 1: 8-bit blocks in 16-channel halves
+  bool mix;                    // strip with sb = 1: 8-bit halves paired with 4-bit halves
   int nstrip4, nstrip;         // gemv: strips of 4-bit blocks, all strips
   bool skinny;
   int rb;                      // skinny: 16-row blocks
@@ -1737,6 +1762,8 @@ Plan make_plan(int M, const mixllm_blob_info &L) {
     pl.sb = 4 * (int64_t)nstrip >= 3 * (int64_t)cus ? 2 : 1;
     pl.nstrip4 = pl.sb == 2 ? nstrip4 : L.nb4;
     pl.h8 = pl.sb == 1 && halves8_fit(L, cus);
+    pl.mix = MIXLLM_ST_MIX && pl.sb == 1 && !pl.h8 && L.nb8 > 0 && L.nb4 >= L.nb8;
+    if (pl.mix) pl.nstrip4 = L.nb4 - L.nb8;
     pl.nstrip = pl.sb == 2 ? nstrip : L.nb4 + (pl.h8 ? 2 : 1) * L.nb8;
     pl.ks = pick_waves(pl.nstrip, L.G, 4 * strip_waves_per_simd(pl.sb, pl.rb), kStWaves, cus,
                        kLdsPerCu / st_lds(pl.rb));
@@ -1802,14 +1829,14 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
     const dim3 grid((unsigned)pl.nstrip), block((unsigned)(64 * pl.ks));
     if (pl.rb == 1) {
       if (pl.sb == 2)
-        hipLaunchKernelGGL((gemm_strip_kernel<2, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, (int)pl.h8);
+        hipLaunchKernelGGL((gemm_strip_kernel<2, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, pl.h8 ? 1 : (pl.mix ? 2 : 0));
       else
-        hipLaunchKernelGGL((gemm_strip_kernel<1, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, (int)pl.h8);
+        hipLaunchKernelGGL((gemm_strip_kernel<1, 1, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, pl.h8 ? 1 : (pl.mix ? 2 : 0));
     } else {
       if (pl.sb == 2)
-        hipLaunchKernelGGL((gemm_strip_kernel<2, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, (int)pl.h8);
+        hipLaunchKernelGGL((gemm_strip_kernel<2, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, pl.h8 ? 1 : (pl.mix ? 2 : 0));
       else
-        hipLaunchKernelGGL((gemm_strip_kernel<1, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, (int)pl.h8);
+        hipLaunchKernelGGL((gemm_strip_kernel<1, 2, PARTIALS>), grid, block, 0, stream, a, pl.ks, pl.nstrip4, pl.h8 ? 1 : (pl.mix ? 2 : 0));
     }
   } else if (pl.skinny) {
     const int ks = pl.ks;
