@@ -1245,7 +1245,7 @@ __global__ __launch_bounds__(64 * gv_max_waves(MT)) void gemm_gemv_kernel(const 
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kStWaves = 8;  // waves per workgroup at most
 #ifndef MIXLLM_ST_MIX
-#define MIXLLM_ST_MIX 1
+#define MIXLLM_ST_MIX 1  // mixed strips (see halves8_fit); 0 keeps whole 8-bit strips, to compare
 #endif
 constexpr int kStMaxRows = 32;  // tokens the strip kernel takes
 // RB 16-row blocks (M <= 16 RB).  Weight ring (registers) and activation ring (LDS) of
@@ -1730,7 +1730,10 @@ int skinny_cost_pm(int M) {
 // run two, which measured slower than the 2:1 imbalance it removes (Llama-3.1-70B down
 // projection at M = 4 / 8: 28.3 / 29.6 us against 33.7 / 35.6).  (The same split of the
 // one-lane-per-channel kernel's 8-bit strips, inputs in quarters, measured 2-6% slower at
-// M = 1..3 on 4096 x 4096 and 6144 x 4096, and is not used.)
+// M = 1..3 on 4096 x 4096 and 6144 x 4096, and is not used.)  Where the halves do not fit,
+// mixed strips pair each half of an 8-bit block with the same half of one of the last nb8
+// 4-bit blocks: as many strips as blocks, the heaviest streaming 24 bytes per input instead
+// of 32 (70B down projection at M = 4 / 8 / 16: 28.4 / 29.8 / 32.7 -> 26.3 / 27.7 / 30.3 us).
 bool halves8_fit(const mixllm_blob_info &L, int cus) { return L.nb4 + 2 * (int64_t)L.nb8 <= cus; }
 
 Plan make_plan(int M, const mixllm_blob_info &L) {
