@@ -1857,11 +1857,14 @@ int launch(GemmArgs &a, const Plan &pl, hipStream_t stream) {
     const int64_t T = (int64_t)a.tiles_m * a.tiles_n;
     if (T > 0x7FFFFFFF) return MIXLLM_E_SHAPE;
     a.spread = T <= device_cus() ? 1 : 0;
-    // Interleaved blocks when each tile gets at most one 8-bit block.  Same box, against
-    // consecutive blocks: Llama-3.1-70B q/o at M = 512 66.2 -> 62.8 us, gate 216.9 -> 210.5,
-    // 4096 x 4096 at M = 128 13.9 -> 13.4, the headline within 1%; with half the channels
-    // 8-bit (two per tile) 19.9 -> 21.0, so there the blocks stay consecutive.
-    a.ileave = a.nb - a.nb4 <= a.tiles_n ? 1 : 0;
+    // Interleaved blocks when each tile gets at most one 8-bit block and the grid runs in
+    // several rounds or has 2-block tiles.  Same box, against consecutive blocks:
+    // Llama-3.1-70B q/o at M = 512 66.2 -> 62.8 us, gate 216.9 -> 210.5, 4096 x 4096 at
+    // M = 128 13.9 -> 13.4; with half the channels 8-bit (two per tile) 19.9 -> 21.0.  A
+    // single round of 4-block tiles (4096 x 4096 at M = 512) ran within 1% either way but
+    // wrote 8.2 MB instead of 7.0 (more workgroups writing partial output lines), so it
+    // keeps consecutive blocks.
+    a.ileave = a.nb - a.nb4 <= a.tiles_n && !(a.spread && pl.nbt == 4) ? 1 : 0;
     const dim3 grid((unsigned)T);
     if (!PARTIALS && a.tiles_m <= kTileBand) {
       if (pl.nbt == 2)
